@@ -1,0 +1,156 @@
+"""Pins of the oracle's frequency rules against closed forms, special cases and
+printed values (CPU only)."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import freqs
+
+# (head_dim, base, factor, original length) of the workloads
+CONFIGS = [
+    (64, 10000.0, 4.0, 64),
+    (128, 10000.0, 4.0, 4096),
+    (128, 500000.0, 8.0, 16384),
+]
+
+
+@pytest.mark.parametrize("d,base", [(64, 10000.0), (128, 10000.0), (128, 500000.0), (8, 16.0)])
+def test_theta_closed_form(d, base):
+    th = freqs.rope_theta(d, base)
+    assert th.shape == (d // 2,)
+    assert th[0] == 1.0
+    # last pair: base^(-(d-2)/d), written through exp/log instead of pow
+    assert th[-1] == pytest.approx(math.exp(-(d - 2) / d * math.log(base)), rel=1e-14)
+    assert np.all(np.diff(th) < 0)
+    # geometric series: constant ratio base^(-2/d)
+    ratios = th[1:] / th[:-1]
+    assert np.allclose(ratios, math.exp(-2.0 / d * math.log(base)), rtol=1e-13, atol=0)
+
+
+def test_theta_tiny_exact_values():
+    # base 16, d = 8: theta = 16^0, 16^-1/4, 16^-1/2, 16^-3/4 = 1, 1/2, 1/4, 1/8
+    assert list(freqs.rope_theta(8, 16.0)) == [1.0, 0.5, 0.25, 0.125]
+
+
+def _regions(d, base, s, L):
+    th = freqs.rope_theta(d, base)
+    tp = freqs.yarn_theta(d, base, s, L)
+    region = []
+    for a, b in zip(th, tp):
+        if b == a:
+            region.append("unscaled")
+        elif b == a / s:
+            region.append("pi")
+        else:
+            region.append("ramp")
+    return region
+
+
+@pytest.mark.parametrize("d,base,s,L", CONFIGS)
+def test_yarn_region_boundaries_closed_form(d, base, s, L):
+    """r_i = L theta_i / 2pi >= beta  <=>  i <= (d/2) ln(L / (2 pi beta)) / ln(base);
+    r_i <= alpha <=> i >= (d/2) ln(L / (2 pi alpha)) / ln(base)."""
+    alpha, beta = 1.0, 32.0
+    i_hi = (d / 2) * math.log(L / (2 * math.pi * beta)) / math.log(base)
+    i_lo = (d / 2) * math.log(L / (2 * math.pi * alpha)) / math.log(base)
+    region = _regions(d, base, s, L)
+    for i, reg in enumerate(region):
+        if i <= i_hi:
+            assert reg == "unscaled", (i, reg)
+        elif i >= i_lo:
+            assert reg == "pi", (i, reg)
+        else:
+            assert reg == "ramp", (i, reg)
+
+
+def test_yarn_region_index_ranges_of_the_workloads():
+    def spans(region):
+        out = {}
+        for i, r in enumerate(region):
+            lo, hi = out.get(r, (i, i))
+            out[r] = (min(lo, i), max(hi, i))
+        return out
+    assert spans(_regions(64, 10000.0, 4.0, 64)) == {"ramp": (0, 8), "pi": (9, 31)}
+    assert spans(_regions(128, 10000.0, 4.0, 4096)) == {
+        "unscaled": (0, 20), "ramp": (21, 45), "pi": (46, 63)}
+    assert spans(_regions(128, 500000.0, 8.0, 16384)) == {
+        "unscaled": (0, 21), "ramp": (22, 38), "pi": (39, 63)}
+
+
+@pytest.mark.parametrize("d,base,s,L", CONFIGS)
+def test_yarn_monotone_and_bracketed(d, base, s, L):
+    th = freqs.rope_theta(d, base)
+    tp = freqs.yarn_theta(d, base, s, L)
+    assert np.all(np.diff(tp) < 0)
+    assert np.all(tp <= th) and np.all(tp >= th / s)
+
+
+def test_gamma_ramp_shape():
+    a, b = 1.0, 32.0
+    assert freqs.yarn_gamma(a, a, b) == 0.0
+    assert freqs.yarn_gamma(b, a, b) == 1.0
+    assert freqs.yarn_gamma(0.0, a, b) == 0.0
+    assert freqs.yarn_gamma(1e9, a, b) == 1.0
+    assert freqs.yarn_gamma((a + b) / 2, a, b) == 0.5
+    # continuity at both ends and linearity inside
+    eps = 1e-9
+    assert freqs.yarn_gamma(a + eps, a, b) == pytest.approx(0.0, abs=1e-9)
+    assert freqs.yarn_gamma(b - eps, a, b) == pytest.approx(1.0, abs=1e-9)
+    xs = np.linspace(a, b, 17)
+    gs = np.array([freqs.yarn_gamma(x, a, b) for x in xs])
+    assert np.allclose(np.diff(gs), gs[1] - gs[0], rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("d,base,L", [(64, 10000.0, 64), (128, 10000.0, 4096), (128, 500000.0, 16384)])
+def test_s1_is_plain_rope_bitwise(d, base, L):
+    assert np.array_equal(freqs.yarn_theta(d, base, 1.0, L), freqs.rope_theta(d, base))
+    assert freqs.attention_temperature(1.0) == 1.0
+    assert np.array_equal(freqs.to_fp32(freqs.yarn_theta(d, base, 1.0, L)),
+                          freqs.rope_theta(d, base).astype(np.float32))
+
+
+@pytest.mark.parametrize("d,base,s", [(64, 10000.0, 4.0), (128, 500000.0, 8.0), (128, 10000.0, 3.0)])
+def test_pi_angles_are_positions_over_s(d, base, s):
+    th = freqs.rope_theta(d, base)
+    tp = freqs.pi_theta(d, base, s)
+    for m in (0, 1, 7, 4095, 65537, 131072):
+        a = m * tp
+        b = (m / s) * th
+        assert np.all(np.abs(a - b) <= np.spacing(np.abs(b)) + 0.0)
+
+
+def test_large_ratio_limit_is_pi_and_small_ratio_limit_is_unscaled():
+    # a tiny original length makes every pair turn less than once: pure PI
+    d, base, s = 64, 10000.0, 4.0
+    assert np.array_equal(freqs.yarn_theta(d, base, s, 1), freqs.rope_theta(d, base) / s)
+    # a huge original length makes every pair turn more than beta times: unscaled
+    assert np.array_equal(freqs.yarn_theta(d, base, s, 10 ** 12), freqs.rope_theta(d, base))
+
+
+def test_temperature_values():
+    ln4 = 1.3862943611198906
+    ln8 = 2.0794415416798357
+    assert freqs.attention_temperature(4.0) == pytest.approx(1.0 + 0.1 * ln4, rel=1e-15)
+    assert freqs.attention_temperature(8.0) == pytest.approx(1.0 + 0.1 * ln8, rel=1e-15)
+    assert freqs.attention_temperature(4.0) == pytest.approx(1.1386294361119891, rel=1e-15)
+    assert freqs.attention_temperature(8.0) == pytest.approx(1.2079441541679836, rel=1e-15)
+    assert freqs.temperature_for("pi", 8.0) == 1.0
+    assert freqs.softmax_scale(64, freqs.attention_temperature(4.0)) == pytest.approx(1.1386294361119891 / 8.0)
+
+
+def test_ntk_worked_example():
+    # printed: base ~ 82,000 for s = 8, d = 128 (exact 82,684.6...)
+    b = freqs.ntk_base(128, 10000.0, 8.0)
+    assert b == pytest.approx(82684.6, rel=1e-5)
+    assert abs(b - 82000.0) / 82000.0 < 0.01
+    th = freqs.ntk_theta(128, 10000.0, 8.0)
+    assert th[0] == 1.0 and th[-1] < freqs.rope_theta(128, 10000.0)[-1]
+
+
+@pytest.mark.parametrize("d,base,s,L", CONFIGS + [(128, 10000.0, 8.0, 4096), (64, 10000.0, 2.0, 2048)])
+@pytest.mark.parametrize("method", ["plain", "pi", "ntk", "yarn"])
+def test_fp32_table_far_from_rounding_midpoints(d, base, s, L, method):
+    th = freqs.theta_for(method, d, base, s, L)
+    assert np.min(freqs.fp32_midpoint_distance(th)) > 2.0 ** -40

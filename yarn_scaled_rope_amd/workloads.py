@@ -1,0 +1,236 @@
+"""Seeded synthetic workloads and algorithmic work counts.
+
+This module holds no part of the attention method: it draws the inputs (the
+same bits go to the GPU library and to the CPU checker) and counts the
+algorithmic work that throughput is quoted on.
+
+Input recipe: ``numpy.random.Generator(PCG64(1000 + index))``; for the decode
+workload the cache lengths are drawn first; then Q, K and V are drawn as
+float32 standard normals in their storage layouts, in that order, and rounded
+once to bfloat16 (round to nearest, ties to even) except for the fp32
+workload.  The decode cache draws K rows of sequence 0, 1, ... then V rows in
+the same order; cache rows past a sequence's length are NaN so any read
+beyond ``seqlens`` shows up in the output.
+
+Shapes follow the attention layers of the models the pages use for their
+worked figures (Llama-2-7B, Llama-3-8B at 128K, Llama-3-70B, GQA with 8 KV
+heads).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+BF16_NAN_BITS = 0x7FC0
+_CHUNK = 1 << 24          # elements per generation chunk (bounds host memory)
+
+
+@dataclasses.dataclass(frozen=True)
+class PrefillConfig:
+    name: str
+    index: int
+    seq_lens: tuple
+    hq: int
+    hkv: int
+    head_dim: int
+    dtype: str                 # "f32" or "bf16" (input storage type)
+    base: float
+    factor: float
+    original_max_position: int
+
+    @property
+    def total_tokens(self) -> int:
+        return int(sum(self.seq_lens))
+
+    @property
+    def max_seqlen(self) -> int:
+        return int(max(self.seq_lens))
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    index: int
+    batch: int
+    max_cache_len: int
+    min_cache_len: int
+    hq: int
+    hkv: int
+    head_dim: int
+    dtype: str
+    base: float
+    factor: float
+    original_max_position: int
+
+
+TINY_F32 = PrefillConfig("tiny_fp32_prefill", 0, (256,), 4, 2, 64, "f32",
+                         10000.0, 4.0, 64)
+LLAMA2_7B_16K = PrefillConfig("llama2_7b_prefill_16k", 1, (16384,), 32, 32,
+                              128, "bf16", 10000.0, 4.0, 4096)
+LLAMA3_8B_128K = PrefillConfig("llama3_8b_gqa_prefill_128k", 2, (131072,),
+                               32, 8, 128, "bf16", 500000.0, 8.0, 16384)
+DECODE_B16 = DecodeConfig("decode_b16_gqa_32k_128k", 3, 16, 131072, 32768,
+                          32, 8, 128, "bf16", 500000.0, 8.0, 16384)
+LLAMA3_70B_RAGGED = PrefillConfig("llama3_70b_ragged_prefill", 4,
+                                  (131072, 65537, 32000, 4097), 64, 8, 128,
+                                  "bf16", 500000.0, 8.0, 16384)
+
+PREFILL_CONFIGS = {c.name: c for c in (TINY_F32, LLAMA2_7B_16K, LLAMA3_8B_128K,
+                                       LLAMA3_70B_RAGGED)}
+DECODE_CONFIGS = {DECODE_B16.name: DECODE_B16}
+
+
+# ---------------------------------------------------------------- bf16 bits
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even.
+    Inputs are finite standard normals, so no NaN/Inf handling is needed."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32)
+            << np.uint32(16)).view(np.float32)
+
+
+def as_f64(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """The exact fp64 values of stored inputs."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(arr).astype(np.float64)
+    return np.asarray(arr, dtype=np.float64)
+
+
+def _draw(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    """Standard normals of the given shape, stored as float32 (fp32 workloads)
+    or bf16 bits; drawn in row-major chunks from the one generator."""
+    n = int(np.prod(shape))
+    if dtype == "f32":
+        return rng.standard_normal(n, dtype=np.float32).reshape(shape)
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, _CHUNK):
+        e = min(n, s + _CHUNK)
+        out[s:e] = round_to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+    return out.reshape(shape)
+
+
+def cu_seqlens_of(seq_lens) -> np.ndarray:
+    cu = np.zeros(len(seq_lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(seq_lens, dtype=np.int64))
+    return cu
+
+
+def make_prefill(cfg: PrefillConfig, seed: int | None = None, seq_lens=None):
+    """Packed ragged prefill inputs: q [T, Hq, D], k, v [T, Hkv, D]."""
+    lens = tuple(cfg.seq_lens if seq_lens is None else seq_lens)
+    rng = np.random.Generator(np.random.PCG64(1000 + cfg.index if seed is None else seed))
+    T = int(sum(lens))
+    q = _draw(rng, (T, cfg.hq, cfg.head_dim), cfg.dtype)
+    k = _draw(rng, (T, cfg.hkv, cfg.head_dim), cfg.dtype)
+    v = _draw(rng, (T, cfg.hkv, cfg.head_dim), cfg.dtype)
+    return {"q": q, "k": k, "v": v, "cu_seqlens": cu_seqlens_of(lens),
+            "seq_lens": lens, "dtype": cfg.dtype}
+
+
+def make_decode(cfg: DecodeConfig, seed: int | None = None, batch=None,
+                max_cache_len=None, min_cache_len=None):
+    """Decode inputs: q [B, Hq, D]; k_cache, v_cache [B, Lmax, Hkv, D] with
+    NaN rows past each sequence's length; seqlens [B] ~ U{min..max}."""
+    B = cfg.batch if batch is None else batch
+    lmax = cfg.max_cache_len if max_cache_len is None else max_cache_len
+    lmin = cfg.min_cache_len if min_cache_len is None else min_cache_len
+    rng = np.random.Generator(np.random.PCG64(1000 + cfg.index if seed is None else seed))
+    seqlens = rng.integers(lmin, lmax, size=B, endpoint=True).astype(np.int32)
+    q = _draw(rng, (B, cfg.hq, cfg.head_dim), cfg.dtype)
+    caches = []
+    for _ in range(2):
+        if cfg.dtype == "bf16":
+            c = np.full((B, lmax, cfg.hkv, cfg.head_dim), BF16_NAN_BITS, dtype=np.uint16)
+        else:
+            c = np.full((B, lmax, cfg.hkv, cfg.head_dim), np.nan, dtype=np.float32)
+        for b in range(B):
+            c[b, :seqlens[b]] = _draw(rng, (int(seqlens[b]), cfg.hkv, cfg.head_dim), cfg.dtype)
+        caches.append(c)
+    return {"q": q, "k_cache": caches[0], "v_cache": caches[1],
+            "seqlens": seqlens, "dtype": cfg.dtype}
+
+
+def sample_rows(seq_lens, hq: int, hkv: int, n_random: int = 32, seed: int = 7,
+                edge_tiles=(32, 64, 128, 256), edge_span: int = 4):
+    """A seeded sample of (token, head) rows of a packed batch for checks at
+    sizes where the dense CPU result is too slow: per (sequence, KV group),
+    every query head of the group at rows 0-3, every tile edge (and its
+    neighbours) in the first ``edge_span`` tiles of each tile size, the last
+    three rows, every row of a partial last tile, and ``n_random`` random
+    rows."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    g = hq // hkv
+    out = []
+    start = 0
+    for n in seq_lens:
+        picks = set(range(min(4, n)))
+        for tsz in edge_tiles:
+            for e in range(1, edge_span + 1):
+                for dlt in (-1, 0, 1):
+                    r = e * tsz + dlt
+                    if 0 <= r < n:
+                        picks.add(r)
+        picks.update(range(max(0, n - 3), n))
+        tail = n % 128
+        if tail:
+            picks.update(range(n - tail, n))
+        for hk in range(hkv):
+            rr = set(picks)
+            if n > 0:
+                rr.update(int(x) for x in rng.integers(0, n, size=n_random))
+            for r in sorted(rr):
+                for h in range(hk * g, (hk + 1) * g):
+                    out.append((start + r, h))
+        start += n
+    return out
+
+
+# ------------------------------------------------------- algorithmic counts
+def prefill_causal_flops(seq_lens, hq: int, head_dim: int) -> int:
+    """Algorithmic FLOPs of causal prefill: QK^T and PV (2 FLOP per
+    multiply-add each) over every visible (query, key) pair, diagonal
+    included: 4 * D * Hq * sum n(n+1)/2."""
+    pairs = sum(int(n) * (int(n) + 1) // 2 for n in seq_lens)
+    return 4 * int(head_dim) * int(hq) * pairs
+
+
+def dense_attention_flops(seq_len: int, head_dim: int, heads: int = 1) -> int:
+    """Non-causal QK^T + PV FLOPs: 4 * T^2 * d per head."""
+    return 4 * int(seq_len) ** 2 * int(head_dim) * int(heads)
+
+
+def decode_kv_bytes(seqlens, hkv: int, head_dim: int, elem_bytes: int = 2) -> int:
+    """Bytes of K and V one decode step must read: 2 * Hkv * D * bytes per
+    cached token."""
+    return 2 * int(hkv) * int(head_dim) * int(elem_bytes) * int(np.sum(np.asarray(seqlens, dtype=np.int64)))
+
+
+def kv_cache_bytes(n_layers, n_kv_heads, head_dim, seq_len, batch=1, dtype_bytes=2) -> int:
+    """Whole-model KV cache size: layers * KV heads * head dim * 2 (K and V)
+    * tokens * batch * bytes per element."""
+    return (int(n_layers) * int(n_kv_heads) * int(head_dim) * 2 * int(seq_len)
+            * int(batch) * int(dtype_bytes))
+
+
+def score_matrix_bytes(seq_len: int, heads: int, dtype_bytes: int = 2) -> int:
+    """Bytes of a materialised T x T score matrix for all heads."""
+    return int(seq_len) ** 2 * int(heads) * int(dtype_bytes)
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-int(a) // int(b))
+
+
+def mean_decode_bytes(cfg: DecodeConfig, elem_bytes: int = 2) -> float:
+    """Expected K+V bytes of the decode workload for uniform cache lengths."""
+    mean_len = (cfg.min_cache_len + cfg.max_cache_len) / 2.0
+    return cfg.batch * mean_len * 2 * cfg.hkv * cfg.head_dim * elem_bytes
+
