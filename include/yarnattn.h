@@ -1,0 +1,199 @@
+/*
+ * yarnattn.h -- C ABI of libyarnattn.so: YaRN-scaled RoPE causal attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every function returns an int status (YR_OK = 0) and never throws or
+ *    aborts.  yr_status_string() names a status; yr_last_error() gives the
+ *    calling thread's message for its last failing call.
+ *  - Arguments are checked on the host before anything is launched; a failed
+ *    check launches nothing and writes nothing.
+ *  - Device pointers are caller-owned.  The library never allocates, frees or
+ *    synchronises: every launch is asynchronous on the caller's stream
+ *    (`stream` is a hipStream_t passed as void*; NULL is the null stream).
+ *    Scratch memory comes in as `workspace`, sized by the matching
+ *    *_workspace_bytes() query; its first 256 bytes are a header the kernels
+ *    use for a device-side error word.
+ *  - Values that only the device sees (cu_seqlens, seqlens, q_pos) are range
+ *    checked by the kernels: out-of-range values are clamped so that no
+ *    access leaves its buffer, and a flag is raised in the workspace header;
+ *    yr_read_device_error() reads it back.  Nothing is silently truncated
+ *    without that flag.
+ *  - Layouts are dense row-major with the last dimension contiguous.
+ *    Element types: YR_F32 (float) or YR_BF16 (bfloat16 bit patterns).
+ *  - Thread safety: the library keeps no global state besides the per-thread
+ *    error message; concurrent calls are safe when their outputs and
+ *    workspaces do not overlap.
+ *
+ * Sources are cited by page title and section ("Arch 03 -- Long Context"
+ * slide deck; "Long-context models", blog.ecitis.org; "LLM context window
+ * mechanics", randomcommits.com; "Long context (engineering 100k+ tokens)",
+ * askaiml academy).
+ */
+#ifndef YARNATTN_H
+#define YARNATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define YR_OK 0
+#define YR_ERR_INVALID 1      /* an argument is out of range or inconsistent  */
+#define YR_ERR_NULL 2         /* a required pointer is NULL                    */
+#define YR_ERR_UNSUPPORTED 3  /* valid, but not provided (head_dim, dtype pair) */
+#define YR_ERR_WORKSPACE 4    /* workspace missing or smaller than required    */
+#define YR_ERR_HIP 5          /* the HIP runtime reported an error             */
+#define YR_ERR_DEVICE_RANGE 6 /* device-side range check failed (see below)    */
+
+/* ---- element types ----------------------------------------------------- */
+#define YR_F32 0
+#define YR_BF16 1
+
+/* ---- frequency rules --------------------------------------------------- */
+#define YR_ROPE_PLAIN 0 /* theta_i = base^(-2i/d)                          */
+#define YR_ROPE_PI 1    /* theta_i / s                                     */
+#define YR_ROPE_NTK 2   /* plain rule over base * s^(d/(d-2))              */
+#define YR_ROPE_YARN 3  /* wavelength-ratio ramp between theta/s and theta */
+
+/* ---- device error bits (yr_read_device_error) -------------------------- */
+#define YR_DEVERR_CU_SEQLENS 1 /* cu_seqlens not 0 = c0 <= c1 <= ... <= cB = T, or a length > max_seqlen */
+#define YR_DEVERR_SEQLENS 2    /* a decode seqlens[b] outside [1, max_cache_len] */
+#define YR_DEVERR_QPOS 4       /* a decode q_pos[b] < 0                           */
+
+/* Bytes at the start of every workspace reserved for the device error word. */
+#define YR_WORKSPACE_HEADER_BYTES 256
+
+/*
+ * yarn_rope_freqs -- host-only: the rotary frequency table and the logit
+ * temperature.
+ *
+ * "Arch 03 -- Long Context": RoPE slide (theta_i = base^(-2i/d), one per
+ * feature pair (2i, 2i+1)), Position Interpolation slide (theta_i / s),
+ * NTK-aware slide (base * s^(d/(d-2))), YaRN slide and steps table (wavelength
+ * lambda_i = 2 pi / theta_i; alpha = 1, beta = 32; temperature
+ * t = 0.1 ln(s) + 1).  For YR_ROPE_YARN with r_i = L / lambda_i
+ * (L = original_max_position): r_i >= beta keeps theta_i, r_i <= alpha gives
+ * theta_i / s, and in between theta_i/s + gamma (theta_i - theta_i/s) with
+ * gamma = (r_i - alpha) / (beta - alpha).  All arithmetic is fp64; the fp32
+ * table is the round-to-nearest-even of the fp64 table.
+ *
+ *   head_dim               even, 2..1024 (rotary dim = head dim)
+ *   base                   > 1
+ *   factor                 s >= 1 (ignored by YR_ROPE_PLAIN)
+ *   original_max_position  L >= 1 (YR_ROPE_YARN only)
+ *   alpha, beta            0 <= alpha < beta (YR_ROPE_YARN only)
+ *   inv_freq_f32           host float[head_dim/2] or NULL
+ *   inv_freq_f64           host double[head_dim/2] or NULL (the table the
+ *                          kernels take, after the caller copies it to the
+ *                          device)
+ *   attn_factor            host double or NULL: t for YaRN, 1 otherwise
+ */
+int yarn_rope_freqs(int head_dim, double base, double factor,
+                    long long original_max_position, double alpha, double beta,
+                    int method, float *inv_freq_f32, double *inv_freq_f64,
+                    double *attn_factor);
+
+/*
+ * rope_apply -- rotate x in place: pair (2i, 2i+1) of row t turns by
+ * positions[t] * theta_i with R = [[cos, -sin], [sin, cos]] ("Arch 03 --
+ * Long Context", RoPE slide; "Long-context models", "Position enters
+ * attention").  The angle is formed and reduced modulo 2 pi in fp64; the
+ * rotation is applied in fp32 and bf16 results are rounded to nearest even.
+ *
+ *   x             device [T, H, head_dim], dtype YR_F32 or YR_BF16, in place
+ *   positions     device int32[T] (any value >= 0)
+ *   inv_freq_f64  device double[head_dim/2]
+ *   head_dim      even, 2..512
+ */
+int rope_apply(void *x, int dtype, long long T, int H, int head_dim,
+               const int *positions, const double *inv_freq_f64, void *stream);
+
+/* Workspace bytes attn_prefill_fwd needs for these sizes. */
+size_t attn_prefill_workspace_bytes(long long T, int Hkv, int head_dim, int in_dtype);
+
+/*
+ * attn_prefill_fwd -- causal prefill over a packed ragged batch: out and LSE.
+ *
+ * For each sequence b (rows cu_seqlens[b] .. cu_seqlens[b+1]-1, positions
+ * restarting at 0) and query head h with KV head h / (Hq / Hkv): q and k are
+ * rotated at their positions, z = softmax_scale * q~ . k~ for keys at or
+ * before the query ("Arch 03 -- Long Context", attention slide and the causal
+ * rule i - j >= 0 on the ALiBi slide), out = softmax(z) v and
+ * lse = ln sum exp(z).  The softmax runs tiled and online ("Long-context
+ * models", "Context parallelism distributes exact attention": per-row maxima,
+ * sums and output accumulators); no T x T score matrix is ever stored.
+ * Pass softmax_scale = t / sqrt(head_dim) for YaRN.
+ *
+ *   q              device [T, Hq, head_dim], unrotated
+ *   k, v           device [T, Hkv, head_dim], k unrotated
+ *   in_dtype       YR_BF16 (bf16 MFMA path) or YR_F32 (fp32 path)
+ *   cu_seqlens     device int32[B+1]: 0, c1, ..., cB = T; lengths <= max_seqlen
+ *                  (zero-length sequences are allowed and produce nothing)
+ *   inv_freq_f64   device double[head_dim/2], or NULL when q and k are already
+ *                  rotated
+ *   out            device [T, Hq, head_dim] of out_dtype (YR_F32 or YR_BF16;
+ *                  YR_F32 inputs require YR_F32 out)
+ *   lse            device float[Hq, T] or NULL
+ *   workspace      device, >= attn_prefill_workspace_bytes(T, Hkv, head_dim,
+ *                  in_dtype) bytes, 256-byte aligned; holds the rotated keys
+ *   head_dim       64 or 128;  Hq % Hkv == 0
+ */
+int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
+                     const int *cu_seqlens, int B, int max_seqlen, long long T,
+                     int Hq, int Hkv, int head_dim, const double *inv_freq_f64,
+                     float softmax_scale, void *out, int out_dtype, float *lse,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes attn_decode needs for these sizes. */
+size_t attn_decode_workspace_bytes(int B, int max_cache_len, int Hq, int head_dim);
+
+/*
+ * attn_decode -- one new query per sequence over a contiguous per-sequence KV
+ * cache (the cache is read in full every decode step: "Long Context",
+ * research hub, "Key math").  The query of sequence b is rotated at q_pos[b]
+ * (or at seqlens[b] when q_pos is NULL) and attends, unmasked, to cache rows
+ * 0 .. seqlens[b]-1, whose keys are taken as already rotated.  The cache is
+ * swept in fixed-size key chunks in parallel; each chunk yields a partial
+ * (out, LSE) and the partials are merged by log-sum-exp ("Long-context
+ * models", "Context parallelism distributes exact attention").
+ *
+ *   q               device [B, Hq, head_dim] (in_dtype), unrotated
+ *   k_cache,v_cache device [B, max_cache_len, Hkv, head_dim] (in_dtype)
+ *   in_dtype        YR_BF16 or YR_F32
+ *   seqlens         device int32[B], each in [1, max_cache_len]
+ *   q_pos           device int32[B] or NULL
+ *   inv_freq_f64    device double[head_dim/2], or NULL if q is already rotated
+ *   out             device [B, Hq, head_dim] of out_dtype (YR_F32 or YR_BF16)
+ *   lse             device float[B, Hq] or NULL
+ *   workspace       device, >= attn_decode_workspace_bytes(...) bytes,
+ *                   256-byte aligned; holds the partials
+ *   head_dim        64 or 128;  Hq % Hkv == 0;  Hq / Hkv <= 16
+ */
+int attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                int in_dtype, const int *seqlens, const int *q_pos, int B,
+                int max_cache_len, int Hq, int Hkv, int head_dim,
+                const double *inv_freq_f64, float softmax_scale, void *out,
+                int out_dtype, float *lse, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+/*
+ * yr_read_device_error -- synchronise `stream`, read the device error word of
+ * `workspace` (written by the last prefill/decode call that used it) into
+ * *flags (YR_DEVERR_* bits).  Returns YR_ERR_DEVICE_RANGE if any bit is set.
+ */
+int yr_read_device_error(const void *workspace, void *stream, int *flags);
+
+const char *yr_status_string(int status);
+const char *yr_last_error(void);
+/* Library version as major*10000 + minor*100 + patch. */
+int yr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* YARNATTN_H */

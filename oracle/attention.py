@@ -104,9 +104,8 @@ def prefill_rows(q, k, v, cu_seqlens, theta, scale, rows):
     each over its full causal prefix.  ``rows`` is an iterable of
     (global token index, query head).  Returns (out [R, D], lse [R]) in the
     order given."""
-    q = np.asarray(q)
-    k = np.asarray(k)
-    v = np.asarray(v)
+    # q, k, v are only sliced here, so any array-like with numpy indexing and
+    # .shape will do (large inputs can be widened slice by slice)
     hq = q.shape[1]
     hkv = k.shape[1]
     g = _group(hq, hkv)
@@ -129,16 +128,21 @@ def prefill_rows(q, k, v, cu_seqlens, theta, scale, rows):
         vv = np.asarray(v[s0:s0 + last + 1, hk, :], dtype=np.float64)
         if theta is not None:
             kk = rotate(kk, np.arange(last + 1), theta)
-        for i in idxs:
-            t, h = rows[i]
-            m = t - s0
-            qr = np.asarray(q[t, h, :], dtype=np.float64)[None, :]
+        # the rows of one group share their keys: form their logits together,
+        # each row over its own causal prefix (later keys set to -inf)
+        for c0 in range(0, len(idxs), 256):
+            part = idxs[c0:c0 + 256]
+            pos = np.array([rows[i][0] - s0 for i in part])
+            qr = np.stack([np.asarray(q[rows[i][0], rows[i][1], :], dtype=np.float64)
+                           for i in part])
             if theta is not None:
-                qr = rotate(qr, [m], theta)
-            z = scale * (qr @ kk[:m + 1].T)
-            o, l = attend(z, vv[:m + 1])
-            out[i] = o[0]
-            lse[i] = l[0]
+                qr = rotate(qr, pos, theta)
+            span = int(pos.max()) + 1
+            z = scale * (qr @ kk[:span].T)
+            z[np.arange(span)[None, :] > pos[:, None]] = -np.inf
+            o, l = attend(z, vv[:span])
+            out[part] = o
+            lse[part] = l
     return out, lse
 
 

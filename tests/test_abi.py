@@ -1,0 +1,179 @@
+"""The C-ABI library on the host (CPU only): it loads, exports every symbol the
+header declares, rejects bad arguments before launching anything, and its
+host-side frequency table matches the oracle bit for bit."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import freqs as ofreqs
+from yarn_scaled_rope_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "yarnattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        pytest.fail("libyarnattn.so is not built (run `python -m yarn_scaled_rope_amd.build`)")
+    return ops.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert {"yarn_rope_freqs", "rope_apply", "attn_prefill_fwd", "attn_decode",
+            "attn_prefill_workspace_bytes", "attn_decode_workspace_bytes",
+            "yr_read_device_error", "yr_status_string", "yr_last_error", "yr_version"} <= set(names)
+    raw = ctypes.CDLL(ops.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings(lib):
+    assert lib.yr_status_string(0) == b"ok"
+    assert b"workspace" in lib.yr_status_string(ops.YR_ERR_WORKSPACE)
+    assert lib.yr_version() >= 100
+
+
+CONFIGS = [
+    (64, 10000.0, 4.0, 64),
+    (128, 10000.0, 4.0, 4096),
+    (128, 500000.0, 8.0, 16384),
+    (128, 10000.0, 1.0, 4096),
+    (128, 10000.0, 8.0, 2048),
+    (64, 500000.0, 16.0, 8192),
+    (256, 1000000.0, 32.0, 32768),
+]
+
+
+@pytest.mark.parametrize("d,base,s,L", CONFIGS)
+@pytest.mark.parametrize("method", ["plain", "pi", "ntk", "yarn"])
+def test_freqs_bit_exact_vs_oracle(lib, d, base, s, L, method):
+    f32, f64, t = ops.yarn_rope_freqs(d, base, s, L, 1.0, 32.0, method)
+    ref = ofreqs.theta_for(method, d, base, s, L)
+    assert np.array_equal(f32, ofreqs.to_fp32(ref)), (f32, ofreqs.to_fp32(ref))
+    ulps = np.abs(f64 - ref) / np.spacing(ref)
+    assert np.max(ulps) <= 4
+    assert t == pytest.approx(ofreqs.temperature_for(method, s), rel=1e-15)
+
+
+def test_freqs_s1_is_plain_bitwise(lib):
+    a32, a64, t = ops.yarn_rope_freqs(128, 500000.0, 1.0, 16384)
+    b32, b64, _ = ops.yarn_rope_freqs(128, 500000.0, 1.0, 16384, method="plain")
+    assert np.array_equal(a64, b64) and np.array_equal(a32, b32) and t == 1.0
+
+
+@pytest.mark.parametrize("args", [
+    (63, 10000.0, 4.0, 64, 1.0, 32.0, "yarn"),       # odd head_dim
+    (0, 10000.0, 4.0, 64, 1.0, 32.0, "yarn"),
+    (64, 1.0, 4.0, 64, 1.0, 32.0, "yarn"),           # base <= 1
+    (64, 10000.0, 0.5, 64, 1.0, 32.0, "yarn"),       # s < 1
+    (64, 10000.0, 0.5, 64, 1.0, 32.0, "pi"),
+    (64, 10000.0, 4.0, 0, 1.0, 32.0, "yarn"),        # L < 1
+    (64, 10000.0, 4.0, 64, 32.0, 32.0, "yarn"),      # alpha >= beta
+    (64, 10000.0, float("nan"), 64, 1.0, 32.0, "ntk"),
+])
+def test_freqs_rejects(lib, args):
+    with pytest.raises(ops.YarnAttnError) as e:
+        ops.yarn_rope_freqs(*args)
+    assert e.value.status == ops.YR_ERR_INVALID
+
+
+FAKE = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+WS = ctypes.c_void_p(1 << 20)     # 256-byte aligned fake workspace
+
+
+def prefill_call(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, in_dtype=ops.YR_BF16, cu=FAKE, B=1, max_seqlen=16, T=16,
+             Hq=4, Hkv=2, D=128, theta=FAKE, scale=0.1, out=FAKE, out_dtype=ops.YR_BF16,
+             lse=FAKE, ws=WS, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.attn_prefill_fwd(a["q"], a["k"], a["v"], a["in_dtype"], a["cu"], a["B"],
+                                a["max_seqlen"], a["T"], a["Hq"], a["Hkv"], a["D"], a["theta"],
+                                a["scale"], a["out"], a["out_dtype"], a["lse"], a["ws"],
+                                a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), ops.YR_ERR_UNSUPPORTED),
+    (dict(D=256), ops.YR_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), ops.YR_ERR_INVALID),
+    (dict(Hkv=0), ops.YR_ERR_INVALID),
+    (dict(B=0), ops.YR_ERR_INVALID),
+    (dict(max_seqlen=0), ops.YR_ERR_INVALID),
+    (dict(T=-1), ops.YR_ERR_INVALID),
+    (dict(scale=0.0), ops.YR_ERR_INVALID),
+    (dict(scale=float("inf")), ops.YR_ERR_INVALID),
+    (dict(in_dtype=7), ops.YR_ERR_UNSUPPORTED),
+    (dict(in_dtype=ops.YR_F32, out_dtype=ops.YR_BF16), ops.YR_ERR_UNSUPPORTED),
+    (dict(q=None), ops.YR_ERR_NULL),
+    (dict(cu=None), ops.YR_ERR_NULL),
+    (dict(out=None), ops.YR_ERR_NULL),
+    (dict(ws=None), ops.YR_ERR_NULL),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 16)), ops.YR_ERR_WORKSPACE),
+    (dict(ws_bytes=100), ops.YR_ERR_WORKSPACE),
+    (dict(T=1 << 20, ws_bytes=(1 << 20) * 2 * 128 * 2), ops.YR_ERR_WORKSPACE),
+])
+def test_prefill_rejects_before_launch(lib, kw, status):
+    assert prefill_call(lib, **kw) == status
+    assert lib.yr_last_error()
+
+
+def decode_call(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, in_dtype=ops.YR_BF16, seqlens=FAKE, qpos=None, B=2,
+             Lmax=1024, Hq=8, Hkv=2, D=128, theta=FAKE, scale=0.1, out=FAKE,
+             out_dtype=ops.YR_BF16, lse=FAKE, ws=WS, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.attn_decode(a["q"], a["kc"], a["vc"], a["in_dtype"], a["seqlens"], a["qpos"],
+                           a["B"], a["Lmax"], a["Hq"], a["Hkv"], a["D"], a["theta"], a["scale"],
+                           a["out"], a["out_dtype"], a["lse"], a["ws"], a["ws_bytes"],
+                           a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=80), ops.YR_ERR_UNSUPPORTED),
+    (dict(Hq=8, Hkv=3), ops.YR_ERR_INVALID),
+    (dict(Hq=64, Hkv=2), ops.YR_ERR_UNSUPPORTED),
+    (dict(B=0), ops.YR_ERR_INVALID),
+    (dict(Lmax=0), ops.YR_ERR_INVALID),
+    (dict(scale=-1.0), ops.YR_ERR_INVALID),
+    (dict(out_dtype=3), ops.YR_ERR_UNSUPPORTED),
+    (dict(seqlens=None), ops.YR_ERR_NULL),
+    (dict(kc=None), ops.YR_ERR_NULL),
+    (dict(ws_bytes=512), ops.YR_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 8)), ops.YR_ERR_WORKSPACE),
+])
+def test_decode_rejects_before_launch(lib, kw, status):
+    assert decode_call(lib, **kw) == status
+
+
+def test_rope_rejects_and_empty(lib):
+    assert lib.rope_apply(FAKE, ops.YR_BF16, 4, 2, 7, FAKE, FAKE, None) == ops.YR_ERR_INVALID
+    assert lib.rope_apply(FAKE, 9, 4, 2, 8, FAKE, FAKE, None) == ops.YR_ERR_UNSUPPORTED
+    assert lib.rope_apply(None, ops.YR_BF16, 4, 2, 8, FAKE, FAKE, None) == ops.YR_ERR_NULL
+    assert lib.rope_apply(None, ops.YR_BF16, 0, 2, 8, None, None, None) == ops.YR_OK  # nothing to do
+
+
+def test_workspace_sizes(lib):
+    assert ops.attn_prefill_workspace_bytes(1000, 8, 128, ops.YR_BF16) == 256 + 1000 * 8 * 128 * 2
+    assert ops.attn_prefill_workspace_bytes(10, 1, 64, ops.YR_F32) == 256 + 2560
+    n = ops.attn_decode_workspace_bytes(16, 131072, 32, 128)
+    assert n > 16 * 32 * 128 * 4 and n % 256 == 0
+    # larger caches never need less
+    assert ops.attn_decode_workspace_bytes(16, 262144, 32, 128) >= n
+
+
+def test_missing_library_raises(monkeypatch, tmp_path):
+    monkeypatch.setattr(ops, "_lib", None)
+    with pytest.raises(ops.YarnAttnError):
+        ops.load_library(str(tmp_path / "nope.so"))

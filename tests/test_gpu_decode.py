@@ -1,0 +1,126 @@
+"""attn_decode on the GPU against the oracle: small caches in full, the full
+16-sequence 32K-128K workload in full, NaN-poisoned cache tails, the
+decode/prefill cross-check, bad seqlens, and determinism."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oatt
+from tests._gpu_util import (BF16_TOL, F32_TOL, LazyF64, lib_theta, max_abs, oracle_theta, say,
+                             to_dev, to_f64)
+from yarn_scaled_rope_amd import ops
+from yarn_scaled_rope_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, cfg, out_dtype=None, q_pos=None):
+    dt = inp["dtype"]
+    th_dev, scale = lib_theta(cfg.head_dim, cfg.base, cfg.factor, cfg.original_max_position)
+    q = to_dev(inp["q"], dt)
+    kc = to_dev(inp["k_cache"], dt)
+    vc = to_dev(inp["v_cache"], dt)
+    sl = torch.from_numpy(inp["seqlens"]).cuda()
+    qp = None if q_pos is None else torch.from_numpy(np.asarray(q_pos, dtype=np.int32)).cuda()
+    out, lse = ops.attn_decode(q, kc, vc, sl, th_dev, scale, q_pos=qp, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return to_f64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def _oracle(inp, cfg, q_pos=None):
+    th, scale = oracle_theta(cfg.head_dim, cfg.base, cfg.factor, cfg.original_max_position)
+    dt = inp["dtype"]
+    return oatt.decode(wl.as_f64(inp["q"], dt), LazyF64(inp["k_cache"], dt),
+                       LazyF64(inp["v_cache"], dt), inp["seqlens"], th, scale, q_pos=q_pos)
+
+
+def _cfg(dtype, hq, hkv, D):
+    return wl.DecodeConfig("t", 80, 0, 0, 0, hq, hkv, D, dtype, 500000.0, 8.0, 16384)
+
+
+@pytest.mark.parametrize("dtype,B,lmax,lmin,hq,hkv,D,out_dtype", [
+    ("bf16", 5, 300, 1, 8, 2, 128, ops.YR_BF16),
+    ("bf16", 3, 5000, 1000, 32, 8, 128, ops.YR_F32),
+    ("bf16", 4, 2100, 1, 4, 4, 64, ops.YR_BF16),
+    ("bf16", 2, 700, 600, 16, 2, 128, ops.YR_BF16),
+    ("f32", 4, 3000, 1, 8, 2, 128, ops.YR_F32),
+    ("f32", 3, 257, 1, 4, 1, 64, ops.YR_F32),
+])
+def test_decode_small_full(dtype, B, lmax, lmin, hq, hkv, D, out_dtype):
+    cfg = _cfg(dtype, hq, hkv, D)
+    inp = wl.make_decode(cfg, seed=90 + B, batch=B, max_cache_len=lmax, min_cache_len=lmin)
+    say(f"decode {dtype} B={B} Lmax={lmax} hq={hq} hkv={hkv} D={D} seqlens={list(inp['seqlens'])}")
+    out, lse = _run(inp, cfg, out_dtype=out_dtype)
+    ro, rl = _oracle(inp, cfg)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    tol = F32_TOL if dtype == "f32" else BF16_TOL
+    e_out, e_lse = max_abs(out, ro), max_abs(lse, rl)
+    print(f"max-abs out {e_out:.3e} lse {e_lse:.3e}")
+    assert e_out <= tol and e_lse <= tol
+
+
+def test_decode_workload_full():
+    cfg = wl.DECODE_B16
+    inp = wl.make_decode(cfg)
+    say(f"decode {cfg.name} full, seqlens={list(inp['seqlens'])}")
+    out, lse = _run(inp, cfg)
+    ro, rl = _oracle(inp, cfg)
+    assert np.all(np.isfinite(out))
+    e_out, e_lse = max_abs(out, ro), max_abs(lse, rl)
+    print(f"{cfg.name}: max-abs out {e_out:.3e} lse {e_lse:.3e}")
+    assert e_out <= BF16_TOL and e_lse <= BF16_TOL
+
+
+def test_decode_matches_prefill_last_row():
+    """Decode at q_pos = L-1 over the keys rotated by rope_apply equals row
+    L-1 of prefill over the same unrotated inputs."""
+    L, hq, hkv, D = 1500, 8, 2, 128
+    cfg = wl.PrefillConfig("t", 81, (L,), hq, hkv, D, "bf16", 500000.0, 8.0, 64)
+    inp = wl.make_prefill(cfg)
+    th_dev, scale = lib_theta(D, cfg.base, cfg.factor, cfg.original_max_position)
+    q, k, v = to_dev(inp["q"], "bf16"), to_dev(inp["k"], "bf16"), to_dev(inp["v"], "bf16")
+    say("decode vs prefill last row")
+    pout, plse = ops.attn_prefill_fwd(q, k, v, torch.from_numpy(inp["cu_seqlens"]).cuda(), L,
+                                      th_dev, scale, out_dtype=ops.YR_F32)
+    kr = k.clone()
+    ops.rope_apply(kr, torch.arange(L, dtype=torch.int32, device="cuda"), th_dev)
+    dout, dlse = ops.attn_decode(q[L - 1:L].contiguous(), kr[None].contiguous(), v[None].contiguous(),
+                                 torch.tensor([L], dtype=torch.int32, device="cuda"), th_dev, scale,
+                                 q_pos=torch.tensor([L - 1], dtype=torch.int32, device="cuda"),
+                                 out_dtype=ops.YR_F32)
+    torch.cuda.synchronize()
+    # both sides round q~ and k~ to bf16 identically; they differ only in how
+    # P is rounded (prefill feeds bf16 P to the matrix cores) and summed
+    assert max_abs(to_f64(dout[0]), to_f64(pout[L - 1])) <= BF16_TOL
+    assert max_abs(dlse[0].cpu().numpy(), plse[:, L - 1].cpu().numpy()) <= 1e-3
+
+
+def test_decode_bad_seqlens_sets_flag():
+    B, lmax, hq, hkv, D = 3, 512, 8, 2, 128
+    th_dev, scale = lib_theta(D, 500000.0, 8.0, 16384)
+    q = torch.randn(B, hq, D, device="cuda").to(torch.bfloat16)
+    kc = torch.randn(B, lmax, hkv, D, device="cuda").to(torch.bfloat16)
+    vc = torch.randn(B, lmax, hkv, D, device="cuda").to(torch.bfloat16)
+    ws = torch.empty(ops.attn_decode_workspace_bytes(B, lmax, hq, D), dtype=torch.uint8,
+                     device="cuda")
+    for sl, bit in (([5, 512, 1], 0), ([0, 10, 10], ops.YR_DEVERR_SEQLENS),
+                    ([5, 513, 7], ops.YR_DEVERR_SEQLENS), ([5, -3, 7], ops.YR_DEVERR_SEQLENS)):
+        say(f"decode device flag seqlens={sl}")
+        out, _ = ops.attn_decode(q, kc, vc, torch.tensor(sl, dtype=torch.int32, device="cuda"),
+                                 th_dev, scale, workspace=ws)
+        assert ops.read_device_error(ws) == bit
+    say("decode device flag q_pos<0")
+    ops.attn_decode(q, kc, vc, torch.tensor([5, 6, 7], dtype=torch.int32, device="cuda"), th_dev,
+                    scale, q_pos=torch.tensor([1, -1, 2], dtype=torch.int32, device="cuda"),
+                    workspace=ws)
+    assert ops.read_device_error(ws) == ops.YR_DEVERR_QPOS
+
+
+def test_decode_deterministic():
+    cfg = _cfg("bf16", 32, 8, 128)
+    inp = wl.make_decode(cfg, seed=5, batch=4, max_cache_len=9000, min_cache_len=3000)
+    say("decode determinism")
+    a = _run(inp, cfg)
+    b = _run(inp, cfg)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

@@ -1,0 +1,190 @@
+"""attn_prefill_fwd on the GPU against the oracle: full element-by-element
+checks at sizes the oracle finishes in seconds (several tiles, ragged tails,
+1-row sequences), sampled rows at the full workload sizes, and the edge
+cases: out-of-range rows poisoned with NaN, bad cu_seqlens, determinism and
+GQA against repeated heads."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oatt
+from tests._gpu_util import (BF16_TOL, F32_TOL, LazyF64, lib_theta, max_abs, oracle_theta, say,
+                             to_dev, to_f64)
+from yarn_scaled_rope_amd import ops
+from yarn_scaled_rope_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, hq, hkv, D, base, s, L, out_dtype=None, pad_rows=0):
+    """Upload, run the library, return (out, lse) as fp64 numpy."""
+    dt = inp["dtype"]
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    T = q.shape[0]
+    th_dev, scale = lib_theta(D, base, s, L)
+    cu = torch.from_numpy(inp["cu_seqlens"]).cuda()
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    if pad_rows:
+        # rows past T hold NaN: any read beyond the packed batch shows up
+        def pad(t):
+            big = torch.full((T + pad_rows,) + tuple(t.shape[1:]), float("nan"), dtype=t.dtype,
+                             device=t.device)
+            big[:T] = t
+            return big
+        qd, kd, vd = pad(qd), pad(kd), pad(vd)
+        qd, kd, vd = qd[:T], kd[:T], vd[:T]   # views: same storage, NaN beyond
+    out, lse = ops.attn_prefill_fwd(qd, kd, vd, cu, max(inp["seq_lens"]), th_dev, scale,
+                                    out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return to_f64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def _oracle(inp, D, base, s, L):
+    th, scale = oracle_theta(D, base, s, L)
+    dt = inp["dtype"]
+    return oatt.prefill(wl.as_f64(inp["q"], dt), wl.as_f64(inp["k"], dt), wl.as_f64(inp["v"], dt),
+                        inp["cu_seqlens"], th, scale)
+
+
+def test_tiny_fp32_workload_full():
+    cfg = wl.TINY_F32
+    inp = wl.make_prefill(cfg)
+    say(f"prefill {cfg.name}")
+    out, lse = _run(inp, cfg.hq, cfg.hkv, cfg.head_dim, cfg.base, cfg.factor, cfg.original_max_position)
+    ro, rl = _oracle(inp, cfg.head_dim, cfg.base, cfg.factor, cfg.original_max_position)
+    assert max_abs(out, ro) <= F32_TOL
+    assert max_abs(lse, rl) <= F32_TOL
+
+
+@pytest.mark.parametrize("lens,hq,hkv,D", [
+    ((1, 100, 250, 64), 4, 2, 64),
+    ((129, 3, 200), 8, 2, 128),
+    ((65,), 2, 2, 128),
+])
+def test_fp32_ragged(lens, hq, hkv, D):
+    cfg = wl.PrefillConfig("t", 50, lens, hq, hkv, D, "f32", 500000.0, 8.0, 32)
+    inp = wl.make_prefill(cfg)
+    say(f"prefill f32 lens={lens} hq={hq} hkv={hkv} D={D}")
+    out, lse = _run(inp, hq, hkv, D, cfg.base, cfg.factor, cfg.original_max_position, pad_rows=64)
+    ro, rl = _oracle(inp, D, cfg.base, cfg.factor, cfg.original_max_position)
+    assert max_abs(out, ro) <= F32_TOL
+    assert max_abs(lse, rl) <= F32_TOL
+
+
+@pytest.mark.parametrize("lens,hq,hkv,D,out_dtype", [
+    ((1, 129, 300, 64), 8, 2, 128, ops.YR_BF16),
+    ((1, 129, 300, 64), 8, 2, 128, ops.YR_F32),
+    ((511, 2, 255), 4, 4, 128, ops.YR_BF16),
+    ((700,), 8, 1, 64, ops.YR_BF16),
+    ((33, 1, 1, 160), 16, 2, 64, ops.YR_F32),
+    ((1000,), 2, 1, 128, ops.YR_BF16),
+])
+def test_bf16_ragged_full(lens, hq, hkv, D, out_dtype):
+    cfg = wl.PrefillConfig("t", 60, lens, hq, hkv, D, "bf16", 500000.0, 8.0, 64)
+    inp = wl.make_prefill(cfg)
+    say(f"prefill bf16 lens={lens} hq={hq} hkv={hkv} D={D} out={out_dtype}")
+    out, lse = _run(inp, hq, hkv, D, cfg.base, cfg.factor, cfg.original_max_position,
+                    out_dtype=out_dtype, pad_rows=128)
+    ro, rl = _oracle(inp, D, cfg.base, cfg.factor, cfg.original_max_position)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    e_out, e_lse = max_abs(out, ro), max_abs(lse, rl)
+    print(f"max-abs out {e_out:.3e} lse {e_lse:.3e}")
+    assert e_out <= BF16_TOL and e_lse <= BF16_TOL
+
+
+def _sampled(cfg, n_random):
+    inp = wl.make_prefill(cfg)
+    say(f"prefill {cfg.name} full size, sampled rows")
+    out, lse = _run(inp, cfg.hq, cfg.hkv, cfg.head_dim, cfg.base, cfg.factor,
+                    cfg.original_max_position)
+    rows = wl.sample_rows(cfg.seq_lens, cfg.hq, cfg.hkv, n_random=n_random)
+    th, scale = oracle_theta(cfg.head_dim, cfg.base, cfg.factor, cfg.original_max_position)
+    dt = inp["dtype"]
+    ro, rl = oatt.prefill_rows(LazyF64(inp["q"], dt), LazyF64(inp["k"], dt),
+                               LazyF64(inp["v"], dt),
+                               inp["cu_seqlens"], th, scale, rows)
+    got_o = np.stack([out[t, h] for t, h in rows])
+    got_l = np.array([lse[h, t] for t, h in rows])
+    e_out, e_lse = max_abs(got_o, ro), max_abs(got_l, rl)
+    print(f"{cfg.name}: {len(rows)} rows, max-abs out {e_out:.3e} lse {e_lse:.3e}")
+    assert np.all(np.isfinite(out))
+    assert e_out <= BF16_TOL and e_lse <= BF16_TOL
+
+
+def test_llama2_7b_16k_sampled():
+    _sampled(wl.LLAMA2_7B_16K, n_random=16)
+
+
+def test_llama3_8b_128k_sampled():
+    _sampled(wl.LLAMA3_8B_128K, n_random=8)
+
+
+def test_llama3_70b_ragged_sampled():
+    _sampled(wl.LLAMA3_70B_RAGGED, n_random=4)
+
+
+def test_gqa_equals_repeated_heads_on_gpu():
+    cfg = wl.PrefillConfig("t", 70, (300, 77), 8, 2, 128, "bf16", 10000.0, 4.0, 64)
+    inp = wl.make_prefill(cfg)
+    say("prefill GQA vs repeated heads")
+    a_out, a_lse = _run(inp, 8, 2, 128, cfg.base, cfg.factor, cfg.original_max_position)
+    rep = dict(inp)
+    rep["k"] = np.repeat(inp["k"], 4, axis=1)
+    rep["v"] = np.repeat(inp["v"], 4, axis=1)
+    b_out, b_lse = _run(rep, 8, 8, 128, cfg.base, cfg.factor, cfg.original_max_position)
+    assert np.array_equal(a_out, b_out) and np.array_equal(a_lse, b_lse)
+
+
+def test_deterministic():
+    cfg = wl.PrefillConfig("t", 71, (999, 130), 8, 2, 128, "bf16", 500000.0, 8.0, 16384)
+    inp = wl.make_prefill(cfg)
+    say("prefill determinism")
+    a = _run(inp, 8, 2, 128, cfg.base, cfg.factor, cfg.original_max_position)
+    b = _run(inp, 8, 2, 128, cfg.base, cfg.factor, cfg.original_max_position)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_bad_cu_seqlens_sets_device_flag():
+    T, hq, hkv, D = 256, 4, 2, 128
+    th_dev, scale = lib_theta(D, 10000.0, 4.0, 64)
+    q = torch.randn(T, hq, D, device="cuda").to(torch.bfloat16)
+    k = torch.randn(T, hkv, D, device="cuda").to(torch.bfloat16)
+    v = torch.randn(T, hkv, D, device="cuda").to(torch.bfloat16)
+    ws = torch.empty(ops.attn_prefill_workspace_bytes(T, hkv, D, ops.YR_BF16), dtype=torch.uint8,
+                     device="cuda")
+    good = torch.tensor([0, 100, 256], dtype=torch.int32, device="cuda")
+    say("prefill device flag: good cu_seqlens")
+    ops.attn_prefill_fwd(q, k, v, good, 156, th_dev, scale, workspace=ws)
+    assert ops.read_device_error(ws) == 0
+    # last entry short of T, then a decreasing pair, then a length above
+    # max_seqlen: the kernels clamp (no access leaves the buffers) and flag it
+    for bad, ms in (([0, 100, 200], 156), ([0, 150, 100, 256], 156), ([0, 256], 128)):
+        say(f"prefill device flag: cu_seqlens={bad}")
+        cu = torch.tensor(bad, dtype=torch.int32, device="cuda")
+        out, _ = ops.attn_prefill_fwd(q, k, v, cu, ms, th_dev, scale, workspace=ws)
+        assert ops.read_device_error(ws) == ops.YR_DEVERR_CU_SEQLENS
+    # and the flag clears on the next good call
+    ops.attn_prefill_fwd(q, k, v, good, 156, th_dev, scale, workspace=ws)
+    assert ops.read_device_error(ws) == 0
+    # already-rotated inputs (no key pass): the attention kernel itself checks
+    cu = torch.tensor([0, 100, 200], dtype=torch.int32, device="cuda")
+    ops.attn_prefill_fwd(q, k, v, cu, 156, None, scale, workspace=ws)
+    assert ops.read_device_error(ws) == ops.YR_DEVERR_CU_SEQLENS
+
+
+def test_prerotated_inputs_equal_fused_rotation():
+    cfg = wl.PrefillConfig("t", 72, (400, 50), 4, 2, 128, "bf16", 500000.0, 8.0, 64)
+    inp = wl.make_prefill(cfg)
+    th_dev, scale = lib_theta(128, cfg.base, cfg.factor, cfg.original_max_position)
+    cu = torch.from_numpy(inp["cu_seqlens"]).cuda()
+    q, k, v = to_dev(inp["q"], "bf16"), to_dev(inp["k"], "bf16"), to_dev(inp["v"], "bf16")
+    say("prefill fused vs pre-rotated")
+    a, al = ops.attn_prefill_fwd(q, k, v, cu, 400, th_dev, scale)
+    pos = torch.cat([torch.arange(400), torch.arange(50)]).to(torch.int32).cuda()
+    qr, kr = q.clone(), k.clone()
+    ops.rope_apply(qr, pos, th_dev)
+    ops.rope_apply(kr, pos, th_dev)
+    b, bl = ops.attn_prefill_fwd(qr, kr, v, cu, 400, None, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(al, bl)

@@ -1,0 +1,247 @@
+// C-ABI entry points of libyarnattn.so: host-side validation, workspace
+// layout and kernel launches.  Every entry point checks its arguments before
+// touching the device, returns a status and never throws.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "yarnattn.h"
+#include "yr_internal.h"
+
+namespace yr {
+
+namespace {
+thread_local std::string g_last_error;
+
+constexpr size_t kHeader = YR_WORKSPACE_HEADER_BYTES;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool dims_ok(int head_dim) { return head_dim == 64 || head_dim == 128; }
+
+int *flag_of(void *ws) { return static_cast<int *>(ws); }
+}  // namespace
+
+int fail(int status, const char *msg) {
+  g_last_error = msg ? msg : "";
+  return status;
+}
+
+int fail_hip(hipError_t err, const char *where) {
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), "%s: HIP error %d (%s)", where, (int)err, hipGetErrorString(err));
+  g_last_error = buf;
+  return YR_ERR_HIP;
+}
+
+}  // namespace yr
+
+using namespace yr;
+
+extern "C" {
+
+const char *yr_status_string(int status) {
+  switch (status) {
+    case YR_OK: return "ok";
+    case YR_ERR_INVALID: return "invalid argument";
+    case YR_ERR_NULL: return "null pointer";
+    case YR_ERR_UNSUPPORTED: return "unsupported configuration";
+    case YR_ERR_WORKSPACE: return "workspace too small";
+    case YR_ERR_HIP: return "HIP runtime error";
+    case YR_ERR_DEVICE_RANGE: return "device-side range check failed";
+    default: return "unknown status";
+  }
+}
+
+const char *yr_last_error(void) { return g_last_error.c_str(); }
+
+int yr_version(void) { return 100; }
+
+int rope_apply(void *x, int dtype, long long T, int H, int head_dim, const int *positions,
+               const double *inv_freq_f64, void *stream) {
+  if (dtype != YR_F32 && dtype != YR_BF16) return fail(YR_ERR_UNSUPPORTED, "rope_apply: dtype");
+  if (T < 0 || H < 1 || head_dim < 2 || head_dim > 512 || (head_dim & 1))
+    return fail(YR_ERR_INVALID, "rope_apply: need T >= 0, H >= 1, even head_dim in [2, 512]");
+  if (T == 0) return YR_OK;
+  if (!x || !positions || !inv_freq_f64) return fail(YR_ERR_NULL, "rope_apply: null pointer");
+  if (T * (long long)H * head_dim > (1LL << 46))
+    return fail(YR_ERR_INVALID, "rope_apply: tensor too large");
+  RopeArgs a{};
+  a.src = x;
+  a.dst = x;
+  a.dtype = dtype;
+  a.T = T;
+  a.H = H;
+  a.head_dim = head_dim;
+  a.positions = positions;
+  a.theta = inv_freq_f64;
+  const hipError_t e = launch_rope(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "rope_apply");
+  return YR_OK;
+}
+
+size_t attn_prefill_workspace_bytes(long long T, int Hkv, int head_dim, int in_dtype) {
+  if (T < 0 || Hkv < 1 || head_dim < 1) return kHeader;
+  const size_t elem = in_dtype == YR_F32 ? 4 : 2;
+  return kHeader + align_up((size_t)T * (size_t)Hkv * (size_t)head_dim * elem, 256);
+}
+
+int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
+                     const int *cu_seqlens, int B, int max_seqlen, long long T, int Hq, int Hkv,
+                     int head_dim, const double *inv_freq_f64, float softmax_scale, void *out,
+                     int out_dtype, float *lse, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+  if (in_dtype != YR_F32 && in_dtype != YR_BF16)
+    return fail(YR_ERR_UNSUPPORTED, "attn_prefill_fwd: in_dtype must be YR_F32 or YR_BF16");
+  if (out_dtype != YR_F32 && out_dtype != YR_BF16)
+    return fail(YR_ERR_UNSUPPORTED, "attn_prefill_fwd: out_dtype must be YR_F32 or YR_BF16");
+  if (in_dtype == YR_F32 && out_dtype != YR_F32)
+    return fail(YR_ERR_UNSUPPORTED, "attn_prefill_fwd: fp32 inputs need fp32 output");
+  if (!dims_ok(head_dim)) return fail(YR_ERR_UNSUPPORTED, "attn_prefill_fwd: head_dim must be 64 or 128");
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return fail(YR_ERR_INVALID, "attn_prefill_fwd: need Hq >= 1, Hkv >= 1, Hq % Hkv == 0");
+  if (B < 1 || T < 0 || max_seqlen < 1)
+    return fail(YR_ERR_INVALID, "attn_prefill_fwd: need B >= 1, T >= 0, max_seqlen >= 1");
+  if (max_seqlen > (1 << 24) || T > (1LL << 31) - 1)
+    return fail(YR_ERR_INVALID, "attn_prefill_fwd: max_seqlen or T too large");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(YR_ERR_INVALID, "attn_prefill_fwd: softmax_scale must be finite and > 0");
+  if (!q || !k || !v || !cu_seqlens || !out || !workspace)
+    return fail(YR_ERR_NULL, "attn_prefill_fwd: q, k, v, cu_seqlens, out and workspace are required");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return fail(YR_ERR_WORKSPACE, "attn_prefill_fwd: workspace must be 256-byte aligned");
+  const size_t need = inv_freq_f64 ? attn_prefill_workspace_bytes(T, Hkv, head_dim, in_dtype) : kHeader;
+  if (workspace_bytes < need) return fail(YR_ERR_WORKSPACE, "attn_prefill_fwd: workspace too small");
+  const long long ntiles = (max_seqlen + 63) / 64;
+  if (ntiles * (long long)B * Hq > 0x7fffffffLL)
+    return fail(YR_ERR_INVALID, "attn_prefill_fwd: grid too large");
+
+  hipStream_t s = (hipStream_t)stream;
+  int *flag = flag_of(workspace);
+  PrefillArgs p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.in_dtype = in_dtype;
+  p.cu_seqlens = cu_seqlens;
+  p.B = B;
+  p.max_seqlen = max_seqlen;
+  p.T = T;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.head_dim = head_dim;
+  p.theta = inv_freq_f64;
+  p.softmax_scale = softmax_scale;
+  p.out = out;
+  p.out_dtype = out_dtype;
+  p.lse = lse;
+  p.dev_flag = flag;
+
+  if (inv_freq_f64 != nullptr && T > 0) {
+    // rotate every key once into the workspace; the attention kernel rotates
+    // queries on load and reads the rotated keys
+    void *krot = static_cast<char *>(workspace) + kHeader;
+    RopeArgs r{};
+    r.src = k;
+    r.dst = krot;
+    r.dtype = in_dtype;
+    r.T = T;
+    r.H = Hkv;
+    r.head_dim = head_dim;
+    r.positions = nullptr;
+    r.cu_seqlens = cu_seqlens;
+    r.B = B;
+    r.max_seqlen = max_seqlen;
+    r.theta = inv_freq_f64;
+    r.dev_flag = flag;
+    hipError_t e = launch_rope(r, s);
+    if (e != hipSuccess) return fail_hip(e, "attn_prefill_fwd (key rotation)");
+    p.k = krot;
+    p.dev_flag = nullptr;  // already validated by the key pass
+  }
+  const hipError_t e =
+      in_dtype == YR_F32 ? launch_prefill_f32(p, s) : launch_prefill_bf16(p, s);
+  if (e != hipSuccess) return fail_hip(e, "attn_prefill_fwd");
+  return YR_OK;
+}
+
+size_t attn_decode_workspace_bytes(int B, int max_cache_len, int Hq, int head_dim) {
+  if (B < 1 || max_cache_len < 1 || Hq < 1 || head_dim < 1) return kHeader;
+  // chunking depends on Hkv only through the split count heuristic; size for
+  // the finest chunking any Hkv <= Hq can select
+  const int chunk = decode_chunk(B, max_cache_len, 1);
+  const size_t ns = (size_t)decode_nsplit(max_cache_len, chunk);
+  const size_t rows = (size_t)B * Hq * ns;
+  return kHeader + align_up(rows * head_dim * 4, 256) + align_up(rows * 4, 256);
+}
+
+int attn_decode(const void *q, const void *k_cache, const void *v_cache, int in_dtype,
+                const int *seqlens, const int *q_pos, int B, int max_cache_len, int Hq, int Hkv,
+                int head_dim, const double *inv_freq_f64, float softmax_scale, void *out,
+                int out_dtype, float *lse, void *workspace, size_t workspace_bytes,
+                void *stream) {
+  if (in_dtype != YR_F32 && in_dtype != YR_BF16)
+    return fail(YR_ERR_UNSUPPORTED, "attn_decode: in_dtype must be YR_F32 or YR_BF16");
+  if (out_dtype != YR_F32 && out_dtype != YR_BF16)
+    return fail(YR_ERR_UNSUPPORTED, "attn_decode: out_dtype must be YR_F32 or YR_BF16");
+  if (!dims_ok(head_dim)) return fail(YR_ERR_UNSUPPORTED, "attn_decode: head_dim must be 64 or 128");
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return fail(YR_ERR_INVALID, "attn_decode: need Hq >= 1, Hkv >= 1, Hq % Hkv == 0");
+  if (Hq / Hkv > 16) return fail(YR_ERR_UNSUPPORTED, "attn_decode: at most 16 query heads per KV head");
+  if (B < 1 || max_cache_len < 1) return fail(YR_ERR_INVALID, "attn_decode: need B >= 1, max_cache_len >= 1");
+  if ((long long)B * max_cache_len > (1LL << 34))
+    return fail(YR_ERR_INVALID, "attn_decode: cache too large");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(YR_ERR_INVALID, "attn_decode: softmax_scale must be finite and > 0");
+  if (!q || !k_cache || !v_cache || !seqlens || !out || !workspace)
+    return fail(YR_ERR_NULL, "attn_decode: q, caches, seqlens, out and workspace are required");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return fail(YR_ERR_WORKSPACE, "attn_decode: workspace must be 256-byte aligned");
+  const size_t need = attn_decode_workspace_bytes(B, max_cache_len, Hq, head_dim);
+  if (workspace_bytes < need) return fail(YR_ERR_WORKSPACE, "attn_decode: workspace too small");
+
+  const int chunk = decode_chunk(B, max_cache_len, Hkv);
+  const int nsplit = decode_nsplit(max_cache_len, chunk);
+  if ((long long)B * Hkv * nsplit > 0x7fffffffLL) return fail(YR_ERR_INVALID, "attn_decode: grid too large");
+  const size_t rows = (size_t)B * Hq * nsplit;
+  char *ws = static_cast<char *>(workspace);
+  DecodeArgs d{};
+  d.q = q;
+  d.k_cache = k_cache;
+  d.v_cache = v_cache;
+  d.in_dtype = in_dtype;
+  d.seqlens = seqlens;
+  d.q_pos = q_pos;
+  d.B = B;
+  d.max_cache_len = max_cache_len;
+  d.Hq = Hq;
+  d.Hkv = Hkv;
+  d.head_dim = head_dim;
+  d.theta = inv_freq_f64;
+  d.softmax_scale = softmax_scale;
+  d.out = out;
+  d.out_dtype = out_dtype;
+  d.lse = lse;
+  d.part_o = reinterpret_cast<float *>(ws + kHeader);
+  d.part_lse = reinterpret_cast<float *>(ws + kHeader + align_up(rows * head_dim * 4, 256));
+  d.chunk = chunk;
+  d.nsplit = nsplit;
+  d.dev_flag = flag_of(workspace);
+  const hipError_t e = launch_decode(d, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "attn_decode");
+  return YR_OK;
+}
+
+int yr_read_device_error(const void *workspace, void *stream, int *flags) {
+  if (!workspace || !flags) return fail(YR_ERR_NULL, "yr_read_device_error: null pointer");
+  int h = 0;
+  hipError_t e = hipMemcpyAsync(&h, workspace, sizeof(int), hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "yr_read_device_error");
+  *flags = h;
+  if (h != 0) return fail(YR_ERR_DEVICE_RANGE, "device-side range check failed (see flag bits)");
+  return YR_OK;
+}
+
+}  // extern "C"

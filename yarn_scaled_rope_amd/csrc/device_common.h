@@ -1,0 +1,90 @@
+// Device helpers shared by the gfx950 kernels: bf16 bit conversions, the
+// rotary angle (fp64 product and reduction, fp32 sine/cosine) and the
+// device-side range checks of cu_seqlens / seqlens.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "yarnattn.h"
+
+namespace yr {
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two floats -> packed bf16 pair (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// cos and sin of (pos * theta).  The product and its reduction to
+// [-pi, pi] are done in fp64 (exact to ~1e-11 rad for positions up to 2^20),
+// the sine and cosine of the reduced angle in fp32.
+__device__ __forceinline__ void rope_cos_sin(double pos, double theta, float *c, float *s) {
+  constexpr double kInvTwoPi = 0.15915494309189533577;
+  constexpr double kTwoPiHi = 6.283185307179586232;    // nearest double to 2 pi
+  constexpr double kTwoPiLo = 2.4492935982947064e-16;  // 2 pi - kTwoPiHi
+  const double x = pos * theta;
+  const double kq = rint(x * kInvTwoPi);
+  double r = fma(-kq, kTwoPiHi, x);
+  r = fma(-kq, kTwoPiLo, r);
+  sincosf((float)r, s, c);
+}
+
+// Rotate one pair in fp32.  The fused multiply-adds are written out so that
+// every kernel that rotates produces the same bits for the same input.
+__device__ __forceinline__ void rotate_pair(float &x0, float &x1, float c, float s) {
+  const float a = fmaf(x0, c, -(x1 * s));
+  const float b = fmaf(x0, s, x1 * c);
+  x0 = a;
+  x1 = b;
+}
+
+// Clamped bounds of sequence b of a packed batch.  Guarantees
+// 0 <= start <= start + len <= T and len <= max_seqlen whatever cu holds.
+__device__ __forceinline__ void seq_bounds(const int *__restrict__ cu, int b, long long T,
+                                           int max_seqlen, long long *start, int *len) {
+  long long s0 = cu[b];
+  long long s1 = cu[b + 1];
+  s0 = s0 < 0 ? 0 : (s0 > T ? T : s0);
+  s1 = s1 < s0 ? s0 : (s1 > T ? T : s1);
+  long long n = s1 - s0;
+  if (n > max_seqlen) n = max_seqlen;
+  *start = s0;
+  *len = (int)n;
+}
+
+// Check cu_seqlens (one workgroup, all threads call it; thread 0 writes the
+// error word).
+__device__ inline void validate_cu_seqlens(const int *__restrict__ cu, int B, long long T,
+                                           int max_seqlen, int *flag) {
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  for (int b = threadIdx.x; b <= B; b += blockDim.x) {
+    const long long c = cu[b];
+    int e = 0;
+    if (b == 0 && c != 0) e = 1;
+    if (b == B && c != T) e = 1;
+    if (b > 0) {
+      const long long p = cu[b - 1];
+      if (c < p || c - p > max_seqlen) e = 1;
+    }
+    if (e) atomicOr(&bad, YR_DEVERR_CU_SEQLENS);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = bad;
+}
+
+}  // namespace yr

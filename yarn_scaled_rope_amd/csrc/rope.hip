@@ -1,0 +1,121 @@
+// rope kernels (gfx950): rotate feature pairs of [T, H, D] rows by
+// position * theta_i ("Arch 03 -- Long Context", RoPE slide).
+//
+// One thread owns one (token, pair): it forms the angle once (fp64 product and
+// reduction, fp32 sine/cosine) and applies it to that pair in every head, so
+// the transcendental work is shared by the H heads of a token.  Lanes of a
+// wave cover consecutive pairs of one token, so each head's row is read and
+// written as one contiguous segment.  Positions come either from an explicit
+// array (rope_apply) or from the row's offset inside its sequence of a packed
+// batch (the key pass of prefill, which also writes out of place).
+#include "device_common.h"
+#include "yr_internal.h"
+
+namespace yr {
+namespace {
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  using pair_t = float2;
+  __device__ static void load(const float *p, float &a, float &b) {
+    const float2 v = *reinterpret_cast<const float2 *>(p);
+    a = v.x;
+    b = v.y;
+  }
+  __device__ static void store(float *p, float a, float b) {
+    *reinterpret_cast<float2 *>(p) = make_float2(a, b);
+  }
+};
+template <>
+struct Elem<uint16_t> {
+  __device__ static void load(const uint16_t *p, float &a, float &b) {
+    const uint32_t v = *reinterpret_cast<const uint32_t *>(p);
+    a = bf16_to_f32(v & 0xffffu);
+    b = bf16_to_f32(v >> 16);
+  }
+  __device__ static void store(uint16_t *p, float a, float b) {
+    *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(a, b);
+  }
+};
+
+// Sequence index of packed row t: the last b with cu[b] <= t.
+__device__ __forceinline__ int seq_of_row(const int *__restrict__ cu, int B, long long t) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((long long)cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <typename T, bool FROM_CU>
+__global__ __launch_bounds__(256) void rope_kernel(const T *__restrict__ src, T *__restrict__ dst,
+                                                  long long ntok, int H, int D,
+                                                  const int *__restrict__ pos_or_cu, int B,
+                                                  int max_seqlen, const double *__restrict__ theta,
+                                                  int *flag) {
+  if (FROM_CU && flag != nullptr && blockIdx.x == 0)
+    validate_cu_seqlens(pos_or_cu, B, ntok, max_seqlen, flag);
+  const int half = D >> 1;
+  const long long total = ntok * (long long)half;
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
+    const long long t = idx / half;
+    const int i = (int)(idx - t * half);
+    long long pos;
+    if (FROM_CU) {
+      const int b = seq_of_row(pos_or_cu, B, t);
+      long long s0 = pos_or_cu[b];
+      s0 = s0 < 0 ? 0 : s0;
+      pos = t - s0;
+      if (pos < 0) pos = 0;
+    } else {
+      pos = pos_or_cu[t];
+    }
+    float c, s;
+    rope_cos_sin((double)pos, theta[i], &c, &s);
+    const long long row = t * (long long)H * D + 2 * i;
+    for (int h = 0; h < H; ++h) {
+      float a, b2;
+      Elem<T>::load(src + row + (long long)h * D, a, b2);
+      rotate_pair(a, b2, c, s);
+      Elem<T>::store(dst + row + (long long)h * D, a, b2);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rope(const RopeArgs &a, hipStream_t s) {
+  const long long total = a.T * (long long)(a.head_dim / 2);
+  long long blocks = (total + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 65536) blocks = 65536;  // grid-stride beyond this
+  const dim3 grid((unsigned)blocks), block(256);
+  const bool from_cu = a.positions == nullptr;
+  const int *pc = from_cu ? a.cu_seqlens : a.positions;
+  if (a.dtype == YR_F32) {
+    if (from_cu)
+      hipLaunchKernelGGL((rope_kernel<float, true>), grid, block, 0, s, (const float *)a.src,
+                         (float *)a.dst, a.T, a.H, a.head_dim, pc, a.B, a.max_seqlen, a.theta,
+                         a.dev_flag);
+    else
+      hipLaunchKernelGGL((rope_kernel<float, false>), grid, block, 0, s, (const float *)a.src,
+                         (float *)a.dst, a.T, a.H, a.head_dim, pc, a.B, a.max_seqlen, a.theta,
+                         a.dev_flag);
+  } else {
+    if (from_cu)
+      hipLaunchKernelGGL((rope_kernel<uint16_t, true>), grid, block, 0, s,
+                         (const uint16_t *)a.src, (uint16_t *)a.dst, a.T, a.H, a.head_dim, pc,
+                         a.B, a.max_seqlen, a.theta, a.dev_flag);
+    else
+      hipLaunchKernelGGL((rope_kernel<uint16_t, false>), grid, block, 0, s,
+                         (const uint16_t *)a.src, (uint16_t *)a.dst, a.T, a.H, a.head_dim, pc,
+                         a.B, a.max_seqlen, a.theta, a.dev_flag);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace yr

@@ -1,0 +1,90 @@
+// Internal declarations shared by the C-ABI shim and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "yarnattn.h"
+
+namespace yr {
+
+// Record a message for yr_last_error() and return `status`.
+int fail(int status, const char *msg);
+int fail_hip(hipError_t err, const char *where);
+
+// ---- launch descriptions (host side; every field already validated) -------
+struct RopeArgs {
+  const void *src;
+  void *dst;             // == src for in-place rotation
+  int dtype;             // YR_F32 / YR_BF16
+  long long T;
+  int H;
+  int head_dim;
+  const int *positions;  // explicit positions, or NULL to derive from cu_seqlens
+  const int *cu_seqlens; // used when positions == NULL
+  int B;
+  int max_seqlen;
+  const double *theta;
+  int *dev_flag;         // device error word or NULL (validates cu_seqlens)
+};
+
+struct PrefillArgs {
+  const void *q;
+  const void *k;         // keys as the kernel reads them (already rotated)
+  const void *v;
+  int in_dtype;
+  const int *cu_seqlens;
+  int B;
+  int max_seqlen;
+  long long T;
+  int Hq;
+  int Hkv;
+  int head_dim;
+  const double *theta;   // rotate q on load when non-NULL
+  float softmax_scale;
+  void *out;
+  int out_dtype;
+  float *lse;
+  int *dev_flag;         // non-NULL: this launch validates cu_seqlens
+};
+
+struct DecodeArgs {
+  const void *q;
+  const void *k_cache;
+  const void *v_cache;
+  int in_dtype;
+  const int *seqlens;
+  const int *q_pos;
+  int B;
+  int max_cache_len;
+  int Hq;
+  int Hkv;
+  int head_dim;
+  const double *theta;
+  float softmax_scale;
+  void *out;
+  int out_dtype;
+  float *lse;
+  float *part_o;         // [B, Hq, nsplit, D]
+  float *part_lse;       // [B, Hq, nsplit]
+  int chunk;
+  int nsplit;
+  int *dev_flag;
+};
+
+hipError_t launch_rope(const RopeArgs &a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+
+// Decode split geometry: keys per chunk and number of chunks for a cache
+// length bound.  Pure function of its arguments so that workspace sizing and
+// the launch agree.
+int decode_chunk(int B, int max_cache_len, int Hkv);
+inline int decode_nsplit(int max_cache_len, int chunk) {
+  return (max_cache_len + chunk - 1) / chunk;
+}
+
+}  // namespace yr

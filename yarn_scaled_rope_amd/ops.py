@@ -1,0 +1,236 @@
+"""ctypes binding of libyarnattn.so with the C entry-point names.
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the computation runs in the library's kernels.  The
+library is loaded on first use (after torch, so that both share one HIP
+runtime); if it is missing, every call raises -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+YR_OK = 0
+YR_ERR_INVALID = 1
+YR_ERR_NULL = 2
+YR_ERR_UNSUPPORTED = 3
+YR_ERR_WORKSPACE = 4
+YR_ERR_HIP = 5
+YR_ERR_DEVICE_RANGE = 6
+
+YR_F32 = 0
+YR_BF16 = 1
+
+YR_ROPE_PLAIN = 0
+YR_ROPE_PI = 1
+YR_ROPE_NTK = 2
+YR_ROPE_YARN = 3
+METHODS = {"plain": YR_ROPE_PLAIN, "pi": YR_ROPE_PI, "ntk": YR_ROPE_NTK, "yarn": YR_ROPE_YARN}
+
+YR_DEVERR_CU_SEQLENS = 1
+YR_DEVERR_SEQLENS = 2
+YR_DEVERR_QPOS = 4
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libyarnattn.so")
+
+_lib = None
+
+
+class YarnAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+def _declare(lib):
+    vp, i, ll, d, f, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_double,
+                           ctypes.c_float, ctypes.c_size_t)
+    sig = {
+        "yarn_rope_freqs": (i, [i, d, d, ll, d, d, i, vp, vp, vp]),
+        "rope_apply": (i, [vp, i, ll, i, i, vp, vp, vp]),
+        "attn_prefill_workspace_bytes": (sz, [ll, i, i, i]),
+        "attn_prefill_fwd": (i, [vp, vp, vp, i, vp, i, i, ll, i, i, i, vp, f, vp, i, vp, vp, sz, vp]),
+        "attn_decode_workspace_bytes": (sz, [i, i, i, i]),
+        "attn_decode": (i, [vp, vp, vp, i, vp, vp, i, i, i, i, i, vp, f, vp, i, vp, vp, sz, vp]),
+        "yr_read_device_error": (i, [vp, vp, vp]),
+        "yr_status_string": (ctypes.c_char_p, [i]),
+        "yr_last_error": (ctypes.c_char_p, []),
+        "yr_version": (i, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+def load_library(path: Optional[str] = None):
+    """Load (once) and return the ctypes handle.  Raises if the library is not
+    built: there is no CPU or PyTorch fallback."""
+    global _lib
+    if _lib is None:
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise YarnAttnError(-1, f"{p} is missing; build it with "
+                                    "`python -m yarn_scaled_rope_amd.build`")
+        _lib = _declare(ctypes.CDLL(p))
+    return _lib
+
+
+def _check(status: int):
+    if status != YR_OK:
+        lib = load_library()
+        raise YarnAttnError(status, f"{lib.yr_status_string(status).decode()}: "
+                                    f"{lib.yr_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return YR_F32
+    if t.dtype == torch.bfloat16:
+        return YR_BF16
+    raise YarnAttnError(YR_ERR_UNSUPPORTED, f"dtype {t.dtype}")
+
+
+def _torch_dtype(code: int):
+    return torch.float32 if code == YR_F32 else torch.bfloat16
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=True):
+    if not t.is_contiguous():
+        raise YarnAttnError(YR_ERR_INVALID, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise YarnAttnError(YR_ERR_INVALID, f"{name} must be {dtype}")
+    if device and not t.is_cuda:
+        raise YarnAttnError(YR_ERR_INVALID, f"{name} must be a device tensor")
+
+
+# ------------------------------------------------------------------ freqs
+def yarn_rope_freqs(head_dim: int, base: float, factor: float = 1.0,
+                    original_max_position: int = 1, alpha: float = 1.0, beta: float = 32.0,
+                    method: str = "yarn"):
+    """Host call: returns (fp32 table, fp64 table, attention factor t)."""
+    lib = load_library()
+    f32 = np.zeros(head_dim // 2, dtype=np.float32)
+    f64 = np.zeros(head_dim // 2, dtype=np.float64)
+    t = ctypes.c_double(0.0)
+    _check(lib.yarn_rope_freqs(int(head_dim), float(base), float(factor),
+                               int(original_max_position), float(alpha), float(beta),
+                               METHODS[method], f32.ctypes.data_as(ctypes.c_void_p),
+                               f64.ctypes.data_as(ctypes.c_void_p), ctypes.byref(t)))
+    return f32, f64, t.value
+
+
+# ------------------------------------------------------------------ rope
+def rope_apply(x: torch.Tensor, positions: torch.Tensor, inv_freq_f64: torch.Tensor, stream=None):
+    """Rotate x [T, H, D] in place at positions[T] (int32)."""
+    _need(x, "x")
+    _need(positions, "positions", torch.int32)
+    _need(inv_freq_f64, "inv_freq_f64", torch.float64)
+    T, H, D = x.shape
+    lib = load_library()
+    _check(lib.rope_apply(_ptr(x), _dtype_code(x), T, H, D, _ptr(positions), _ptr(inv_freq_f64),
+                          _stream(stream)))
+    return x
+
+
+# ------------------------------------------------------------------ prefill
+def attn_prefill_workspace_bytes(T: int, hkv: int, head_dim: int, in_dtype: int) -> int:
+    return int(load_library().attn_prefill_workspace_bytes(T, hkv, head_dim, in_dtype))
+
+
+def attn_prefill_fwd(q, k, v, cu_seqlens, max_seqlen: int, inv_freq_f64, softmax_scale: float,
+                     out=None, out_dtype=None, lse=None, workspace=None, want_lse=True,
+                     stream=None):
+    """Causal prefill.  q [T, Hq, D], k/v [T, Hkv, D] unrotated (or rotated,
+    with inv_freq_f64=None); cu_seqlens int32 [B+1].  Returns (out, lse)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n)
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    if inv_freq_f64 is not None:
+        _need(inv_freq_f64, "inv_freq_f64", torch.float64)
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    if k.shape != (T, hkv, D) or v.shape != (T, hkv, D) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise YarnAttnError(YR_ERR_INVALID, "k and v must be [T, Hkv, D] of q's dtype")
+    in_code = _dtype_code(q)
+    out_code = (YR_F32 if in_code == YR_F32 else YR_BF16) if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((T, hq, D), dtype=_torch_dtype(out_code), device=q.device)
+    else:
+        _need(out, "out", _torch_dtype(out_code))
+    if lse is None and want_lse:
+        lse = torch.empty((hq, T), dtype=torch.float32, device=q.device)
+    need = attn_prefill_workspace_bytes(T, hkv, D, in_code) if inv_freq_f64 is not None else 256
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    B = cu_seqlens.numel() - 1
+    lib = load_library()
+    _check(lib.attn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), in_code, _ptr(cu_seqlens), B,
+                                int(max_seqlen), T, hq, hkv, D, _ptr(inv_freq_f64),
+                                float(softmax_scale), _ptr(out), out_code, _ptr(lse),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream)))
+    return out, lse
+
+
+# ------------------------------------------------------------------ decode
+def attn_decode_workspace_bytes(B: int, max_cache_len: int, hq: int, head_dim: int) -> int:
+    return int(load_library().attn_decode_workspace_bytes(B, max_cache_len, hq, head_dim))
+
+
+def attn_decode(q, k_cache, v_cache, seqlens, inv_freq_f64, softmax_scale: float, q_pos=None,
+                out=None, out_dtype=None, lse=None, workspace=None, want_lse=True, stream=None):
+    """One query per sequence over a contiguous cache.  q [B, Hq, D];
+    caches [B, Lmax, Hkv, D]; seqlens int32 [B].  Returns (out, lse)."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n)
+    _need(seqlens, "seqlens", torch.int32)
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int32)
+    if inv_freq_f64 is not None:
+        _need(inv_freq_f64, "inv_freq_f64", torch.float64)
+    B, hq, D = q.shape
+    _, lmax, hkv, _ = k_cache.shape
+    if k_cache.shape != (B, lmax, hkv, D) or v_cache.shape != k_cache.shape:
+        raise YarnAttnError(YR_ERR_INVALID, "caches must be [B, Lmax, Hkv, D]")
+    in_code = _dtype_code(q)
+    out_code = (YR_F32 if in_code == YR_F32 else YR_BF16) if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, hq, D), dtype=_torch_dtype(out_code), device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(attn_decode_workspace_bytes(B, lmax, hq, D), dtype=torch.uint8,
+                                device=q.device)
+    lib = load_library()
+    _check(lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), in_code, _ptr(seqlens),
+                           _ptr(q_pos), B, lmax, hq, hkv, D, _ptr(inv_freq_f64),
+                           float(softmax_scale), _ptr(out), out_code, _ptr(lse), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse
+
+
+def read_device_error(workspace: torch.Tensor, stream=None) -> int:
+    """Synchronise and return the device error bits of a workspace."""
+    flags = ctypes.c_int(0)
+    lib = load_library()
+    st = lib.yr_read_device_error(_ptr(workspace), _stream(stream), ctypes.byref(flags))
+    if st not in (YR_OK, YR_ERR_DEVICE_RANGE):
+        _check(st)
+    return flags.value
