@@ -1,0 +1,390 @@
+#!/usr/bin/env python3
+"""Benchmark of the YaRN-RoPE causal attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the prefill hot path over the Llama-2-7B-shaped 16K
+prefill (batch 1, 32/32 heads, head_dim 128, bf16, YaRN s=4 over 4096, base
+1e4): the frequency table (host, fp64; computed once per model and timed
+separately), the key rotation pass (rope_apply_packed) and the attention
+kernel (queries rotated on load, causal online softmax on bf16 MFMA, out +
+LSE).  W untimed steps, then exactly K steps between two device
+synchronisations; the JSON line's `value` is the algorithmic causal FLOPs of
+one step over the wall time of one step.
+
+The same run then times the decode hot path (split-K sweep + LSE merge) over
+the 16-sequence 32K-128K cache workload and reports it as `decode`, and
+times the fp64 CPU checker on a bounded sample of the prefill workload as
+`cpu_baseline`.
+
+Roofline: the attention kernel's own duration comes from HIP events on the
+launch stream around its launch inside every timed step.  `traffic` is filled
+from a counter summary under profiles/ when one exists for the current
+kernel source (FETCH_SIZE + WRITE_SIZE per dispatch, scaled by the same
+counters on a plain copy of known size); otherwise it is null.
+
+Other modes:
+    --workload NAME           time another prefill workload (parity configs)
+    --copy-probe              also run a 1 GiB device copy (counter calibration)
+    --summarize DIR --out F   turn rocprofv3 output (kernel stats or counter
+                              CSVs under DIR) into a short text summary
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0       # HBM3E
+METRIC = "causal prefill TFLOP/s + % bf16 MFMA peak; decode KV GB/s + % HBM peak"
+ATTN_SOURCES = ["yarn_scaled_rope_amd/csrc/prefill_bf16.hip",
+                "yarn_scaled_rope_amd/csrc/device_common.h"]
+DECODE_SOURCES = ["yarn_scaled_rope_amd/csrc/decode.hip",
+                  "yarn_scaled_rope_amd/csrc/device_common.h"]
+
+
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def traffic_from_profiles(kind: str, workload: str, digest: str):
+    """HBM bytes per launch from a committed counter summary, or None when
+    there is none for this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}_hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    if d.get("source_digest") != digest:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ prefill
+def bench_prefill(args, torch, ops, wl):
+    cfg = wl.PREFILL_CONFIGS[args.workload]
+    if cfg.dtype != "bf16":
+        raise SystemExit("bench times the bf16 path; the fp32 workload is a parity case")
+    D, hq, hkv = cfg.head_dim, cfg.hq, cfg.hkv
+    t0 = time.perf_counter()
+    for _ in range(100):
+        _, f64, t = ops.yarn_rope_freqs(D, cfg.base, cfg.factor, cfg.original_max_position)
+    a1_us = (time.perf_counter() - t0) / 100 * 1e6
+    theta = torch.from_numpy(f64).cuda()
+    scale = t / math.sqrt(D)
+
+    log(f"generating {cfg.name} inputs")
+    inp = wl.make_prefill(cfg)
+    import numpy as np
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = up(inp["q"]), up(inp["k"]), up(inp["v"])
+    del inp["q"], inp["k"], inp["v"]
+    cu = torch.from_numpy(inp["cu_seqlens"]).cuda()
+    T = q.shape[0]
+    maxlen = cfg.max_seqlen
+    krot = torch.empty_like(k)
+    out = torch.empty((T, hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((hq, T), dtype=torch.float32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    dev_err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ops.rope_apply_packed(k, cu, maxlen, theta, dst=krot, dev_error=dev_err, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        ops.attn_prefill_fwd(q, krot, v, cu, maxlen, theta, scale, out=out, lse=lse, workspace=ws,
+                             k_rotated=True, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    log(f"prefill warmup x{args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(dev_err.item()) != 0 or ops.read_device_error(ws) != 0:
+        raise SystemExit("device range check failed")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"prefill timed x{args.steps}")
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    rope_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    ms_per_step = wall / args.steps * 1e3
+    flops = wl.prefill_causal_flops(cfg.seq_lens, hq, D)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    digest = source_digest(ATTN_SOURCES)
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_from_profiles("prefill_bf16", cfg.name, digest),
+            "kernel": "prefill_bf16_kernel<128,false,true>", "kernel_ms": round(attn_ms, 4),
+            "flops_per_launch": flops}
+    extra = {"rope_pass_ms": round(rope_ms, 4), "freqs_host_us": round(a1_us, 2),
+             "wall_ms_per_step": round(ms_per_step, 4), "source_digest": digest}
+    conf = {"workload": cfg.name, "batch": len(cfg.seq_lens), "seq_lens": list(cfg.seq_lens),
+            "hq": hq, "hkv": hkv, "head_dim": D, "rope": "yarn", "rope_base": cfg.base,
+            "factor": cfg.factor, "original_max_position": cfg.original_max_position,
+            "out_dtype": "bf16", "seed": 1000 + cfg.index}
+    state = {"inp": inp, "q": q, "k": k, "v": v, "theta_host": f64, "scale": scale}
+    return value, ms_per_step, roof, extra, conf, state
+
+
+# ------------------------------------------------------------------ decode
+def bench_decode(args, torch, ops, wl):
+    import numpy as np
+    cfg = wl.DECODE_B16
+    D = cfg.head_dim
+    _, f64, t = ops.yarn_rope_freqs(D, cfg.base, cfg.factor, cfg.original_max_position)
+    theta = torch.from_numpy(f64).cuda()
+    scale = t / math.sqrt(D)
+    log(f"generating {cfg.name} inputs")
+    inp = wl.make_decode(cfg)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    q = up(inp["q"])
+    kc = up(inp["k_cache"])
+    del inp["k_cache"]
+    vc = up(inp["v_cache"])
+    del inp["v_cache"]
+    sl = torch.from_numpy(inp["seqlens"]).cuda()
+    out = torch.empty((cfg.batch, cfg.hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((cfg.batch, cfg.hq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ops.attn_decode_workspace_bytes(cfg.batch, cfg.max_cache_len, cfg.hq, D),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    steps = args.decode_steps
+    log(f"decode warmup x{args.warmup} timed x{steps}")
+    for _ in range(args.warmup):
+        ops.attn_decode(q, kc, vc, sl, theta, scale, out=out, lse=lse, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    if ops.read_device_error(ws) != 0:
+        raise SystemExit("device range check failed (decode)")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        ops.attn_decode(q, kc, vc, sl, theta, scale, out=out, lse=lse, workspace=ws, stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    call_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    nbytes = wl.decode_kv_bytes(inp["seqlens"], cfg.hkv, D)
+    gbs = nbytes / (wall / steps) / 1e9
+    achieved = nbytes / (call_ms * 1e-3) / 1e9
+    digest = source_digest(DECODE_SOURCES)
+    res = {"metric": "decode KV GB/s", "value": round(gbs, 2), "unit": "GB/s",
+           "ms_per_step": round(wall / steps * 1e3, 4), "steps": steps,
+           "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+           "config": {"workload": cfg.name, "batch": cfg.batch, "seqlens": [int(x) for x in inp["seqlens"]],
+                      "kv_bytes": int(nbytes), "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": D,
+                      "rope": "yarn", "rope_base": cfg.base, "factor": cfg.factor,
+                      "original_max_position": cfg.original_max_position,
+                      "seed": 1000 + cfg.index},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                        "traffic": traffic_from_profiles("decode", cfg.name, digest),
+                        "kernel": "decode_split_kernel + decode_merge_kernel (one call)",
+                        "kernel_ms": round(call_ms, 4), "bytes_per_launch": int(nbytes)},
+           "source_digest": digest}
+    state = {"seqlens": inp["seqlens"], "q": q, "kc": kc, "vc": vc}
+    return res, state
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(cfg_name, state, wl, target_s: float):
+    """The fp64 oracle, as it stands, on the first heads of the same prefill
+    inputs (all rows of each head), until about target_s seconds of work."""
+    from oracle import attention as oatt
+    from oracle import freqs as ofreqs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    cfg = wl.PREFILL_CONFIGS[cfg_name]
+    inp = state["inp"]
+    th = ofreqs.yarn_theta(cfg.head_dim, cfg.base, cfg.factor, cfg.original_max_position)
+    sc = ofreqs.softmax_scale(cfg.head_dim, ofreqs.attention_temperature(cfg.factor))
+    g = cfg.hq // cfg.hkv
+    import torch
+    q_host = state["q"].view(torch.int16).cpu().numpy()
+    k_host = state["k"].view(torch.int16).cpu().numpy()
+    v_host = state["v"].view(torch.int16).cpu().numpy()
+    done_heads, flops, elapsed = 0, 0, 0.0
+    while done_heads < cfg.hq and elapsed < target_s:
+        h = done_heads
+        hk = h // g
+        q = wl.as_f64(q_host[:, h:h + 1].view("uint16"), "bf16")
+        k = wl.as_f64(k_host[:, hk:hk + 1].view("uint16"), "bf16")
+        v = wl.as_f64(v_host[:, hk:hk + 1].view("uint16"), "bf16")
+        t0 = time.perf_counter()
+        oatt.prefill(q, k, v, inp["cu_seqlens"], th, sc)
+        elapsed += time.perf_counter() - t0
+        flops += wl.prefill_causal_flops(cfg.seq_lens, 1, cfg.head_dim)
+        done_heads += 1
+    return {"value": round(flops / elapsed / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(elapsed, 2),
+            "sample": f"fp64 dense causal prefill of the first {done_heads} of {cfg.hq} query "
+                      f"heads, all {cfg.total_tokens} rows each, same inputs"}
+
+
+def cpu_baseline_decode(state, wl, torch):
+    """The fp64 oracle on one sequence of the decode workload (its inputs
+    copied back from device memory)."""
+    import numpy as np
+    from oracle import attention as oatt
+    from oracle import freqs as ofreqs
+    cfg = wl.DECODE_B16
+    th = ofreqs.yarn_theta(cfg.head_dim, cfg.base, cfg.factor, cfg.original_max_position)
+    sc = ofreqs.softmax_scale(cfg.head_dim, ofreqs.attention_temperature(cfg.factor))
+    b = 0
+    L = int(state["seqlens"][b])
+
+    def host(t):
+        return wl.as_f64(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+
+    kc = host(state["kc"][b:b + 1, :L])
+    vc = host(state["vc"][b:b + 1, :L])
+    q = host(state["q"][b:b + 1])
+    t0 = time.perf_counter()
+    oatt.decode(q, kc, vc, state["seqlens"][b:b + 1], th, sc)
+    dt = time.perf_counter() - t0
+    nbytes = wl.decode_kv_bytes([L], cfg.hkv, cfg.head_dim)
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"fp64 decode of sequence 0 (cache length {L}) of the same inputs"}
+
+
+# ------------------------------------------------------------------ rocprof summaries
+def summarize(dirname: str, out_path: str, command: str):
+    """Condense rocprofv3 CSV output under dirname into a short text file."""
+    import csv
+    lines = [f"# rocprofv3 summary", f"# command: {command}", ""]
+    stats = glob.glob(os.path.join(dirname, "**", "*kernel_stats.csv"), recursive=True)
+    for p in stats:
+        rows = list(csv.DictReader(open(p)))
+        lines.append(f"## kernel stats ({os.path.relpath(p, dirname)})")
+        lines.append("name | calls | total_ns | avg_ns | min_ns | max_ns | pct")
+        for r in rows:
+            name = r.get("Name", "")[:110]
+            lines.append(f"{name} | {r.get('Calls')} | {r.get('TotalDurationNs')} | "
+                         f"{r.get('AverageNs')} | {r.get('MinNs')} | {r.get('MaxNs')} | "
+                         f"{r.get('Percentage')}")
+        lines.append("")
+    ctrs = glob.glob(os.path.join(dirname, "**", "*counter_collection.csv"), recursive=True)
+    for p in ctrs:
+        rows = list(csv.DictReader(open(p)))
+        agg = {}
+        for r in rows:
+            key = (r.get("Kernel_Name", "")[:110], r.get("Counter_Name", ""))
+            agg.setdefault(key, []).append(float(r.get("Counter_Value", 0) or 0))
+        lines.append(f"## counters ({os.path.relpath(p, dirname)}): mean per dispatch")
+        lines.append("kernel | counter | dispatches | mean | min | max")
+        for (kname, cname), vals in sorted(agg.items()):
+            lines.append(f"{kname} | {cname} | {len(vals)} | {sum(vals) / len(vals):.6g} | "
+                         f"{min(vals):.6g} | {max(vals):.6g}")
+        lines.append("")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out_path)
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=None)
+    ap.add_argument("--workload", default="llama2_7b_prefill_16k")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--summarize", default=None)
+    ap.add_argument("--out", default=None)
+    ap.add_argument("--command", default="")
+    args = ap.parse_args()
+
+    if args.summarize:
+        summarize(args.summarize, args.out or "summary.txt", args.command)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+    if args.decode_steps is None:
+        args.decode_steps = max(args.steps, 20)
+
+    import torch
+    from yarn_scaled_rope_amd import ops
+    from yarn_scaled_rope_amd import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    ops.load_library()
+    torch.cuda.set_device(0)
+
+    value, ms, roof, extra, conf, pstate = bench_prefill(args, torch, ops, wl)
+    line = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic", "config": conf, "roofline": roof,
+            "frac_mfma_peak_wall": round(value / PEAK_BF16_TFLOPS, 4)}
+    line.update(extra)
+    if args.copy_probe:
+        a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        line["copy_probe_bytes"] = {"read": a.numel() * 2, "written": b.numel() * 2}
+        del a, b
+    if not args.no_decode:
+        dres, dstate = bench_decode(args, torch, ops, wl)
+        line["decode"] = dres
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle on a bounded sample")
+        line["cpu_baseline"] = cpu_baseline(args.workload, pstate, wl, args.cpu_seconds)
+        if not args.no_decode:
+            line["decode"]["cpu_baseline"] = cpu_baseline_decode(dstate, wl, torch)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

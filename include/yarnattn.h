@@ -112,7 +112,30 @@ int yarn_rope_freqs(int head_dim, double base, double factor,
 int rope_apply(void *x, int dtype, long long T, int H, int head_dim,
                const int *positions, const double *inv_freq_f64, void *stream);
 
-/* Workspace bytes attn_prefill_fwd needs for these sizes. */
+/*
+ * rope_apply_packed -- rotate the rows of a packed ragged batch at their
+ * 0-based position inside their own sequence (row t of sequence b sits at
+ * t - cu_seqlens[b]), out of place (dst may equal src).  Same rotation as
+ * rope_apply.  It is the key pass of prefill, and the way to fill a KV cache
+ * with rotated keys.
+ *
+ *   src, dst      device [T, H, head_dim], dtype YR_F32 or YR_BF16
+ *   cu_seqlens    device int32[B+1], checked like attn_prefill_fwd's
+ *   dev_error     device int or NULL: receives the YR_DEVERR_CU_SEQLENS bit
+ *                 (0 when cu_seqlens is well formed)
+ *   head_dim      even, 2..512
+ */
+int rope_apply_packed(const void *src, void *dst, int dtype, const int *cu_seqlens, int B,
+                      int max_seqlen, long long T, int H, int head_dim,
+                      const double *inv_freq_f64, int *dev_error, void *stream);
+
+/* attn_prefill_fwd flags */
+#define YR_PREFILL_K_ROTATED 1 /* k already holds rotated keys (e.g. from
+                                  rope_apply_packed or a rotated cache): no key
+                                  pass; queries are still rotated on load when
+                                  inv_freq_f64 != NULL */
+
+/* Workspace bytes attn_prefill_fwd needs for these sizes (with flags = 0). */
 size_t attn_prefill_workspace_bytes(long long T, int Hkv, int head_dim, int in_dtype);
 
 /*
@@ -135,17 +158,19 @@ size_t attn_prefill_workspace_bytes(long long T, int Hkv, int head_dim, int in_d
  *                  (zero-length sequences are allowed and produce nothing)
  *   inv_freq_f64   device double[head_dim/2], or NULL when q and k are already
  *                  rotated
+ *   flags          0, or YR_PREFILL_K_ROTATED
  *   out            device [T, Hq, head_dim] of out_dtype (YR_F32 or YR_BF16;
  *                  YR_F32 inputs require YR_F32 out)
  *   lse            device float[Hq, T] or NULL
- *   workspace      device, >= attn_prefill_workspace_bytes(T, Hkv, head_dim,
- *                  in_dtype) bytes, 256-byte aligned; holds the rotated keys
+ *   workspace      device, 256-byte aligned, >= attn_prefill_workspace_bytes(T,
+ *                  Hkv, head_dim, in_dtype) bytes when the library rotates the
+ *                  keys (it holds them), else >= YR_WORKSPACE_HEADER_BYTES
  *   head_dim       64 or 128;  Hq % Hkv == 0
  */
 int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
                      const int *cu_seqlens, int B, int max_seqlen, long long T,
                      int Hq, int Hkv, int head_dim, const double *inv_freq_f64,
-                     float softmax_scale, void *out, int out_dtype, float *lse,
+                     int flags, float softmax_scale, void *out, int out_dtype, float *lse,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes attn_decode needs for these sizes. */

@@ -31,7 +31,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert {"yarn_rope_freqs", "rope_apply", "attn_prefill_fwd", "attn_decode",
+    assert {"yarn_rope_freqs", "rope_apply", "rope_apply_packed", "attn_prefill_fwd", "attn_decode",
             "attn_prefill_workspace_bytes", "attn_decode_workspace_bytes",
             "yr_read_device_error", "yr_status_string", "yr_last_error", "yr_version"} <= set(names)
     raw = ctypes.CDLL(ops.LIB_PATH)
@@ -95,12 +95,12 @@ WS = ctypes.c_void_p(1 << 20)     # 256-byte aligned fake workspace
 
 def prefill_call(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, in_dtype=ops.YR_BF16, cu=FAKE, B=1, max_seqlen=16, T=16,
-             Hq=4, Hkv=2, D=128, theta=FAKE, scale=0.1, out=FAKE, out_dtype=ops.YR_BF16,
+             Hq=4, Hkv=2, D=128, theta=FAKE, flags=0, scale=0.1, out=FAKE, out_dtype=ops.YR_BF16,
              lse=FAKE, ws=WS, ws_bytes=1 << 30, stream=None)
     a.update(kw)
     return lib.attn_prefill_fwd(a["q"], a["k"], a["v"], a["in_dtype"], a["cu"], a["B"],
                                 a["max_seqlen"], a["T"], a["Hq"], a["Hkv"], a["D"], a["theta"],
-                                a["scale"], a["out"], a["out_dtype"], a["lse"], a["ws"],
+                                a["flags"], a["scale"], a["out"], a["out_dtype"], a["lse"], a["ws"],
                                 a["ws_bytes"], a["stream"])
 
 
@@ -123,6 +123,8 @@ def prefill_call(lib, **kw):
     (dict(ws=ctypes.c_void_p((1 << 20) + 16)), ops.YR_ERR_WORKSPACE),
     (dict(ws_bytes=100), ops.YR_ERR_WORKSPACE),
     (dict(T=1 << 20, ws_bytes=(1 << 20) * 2 * 128 * 2), ops.YR_ERR_WORKSPACE),
+    (dict(flags=2), ops.YR_ERR_INVALID),
+    (dict(flags=ops.YR_PREFILL_K_ROTATED, ws_bytes=255), ops.YR_ERR_WORKSPACE),
 ])
 def test_prefill_rejects_before_launch(lib, kw, status):
     assert prefill_call(lib, **kw) == status
@@ -162,6 +164,12 @@ def test_rope_rejects_and_empty(lib):
     assert lib.rope_apply(FAKE, 9, 4, 2, 8, FAKE, FAKE, None) == ops.YR_ERR_UNSUPPORTED
     assert lib.rope_apply(None, ops.YR_BF16, 4, 2, 8, FAKE, FAKE, None) == ops.YR_ERR_NULL
     assert lib.rope_apply(None, ops.YR_BF16, 0, 2, 8, None, None, None) == ops.YR_OK  # nothing to do
+    rp = lib.rope_apply_packed
+    assert rp(FAKE, FAKE, ops.YR_BF16, FAKE, 1, 8, 8, 2, 9, FAKE, None, None) == ops.YR_ERR_INVALID
+    assert rp(FAKE, FAKE, ops.YR_BF16, FAKE, 0, 8, 8, 2, 8, FAKE, None, None) == ops.YR_ERR_INVALID
+    assert rp(FAKE, FAKE, ops.YR_BF16, None, 1, 8, 8, 2, 8, FAKE, None, None) == ops.YR_ERR_NULL
+    assert rp(FAKE, None, ops.YR_BF16, FAKE, 1, 8, 8, 2, 8, FAKE, None, None) == ops.YR_ERR_NULL
+    assert rp(FAKE, FAKE, 5, FAKE, 1, 8, 8, 2, 8, FAKE, None, None) == ops.YR_ERR_UNSUPPORTED
 
 
 def test_workspace_sizes(lib):

@@ -188,3 +188,17 @@ def test_prerotated_inputs_equal_fused_rotation():
     b, bl = ops.attn_prefill_fwd(qr, kr, v, cu, 400, None, scale)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(al, bl)
+
+
+def test_k_rotated_flag_equals_library_key_pass():
+    cfg = wl.PrefillConfig("t", 73, (700, 1, 129), 8, 2, 128, "bf16", 500000.0, 8.0, 16384)
+    inp = wl.make_prefill(cfg)
+    th_dev, scale = lib_theta(128, cfg.base, cfg.factor, cfg.original_max_position)
+    cu = torch.from_numpy(inp["cu_seqlens"]).cuda()
+    q, k, v = to_dev(inp["q"], "bf16"), to_dev(inp["k"], "bf16"), to_dev(inp["v"], "bf16")
+    say("prefill k_rotated flag vs internal key pass")
+    a, al = ops.attn_prefill_fwd(q, k, v, cu, 700, th_dev, scale)
+    kr = ops.rope_apply_packed(k, cu, 700, th_dev)
+    b, bl = ops.attn_prefill_fwd(q, kr, v, cu, 700, th_dev, scale, k_rotated=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(al, bl)

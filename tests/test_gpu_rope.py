@@ -59,3 +59,47 @@ def test_rope_apply_empty():
     th_dev, _ = lib_theta(64, 10000.0, 4.0, 64)
     x = torch.empty(0, 2, 64, device="cuda")
     ops.rope_apply(x, torch.empty(0, dtype=torch.int32, device="cuda"), th_dev)
+
+
+@pytest.mark.parametrize("dtype,lens,H,D", [
+    ("bf16", (1, 300, 77, 1024), 8, 128),
+    ("f32", (5, 1, 64), 2, 64),
+])
+def test_rope_apply_packed_matches_oracle(dtype, lens, H, D):
+    rng = np.random.Generator(np.random.PCG64(200 + len(lens)))
+    T = sum(lens)
+    x32 = rng.standard_normal((T, H, D), dtype=np.float32)
+    x = wl.round_to_bf16_bits(x32) if dtype == "bf16" else x32
+    cu = wl.cu_seqlens_of(lens)
+    pos = np.concatenate([np.arange(n) for n in lens])
+    th_dev, _ = lib_theta(D, 500000.0, 8.0, 16384)
+    th_ref, _ = oracle_theta(D, 500000.0, 8.0, 16384)
+    say(f"rope_apply_packed {dtype} lens={lens}")
+    src = to_dev(x, dtype)
+    err = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    dst = ops.rope_apply_packed(src, torch.from_numpy(cu).cuda(), max(lens), th_dev, dev_error=err)
+    # in place gives the same bits
+    src2 = src.clone()
+    ops.rope_apply_packed(src2, torch.from_numpy(cu).cuda(), max(lens), th_dev, dst=src2)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.equal(dst, src2)
+    assert torch.equal(src, to_dev(x, dtype))          # out of place left src alone
+    ref = orope.rotate(wl.as_f64(x, dtype), pos, th_ref)
+    assert max_abs(to_f64(dst), ref) <= (F32_TOL if dtype == "f32" else BF16_TOL)
+    # and it equals rope_apply at the same explicit positions
+    y = to_dev(x, dtype)
+    ops.rope_apply(y, torch.from_numpy(pos.astype(np.int32)).cuda(), th_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(y, dst)
+
+
+def test_rope_apply_packed_flags_bad_cu():
+    th_dev, _ = lib_theta(64, 10000.0, 4.0, 64)
+    x = torch.randn(40, 2, 64, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("rope_apply_packed bad cu_seqlens")
+    ops.rope_apply_packed(x, torch.tensor([0, 30, 20], dtype=torch.int32, device="cuda"), 40, th_dev,
+                          dev_error=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == ops.YR_DEVERR_CU_SEQLENS

@@ -81,6 +81,35 @@ int rope_apply(void *x, int dtype, long long T, int H, int head_dim, const int *
   return YR_OK;
 }
 
+int rope_apply_packed(const void *src, void *dst, int dtype, const int *cu_seqlens, int B,
+                      int max_seqlen, long long T, int H, int head_dim,
+                      const double *inv_freq_f64, int *dev_error, void *stream) {
+  if (dtype != YR_F32 && dtype != YR_BF16) return fail(YR_ERR_UNSUPPORTED, "rope_apply_packed: dtype");
+  if (T < 0 || H < 1 || head_dim < 2 || head_dim > 512 || (head_dim & 1))
+    return fail(YR_ERR_INVALID, "rope_apply_packed: need T >= 0, H >= 1, even head_dim in [2, 512]");
+  if (B < 1 || max_seqlen < 1) return fail(YR_ERR_INVALID, "rope_apply_packed: need B >= 1, max_seqlen >= 1");
+  if (T * (long long)H * head_dim > (1LL << 46))
+    return fail(YR_ERR_INVALID, "rope_apply_packed: tensor too large");
+  if (!cu_seqlens || !inv_freq_f64 || ((!src || !dst) && T > 0))
+    return fail(YR_ERR_NULL, "rope_apply_packed: null pointer");
+  RopeArgs a{};
+  a.src = src;
+  a.dst = dst;
+  a.dtype = dtype;
+  a.T = T;
+  a.H = H;
+  a.head_dim = head_dim;
+  a.positions = nullptr;
+  a.cu_seqlens = cu_seqlens;
+  a.B = B;
+  a.max_seqlen = max_seqlen;
+  a.theta = inv_freq_f64;
+  a.dev_flag = dev_error;
+  const hipError_t e = launch_rope(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "rope_apply_packed");
+  return YR_OK;
+}
+
 size_t attn_prefill_workspace_bytes(long long T, int Hkv, int head_dim, int in_dtype) {
   if (T < 0 || Hkv < 1 || head_dim < 1) return kHeader;
   const size_t elem = in_dtype == YR_F32 ? 4 : 2;
@@ -89,9 +118,10 @@ size_t attn_prefill_workspace_bytes(long long T, int Hkv, int head_dim, int in_d
 
 int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
                      const int *cu_seqlens, int B, int max_seqlen, long long T, int Hq, int Hkv,
-                     int head_dim, const double *inv_freq_f64, float softmax_scale, void *out,
-                     int out_dtype, float *lse, void *workspace, size_t workspace_bytes,
+                     int head_dim, const double *inv_freq_f64, int flags, float softmax_scale,
+                     void *out, int out_dtype, float *lse, void *workspace, size_t workspace_bytes,
                      void *stream) {
+  if (flags & ~YR_PREFILL_K_ROTATED) return fail(YR_ERR_INVALID, "attn_prefill_fwd: unknown flags");
   if (in_dtype != YR_F32 && in_dtype != YR_BF16)
     return fail(YR_ERR_UNSUPPORTED, "attn_prefill_fwd: in_dtype must be YR_F32 or YR_BF16");
   if (out_dtype != YR_F32 && out_dtype != YR_BF16)
@@ -111,7 +141,8 @@ int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
     return fail(YR_ERR_NULL, "attn_prefill_fwd: q, k, v, cu_seqlens, out and workspace are required");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return fail(YR_ERR_WORKSPACE, "attn_prefill_fwd: workspace must be 256-byte aligned");
-  const size_t need = inv_freq_f64 ? attn_prefill_workspace_bytes(T, Hkv, head_dim, in_dtype) : kHeader;
+  const bool key_pass = inv_freq_f64 != nullptr && !(flags & YR_PREFILL_K_ROTATED);
+  const size_t need = key_pass ? attn_prefill_workspace_bytes(T, Hkv, head_dim, in_dtype) : kHeader;
   if (workspace_bytes < need) return fail(YR_ERR_WORKSPACE, "attn_prefill_fwd: workspace too small");
   const long long ntiles = (max_seqlen + 63) / 64;
   if (ntiles * (long long)B * Hq > 0x7fffffffLL)
@@ -138,7 +169,7 @@ int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
   p.lse = lse;
   p.dev_flag = flag;
 
-  if (inv_freq_f64 != nullptr && T > 0) {
+  if (key_pass && T > 0) {
     // rotate every key once into the workspace; the attention kernel rotates
     // queries on load and reads the rotated keys
     void *krot = static_cast<char *>(workspace) + kHeader;

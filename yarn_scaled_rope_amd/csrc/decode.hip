@@ -25,40 +25,70 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kUnroll = 4;  // keys per lane group per iteration
+constexpr int kUnroll = 8;  // keys per lane group per iteration (loads in flight)
 constexpr float kLn2 = 0.69314718055994530942f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// 8 consecutive elements of a cache row as floats.
+// 8 consecutive elements of a cache row: loaded raw (non-temporal: the sweep
+// reads each byte once), widened to float at use.
 template <typename T>
 struct Row8;
 template <>
 struct Row8<uint16_t> {
-  __device__ static void load(const uint16_t *p, float *x) {
-    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  struct Raw {
+    u32x4 w;
+  };
+  __device__ static Raw load(const uint16_t *p) {
+    return Raw{__builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p))};
+  }
+  __device__ static Raw zero() { return Raw{u32x4{0u, 0u, 0u, 0u}}; }
+  __device__ static void widen(const Raw &r, float *x) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      x[2 * e] = bf16_to_f32(w[e] & 0xffffu);
-      x[2 * e + 1] = bf16_to_f32(w[e] >> 16);
+      x[2 * e] = bf16_to_f32(r.w[e] & 0xffffu);
+      x[2 * e + 1] = bf16_to_f32(r.w[e] >> 16);
     }
   }
   __device__ static float scalar(const uint16_t *p) { return bf16_to_f32(*p); }
 };
 template <>
 struct Row8<float> {
-  __device__ static void load(const float *p, float *x) {
-    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
-    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p + 4));
+  struct Raw {
+    f32x4 a, b;
+  };
+  __device__ static Raw load(const float *p) {
+    return Raw{__builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p)),
+               __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p + 4))};
+  }
+  __device__ static Raw zero() { return Raw{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}; }
+  __device__ static void widen(const Raw &r, float *x) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      x[e] = a[e];
-      x[4 + e] = b[e];
+      x[e] = r.a[e];
+      x[4 + e] = r.b[e];
     }
   }
   __device__ static float scalar(const float *p) { return *p; }
 };
+
+// Sum over the LPK lanes that share a key row (LPK = 16 or 8 adjacent lanes of
+// one DPP row); every lane gets the total.  DPP moves, no LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+template <int LPK>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp_move<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_move<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_move<0x141>(x);  // row_half_mirror: quads 0<->1, 2<->3
+  if (LPK == 16) x += dpp_move<0x140>(x);  // row_mirror: half rows swap
+  return x;
+}
 
 // Merge running state (m, l, acc[8]) with another one; -inf maxima mean
 // "no key seen yet".
@@ -120,25 +150,29 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   const int grp = lane / LPK;  // which key row of the wave load
   const int d0 = sub * 8;
 
-  // query slice, rotated at its position and pre-scaled into log2 units
+  // query slice, rotated at its position and pre-scaled into log2 units; the
+  // angle of a pair is the same for every head of the group
   float qv[GM][8];
   {
     int m = qpos != nullptr ? qpos[b] : L;
     m = m < 0 ? 0 : m;
+    float cs[4], sn[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      cs[e] = 1.f;
+      sn[e] = 0.f;
+      if (theta != nullptr) rope_cos_sin((double)m, theta[(d0 >> 1) + e], &cs[e], &sn[e]);
+    }
 #pragma unroll
     for (int gi = 0; gi < GM; ++gi) {
       if (gi < g) {
         const T *qp = q + ((long long)b * Hq + hk * g + gi) * D + d0;
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          float x0 = Row8<T>::scalar(qp + e), x1 = Row8<T>::scalar(qp + e + 1);
-          if (theta != nullptr) {
-            float c, s;
-            rope_cos_sin((double)m, theta[(d0 + e) >> 1], &c, &s);
-            rotate_pair(x0, x1, c, s);
-          }
-          qv[gi][e] = x0 * scale_log2;
-          qv[gi][e + 1] = x1 * scale_log2;
+        for (int e = 0; e < 4; ++e) {
+          float x0 = Row8<T>::scalar(qp + 2 * e), x1 = Row8<T>::scalar(qp + 2 * e + 1);
+          rotate_pair(x0, x1, cs[e], sn[e]);
+          qv[gi][2 * e] = x0 * scale_log2;
+          qv[gi][2 * e + 1] = x1 * scale_log2;
         }
       } else {
 #pragma unroll
@@ -161,55 +195,67 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   const T *vb = vc + ((long long)b * Lmax * Hkv + hk) * D + d0;
 
   for (int base = c0 + wave * KPW; base < c1; base += KPI) {
-    float kx[kUnroll][8], vx[kUnroll][8];
+    typename Row8<T>::Raw kr[kUnroll], vr[kUnroll];
     bool ok[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int key = base + u * GPW + grp;
       ok[u] = key < c1;
-      if (ok[u]) {
-        Row8<T>::load(kb + key * rstride, kx[u]);
-        Row8<T>::load(vb + key * rstride, vx[u]);
-      } else {
+      kr[u] = ok[u] ? Row8<T>::load(kb + key * rstride) : Row8<T>::zero();
+      vr[u] = ok[u] ? Row8<T>::load(vb + key * rstride) : Row8<T>::zero();
+    }
+    float sc[GM][kUnroll];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kx[u][e] = vx[u][e] = 0.f;
+    for (int u = 0; u < kUnroll; ++u) {
+      float kx[8];
+      Row8<T>::widen(kr[u], kx);
+#pragma unroll
+      for (int gi = 0; gi < GM; ++gi) {
+        float p = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p = fmaf(qv[gi][e], kx[e], p);
+        sc[gi][u] = p;
       }
     }
 #pragma unroll
     for (int gi = 0; gi < GM; ++gi) {
-      if (gi >= g) break;
-      float sc[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        float p = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p += qv[gi][e] * kx[u][e];
-#pragma unroll
-        for (int off = LPK / 2; off >= 1; off >>= 1) p += __shfl_xor(p, off);
-        sc[u] = ok[u] ? p : -INFINITY;
+        const float t = group_sum<LPK>(sc[gi][u]);
+        sc[gi][u] = ok[u] ? t : -INFINITY;
       }
-      float mx = sc[0];
+    }
+    float pu[GM][kUnroll];
 #pragma unroll
-      for (int u = 1; u < kUnroll; ++u) mx = fmaxf(mx, sc[u]);
+    for (int gi = 0; gi < GM; ++gi) {
+      if (gi >= g) break;
+      float mx = sc[gi][0];
+#pragma unroll
+      for (int u = 1; u < kUnroll; ++u) mx = fmaxf(mx, sc[gi][u]);
       const float mn = fmaxf(mrun[gi], mx);
       const float mu = mn == -INFINITY ? 0.f : mn;
       const float alpha = __builtin_amdgcn_exp2f(mrun[gi] - mu);
       float psum = 0.f;
-      float pu[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        pu[u] = __builtin_amdgcn_exp2f(sc[u] - mu);
-        psum += pu[u];
+        pu[gi][u] = __builtin_amdgcn_exp2f(sc[gi][u] - mu);
+        psum += pu[gi][u];
       }
       lrun[gi] = lrun[gi] * alpha + psum;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float a = acc[gi][e] * alpha;
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) a += pu[u] * vx[u][e];
-        acc[gi][e] = a;
-      }
+      for (int e = 0; e < 8; ++e) acc[gi][e] *= alpha;
       mrun[gi] = mn;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float vx[8];
+      Row8<T>::widen(vr[u], vx);
+#pragma unroll
+      for (int gi = 0; gi < GM; ++gi) {
+        if (gi >= g) break;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[gi][e] = fmaf(pu[gi][u], vx[e], acc[gi][e]);
+      }
     }
   }
 

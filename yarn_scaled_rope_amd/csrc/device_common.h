@@ -15,17 +15,18 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// float -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+typedef __bf16 yr_bf16x2 __attribute__((ext_vector_type(2)));
+
+// float -> bfloat16 bits, round to nearest even (the hardware conversion,
+// v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// Two floats -> packed bf16 pair (lo in bits 0..15).
+// Two floats -> packed bf16 pair (lo in bits 0..15), one instruction.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const yr_bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // cos and sin of (pos * theta).  The product and its reduction to

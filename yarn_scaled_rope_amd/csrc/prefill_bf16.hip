@@ -191,30 +191,40 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       }
     }
 
-    // ---- scale, mask, row max -------------------------------------------
+    // ---- mask, row max (on raw scores: the scale is positive) ----------
     const bool need_mask = (key0 + kBC - 1 > tw0) || (key0 + kBC > n);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+          if (key > tq || key >= n) sc[kb][r] = -INFINITY;
+        }
+      }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sc[kb][r] * scale_log2;
-        if (need_mask) {
-          const int key = key0 + kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-          if (key > tq || key >= n) x = -INFINITY;
-        }
-        sc[kb][r] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    l_part *= alpha;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+
+    // ---- lazy rescale: the reference max moves only when the row max
+    // exceeds it by more than 2^8, so exp2 stays <= 256 and the O rescale
+    // (64 multiplies) is skipped on most tiles; softmax does not depend on
+    // the reference, so the result is unchanged up to rounding.
+    const bool grow = mx > m_run + 8.0f;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+      m_run = m_new;
+      l_part *= alpha;
 #pragma unroll
-    for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
+      for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
+    }
+    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
 
     // ---- P^T in bf16, 4 k-steps of 16 keys ------------------------------
     bf16x8 pf[4];
@@ -223,8 +233,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       u32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(sc[ks >> 1][(ks & 1) * 8 + 2 * e] - m_use);
-        const float p1 = __builtin_amdgcn_exp2f(sc[ks >> 1][(ks & 1) * 8 + 2 * e + 1] - m_use);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[ks >> 1][(ks & 1) * 8 + 2 * e], scale_log2, neg_m));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[ks >> 1][(ks & 1) * 8 + 2 * e + 1], scale_log2, neg_m));
         l_part += p0 + p1;
         w[e] = pack_bf16x2(p0, p1);
       }

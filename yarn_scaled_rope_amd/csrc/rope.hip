@@ -18,7 +18,6 @@ template <typename T>
 struct Elem;
 template <>
 struct Elem<float> {
-  using pair_t = float2;
   __device__ static void load(const float *p, float &a, float &b) {
     const float2 v = *reinterpret_cast<const float2 *>(p);
     a = v.x;
@@ -51,7 +50,7 @@ __device__ __forceinline__ int seq_of_row(const int *__restrict__ cu, int B, lon
 }
 
 template <typename T, bool FROM_CU>
-__global__ __launch_bounds__(256) void rope_kernel(const T *__restrict__ src, T *__restrict__ dst,
+__global__ __launch_bounds__(256) void rope_kernel(const T *src, T *dst,  // may alias (in place)
                                                   long long ntok, int H, int D,
                                                   const int *__restrict__ pos_or_cu, int B,
                                                   int max_seqlen, const double *__restrict__ theta,

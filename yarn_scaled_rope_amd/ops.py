@@ -32,6 +32,8 @@ YR_ROPE_NTK = 2
 YR_ROPE_YARN = 3
 METHODS = {"plain": YR_ROPE_PLAIN, "pi": YR_ROPE_PI, "ntk": YR_ROPE_NTK, "yarn": YR_ROPE_YARN}
 
+YR_PREFILL_K_ROTATED = 1
+
 YR_DEVERR_CU_SEQLENS = 1
 YR_DEVERR_SEQLENS = 2
 YR_DEVERR_QPOS = 4
@@ -53,8 +55,9 @@ def _declare(lib):
     sig = {
         "yarn_rope_freqs": (i, [i, d, d, ll, d, d, i, vp, vp, vp]),
         "rope_apply": (i, [vp, i, ll, i, i, vp, vp, vp]),
+        "rope_apply_packed": (i, [vp, vp, i, vp, i, i, ll, i, i, vp, vp, vp]),
         "attn_prefill_workspace_bytes": (sz, [ll, i, i, i]),
-        "attn_prefill_fwd": (i, [vp, vp, vp, i, vp, i, i, ll, i, i, i, vp, f, vp, i, vp, vp, sz, vp]),
+        "attn_prefill_fwd": (i, [vp, vp, vp, i, vp, i, i, ll, i, i, i, vp, i, f, vp, i, vp, vp, sz, vp]),
         "attn_decode_workspace_bytes": (sz, [i, i, i, i]),
         "attn_decode": (i, [vp, vp, vp, i, vp, vp, i, i, i, i, i, vp, f, vp, i, vp, vp, sz, vp]),
         "yr_read_device_error": (i, [vp, vp, vp]),
@@ -149,6 +152,29 @@ def rope_apply(x: torch.Tensor, positions: torch.Tensor, inv_freq_f64: torch.Ten
     return x
 
 
+def rope_apply_packed(src: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                      inv_freq_f64: torch.Tensor, dst: Optional[torch.Tensor] = None,
+                      dev_error: Optional[torch.Tensor] = None, stream=None):
+    """Rotate the rows of a packed batch [T, H, D] at their in-sequence
+    positions into dst (a new tensor by default; may be src)."""
+    _need(src, "src")
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    _need(inv_freq_f64, "inv_freq_f64", torch.float64)
+    if dst is None:
+        dst = torch.empty_like(src)
+    _need(dst, "dst", src.dtype)
+    if dst.shape != src.shape:
+        raise YarnAttnError(YR_ERR_INVALID, "dst must match src")
+    if dev_error is not None:
+        _need(dev_error, "dev_error", torch.int32)
+    T, H, D = src.shape
+    lib = load_library()
+    _check(lib.rope_apply_packed(_ptr(src), _ptr(dst), _dtype_code(src), _ptr(cu_seqlens),
+                                 cu_seqlens.numel() - 1, int(max_seqlen), T, H, D,
+                                 _ptr(inv_freq_f64), _ptr(dev_error), _stream(stream)))
+    return dst
+
+
 # ------------------------------------------------------------------ prefill
 def attn_prefill_workspace_bytes(T: int, hkv: int, head_dim: int, in_dtype: int) -> int:
     return int(load_library().attn_prefill_workspace_bytes(T, hkv, head_dim, in_dtype))
@@ -156,9 +182,10 @@ def attn_prefill_workspace_bytes(T: int, hkv: int, head_dim: int, in_dtype: int)
 
 def attn_prefill_fwd(q, k, v, cu_seqlens, max_seqlen: int, inv_freq_f64, softmax_scale: float,
                      out=None, out_dtype=None, lse=None, workspace=None, want_lse=True,
-                     stream=None):
+                     k_rotated=False, stream=None):
     """Causal prefill.  q [T, Hq, D], k/v [T, Hkv, D] unrotated (or rotated,
-    with inv_freq_f64=None); cu_seqlens int32 [B+1].  Returns (out, lse)."""
+    with inv_freq_f64=None; or only k rotated, with k_rotated=True);
+    cu_seqlens int32 [B+1].  Returns (out, lse)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n)
     _need(cu_seqlens, "cu_seqlens", torch.int32)
@@ -176,13 +203,15 @@ def attn_prefill_fwd(q, k, v, cu_seqlens, max_seqlen: int, inv_freq_f64, softmax
         _need(out, "out", _torch_dtype(out_code))
     if lse is None and want_lse:
         lse = torch.empty((hq, T), dtype=torch.float32, device=q.device)
-    need = attn_prefill_workspace_bytes(T, hkv, D, in_code) if inv_freq_f64 is not None else 256
+    key_pass = inv_freq_f64 is not None and not k_rotated
+    need = attn_prefill_workspace_bytes(T, hkv, D, in_code) if key_pass else 256
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     B = cu_seqlens.numel() - 1
     lib = load_library()
     _check(lib.attn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), in_code, _ptr(cu_seqlens), B,
                                 int(max_seqlen), T, hq, hkv, D, _ptr(inv_freq_f64),
+                                YR_PREFILL_K_ROTATED if k_rotated else 0,
                                 float(softmax_scale), _ptr(out), out_code, _ptr(lse),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 _stream(stream)))
