@@ -29,18 +29,30 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// cos and sin of (pos * theta).  The product and its reduction to
-// [-pi, pi] are done in fp64 (exact to ~1e-11 rad for positions up to 2^20),
-// the sine and cosine of the reduced angle in fp32.
+// cos and sin of (pos * theta).  The product and its Cody-Waite reduction by
+// pi/2 are done in fp64 (exact to ~1e-11 rad for positions up to 2^20); the
+// reduced angle, in [-pi/4, pi/4], goes through the single-precision minimax
+// polynomials of the Cephes library (sinf/cosf), and the quadrant picks the
+// signs.  Max abs error ~1e-7 (about 1.5 fp32 ulp of 1.0).
 __device__ __forceinline__ void rope_cos_sin(double pos, double theta, float *c, float *s) {
-  constexpr double kInvTwoPi = 0.15915494309189533577;
-  constexpr double kTwoPiHi = 6.283185307179586232;    // nearest double to 2 pi
-  constexpr double kTwoPiLo = 2.4492935982947064e-16;  // 2 pi - kTwoPiHi
+  constexpr double kTwoOverPi = 0.63661977236758134308;
+  constexpr double kPio2Hi = 1.5707963267948966192;    // nearest double to pi/2
+  constexpr double kPio2Lo = 6.123233995736766036e-17;  // pi/2 - kPio2Hi
   const double x = pos * theta;
-  const double kq = rint(x * kInvTwoPi);
-  double r = fma(-kq, kTwoPiHi, x);
-  r = fma(-kq, kTwoPiLo, r);
-  sincosf((float)r, s, c);
+  const double kq = rint(x * kTwoOverPi);
+  double r = fma(-kq, kPio2Hi, x);
+  r = fma(-kq, kPio2Lo, r);
+  const float rf = (float)r, z = rf * rf;
+  const float sp = fmaf(rf * z, fmaf(z, fmaf(z, -1.9515295891e-4f, 8.3321608736e-3f), -1.6666654611e-1f), rf);
+  const float cp = fmaf(z * z, fmaf(z, fmaf(z, 2.443315711809948e-5f, -1.388731625493765e-3f), 4.166664568298827e-2f),
+                        fmaf(-0.5f, z, 1.0f));
+  const int quad = (int)((long long)kq & 3);
+  float ss = (quad & 1) ? cp : sp;
+  float cc = (quad & 1) ? sp : cp;
+  if (quad == 1 || quad == 2) cc = -cc;
+  if (quad >= 2) ss = -ss;
+  *c = cc;
+  *s = ss;
 }
 
 // Rotate one pair in fp32.  The fused multiply-adds are written out so that
