@@ -19,9 +19,11 @@
 //     owns a query owns its output column and its rescale factor.
 //   * P^T goes straight from the score accumulator into the B operand: the
 //     8 consecutive accumulator registers 8*(ks%2)..+7 of key block ks/2 are
-//     one 16-key k-step, with the key order permuted identically in V^T.
-//   * K tiles are staged row-major in LDS (padded rows), V tiles transposed
-//     (V^T[d][key], 4-key units XOR-swizzled per row), both double-buffered:
+//     one 16-key k-step.  K rows are permuted in LDS (kperm) so that those 8
+//     registers are 8 consecutive keys, read from V^T as one 16-byte load.
+//   * K tiles are staged row-major in LDS, V tiles transposed (V^T[d][key]),
+//     rows padded so that both the staging writes and the operand reads are
+//     free of bank conflicts, and double-buffered:
 //     one barrier per 64-key tile, and the loads of tile j+1 are in flight
 //     while tile j is computed.  Loads are buffer
 //     loads whose range ends at the sequence end, so rows past it read as 0
@@ -46,7 +48,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kBC = 64;    // keys per tile
-constexpr int kKPad = 8;   // bf16 elements of padding per K row (row = 68 dwords)
+constexpr int kKPad = 8;   // bf16 elements of padding per K row   (row = 68 dwords)
+constexpr int kVPad = 8;   // bf16 elements of padding per V^T row (row = 36 dwords)
 constexpr int kXcds = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr uint32_t kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, range-checked
@@ -54,21 +57,30 @@ constexpr uint32_t kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, range-checked
 template <int D>
 struct Smem {
   uint16_t k[2][kBC][D + kKPad];
-  uint16_t vt[2][D][kBC];  // 4-key units XOR-swizzled per row, see vt_unit()
+  uint16_t vt[2][D][kBC + kVPad];
 };
 
-// V^T rows hold 16 units of 4 keys (8 bytes).  Unit u of row d is stored at
-// u ^ g(d), g(d) = ((d >> 3) + 2 (d & 7)) & 15: the transposing writes (16
-// lanes on rows 8 apart) and the operand reads (16 lanes on consecutive rows)
-// then both hit 16 distinct bank pairs.
-__device__ __forceinline__ int vt_unit(int d, int u) { return u ^ (((d >> 3) + 2 * (d & 7)) & 15); }
+// LDS row r of a K tile holds key kperm(r): bits 2 and 3 of the row index
+// swapped within each 16.  The score accumulator slot 8j + 4h + i (lane half
+// h) then belongs to key 16(j >> 1) + 8h + 4(j & 1) + i, so the 8 accumulator
+// registers that form one 16-key k-step of P hold 8 CONSECUTIVE keys per lane
+// half, and the matching V^T operand is a single 16-byte LDS read.
+__device__ __forceinline__ int kperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
 __device__ __forceinline__ uint32_t sel16(uint32_t w, int hi) { return hi ? (w >> 16) : (w & 0xffffu); }
 
+// Buffer descriptor over [base, base + bytes).  Callers pass wave-uniform
+// values; readfirstlane puts them in scalar registers, where the descriptor
+// must live (otherwise the compiler wraps every load in a waterfall loop).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, (int)kRsrcWord3);
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void *p = (void *)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           (int)kRsrcWord3);
 }
 
 template <int D, bool OUT_F32, bool ROTATE_Q, int QB>
@@ -82,7 +94,7 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel
   constexpr int CH = D / 8;             // 16-byte chunks per row
   constexpr int KROWS = kThreads / CH;  // K rows per load pass
   constexpr int KPASS = kBC / KROWS;
-  constexpr int VUNITS = CH * (kBC / 4);  // (chunk, 4-key group) units of a V tile
+  constexpr int VUNITS = CH * (kBC / 4);  // (4-key group, chunk) units of a V tile
   constexpr int RW = 32 * QB;             // query rows per wave
   constexpr int BQ = 4 * RW;              // query rows per workgroup
   static_assert(VUNITS <= kThreads, "V tile mapping");
@@ -102,6 +114,11 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel
   long long s0;
   int n;
   seq_bounds(cu, b, T, max_seqlen, &s0, &n);
+  // uniform across the workgroup: keep them in scalar registers so the
+  // per-tile buffer descriptors need no per-lane fix-up
+  n = __builtin_amdgcn_readfirstlane(n);
+  s0 = ((long long)__builtin_amdgcn_readfirstlane((int)(s0 >> 32)) << 32) |
+       (unsigned)__builtin_amdgcn_readfirstlane((int)(s0 & 0xffffffff));
   const int q0 = tile * BQ;
   if (q0 >= n) return;
   const int qend = min(n, q0 + BQ);
@@ -151,8 +168,9 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel
   }
 
   // ---- staging maps ------------------------------------------------------
-  const int krow0 = tid / CH, kch = tid % CH;       // K: row krow0 + KROWS*p, chunk kch
-  const int vch = tid % CH, vkey = (tid / CH) * 4;  // V: chunk vch, keys vkey..vkey+3
+  const int krow0 = tid / CH, kch = tid % CH;   // K: LDS row krow0 + KROWS*p, chunk kch
+  const int kkey0 = kperm(krow0);                // ... holding key kperm(row)
+  const int vkey = (tid & 15) * 4, vch = tid >> 4;  // V: keys vkey..vkey+3, chunk vch
   const bool vact = tid < VUNITS;
   const long long rstride = (long long)Hkv * D;     // elements between key rows
   const uint16_t *kseq = k + (s0 * Hkv + hk) * (long long)D;
@@ -168,7 +186,7 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vseq + key0 * rstride, valid);
 #pragma unroll
     for (int p = 0; p < KPASS; ++p)
-      kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(kr, (krow0 + p * KROWS) * rbytes + kch * 16, 0, 0);
+      kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(kr, (kkey0 + p * KROWS) * rbytes + kch * 16, 0, 0);
     if (vact) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
@@ -186,8 +204,7 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel
         u32x2 pk;
         pk[0] = sel16(vreg[0][wsel], hi) | (sel16(vreg[1][wsel], hi) << 16);
         pk[1] = sel16(vreg[2][wsel], hi) | (sel16(vreg[3][wsel], hi) << 16);
-        const int row = vch * 8 + e;
-        *reinterpret_cast<u32x2 *>(&sm.vt[buf][row][4 * vt_unit(row, vkey >> 2)]) = pk;
+        *reinterpret_cast<u32x2 *>(&sm.vt[buf][vch * 8 + e][vkey]) = pk;
       }
     }
   };
@@ -235,7 +252,7 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) {
-            const int key = key0 + kb * 32 + (rr >> 2) * 8 + hh * 4 + (rr & 3);
+            const int key = key0 + kb * 32 + (rr >> 3) * 16 + hh * 8 + ((rr >> 2) & 1) * 4 + (rr & 3);
             if (key > tq || key >= n) sc[qb][kb][rr] = -INFINITY;
           }
         }
@@ -278,13 +295,10 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel
     // ---- O^T += V^T P^T, each V^T fragment used QB times --------------------
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
-      const int row = db * 32 + l32;
-      const uint16_t *vrow = &sm.vt[buf][row][0];
+      const uint16_t *vrow = &sm.vt[buf][db * 32 + l32][hh * 8];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + 4 * vt_unit(row, 4 * ks + hh));
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 4 * vt_unit(row, 4 * ks + 2 + hh));
-        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(vrow + ks * 16);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), pf[qb][ks], o[qb][db], 0, 0, 0);
