@@ -79,8 +79,7 @@ def test_fp32_ragged(lens, hq, hkv, D):
     ((700,), 8, 1, 64, ops.YR_BF16),
     ((33, 1, 1, 160), 16, 2, 64, ops.YR_F32),
     ((1000,), 2, 1, 128, ops.YR_BF16),
-    # enough 256-row tiles (B * Hq * ceil(max_len / 256) >= 512) for the
-    # 64-rows-per-wave variant of the kernel
+    # many heads per KV head, several sequences sharing the grid
     ((1000, 999, 1, 77), 64, 8, 128, ops.YR_BF16),
     ((600, 257), 128, 16, 64, ops.YR_F32),
 ])

@@ -7,27 +7,28 @@
 // sums and output accumulators; "LLM context window mechanics": tiles kept on
 // chip).  Queries are rotated on load with fp64 angles; keys arrive rotated.
 //
-// Work decomposition (one workgroup = 4 waves, one query head, QB*128 rows):
-//   * Every wave owns QB blocks of 32 consecutive query rows.  Scores are
-//     formed transposed, S^T = K * Q^T, so the 32x32 accumulator of a lane
-//     holds ONE query (lane % 32) against 16 keys; the row max and row sum
-//     need only the lane's own registers plus one exchange with lane ^ 32.
-//   * Each K / V^T fragment read from LDS feeds QB matrix instructions (one
-//     per query block): with QB = 2 the LDS traffic per FLOP halves, which is
-//     what lets the matrix cores run faster than LDS can feed 32-row waves.
+// Work decomposition (one workgroup = 4 waves = 128 query rows of one head):
+//   * Every wave owns 32 consecutive query rows.  Scores are formed
+//     transposed, S^T = K * Q^T, so the 32x32 accumulator of a lane holds ONE
+//     query (lane % 32) against 16 keys; the row max and row sum need only
+//     the lane's own registers plus one exchange with lane ^ 32.
 //   * The output is also formed transposed, O^T = V^T * P^T, so the lane that
 //     owns a query owns its output column and its rescale factor.
 //   * P^T goes straight from the score accumulator into the B operand: the
 //     8 consecutive accumulator registers 8*(ks%2)..+7 of key block ks/2 are
 //     one 16-key k-step.  K rows are permuted in LDS (kperm) so that those 8
 //     registers are 8 consecutive keys, read from V^T as one 16-byte load.
-//   * K tiles are staged row-major in LDS, V tiles transposed (V^T[d][key]),
-//     rows padded so that both the staging writes and the operand reads are
-//     free of bank conflicts, and double-buffered:
-//     one barrier per 64-key tile, and the loads of tile j+1 are in flight
-//     while tile j is computed.  Loads are buffer
-//     loads whose range ends at the sequence end, so rows past it read as 0
-//     without branches.
+//   * Software pipeline inside each wave: step j issues the score MFMAs of
+//     tile j+1 and, independent of them, the softmax of tile j (VALU and
+//     transcendental work), then the PV MFMAs of tile j.  The matrix cores
+//     and the vector ALUs of one wave therefore overlap without relying on
+//     the other wave of the SIMD being out of phase.
+//   * K tiles are staged two tiles ahead and V tiles one tile ahead in LDS
+//     (double-buffered each; K row-major, V transposed to V^T[d][key]), rows
+//     padded so that both the staging writes and the operand reads are free
+//     of bank conflicts; one barrier per step; the global loads of the next
+//     tiles are in flight while a step computes.  Loads are buffer loads
+//     whose range ends at the sequence end, so rows past it read as 0.
 //   * The running max is lazy: it moves only when a row max exceeds it by
 //     more than 2^8, so the O rescale is skipped on most tiles.
 //   * Tiles wholly above a wave's diagonal are skipped by that wave; masking
@@ -47,6 +48,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
+constexpr int kBQ = 128;   // query rows per workgroup (4 waves x 32)
 constexpr int kBC = 64;    // keys per tile
 constexpr int kKPad = 8;   // bf16 elements of padding per K row   (row = 68 dwords)
 constexpr int kVPad = 8;   // bf16 elements of padding per V^T row (row = 36 dwords)
@@ -83,8 +85,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                            (int)kRsrcWord3);
 }
 
-template <int D, bool OUT_F32, bool ROTATE_Q, int QB>
-__global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel(
+template <int D, bool OUT_F32, bool ROTATE_Q>
+__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int *__restrict__ cu, int B, int max_seqlen,
     long long T, int Hq, int Hkv, const double *__restrict__ theta, float scale_log2,
@@ -95,8 +97,6 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel
   constexpr int KROWS = kThreads / CH;  // K rows per load pass
   constexpr int KPASS = kBC / KROWS;
   constexpr int VUNITS = CH * (kBC / 4);  // (4-key group, chunk) units of a V tile
-  constexpr int RW = 32 * QB;             // query rows per wave
-  constexpr int BQ = 4 * RW;              // query rows per workgroup
   static_assert(VUNITS <= kThreads, "V tile mapping");
 
   __shared__ __align__(16) Smem<D> sm;
@@ -119,22 +119,21 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel
   n = __builtin_amdgcn_readfirstlane(n);
   s0 = ((long long)__builtin_amdgcn_readfirstlane((int)(s0 >> 32)) << 32) |
        (unsigned)__builtin_amdgcn_readfirstlane((int)(s0 & 0xffffffff));
-  const int q0 = tile * BQ;
+  const int q0 = tile * kBQ;
   if (q0 >= n) return;
-  const int qend = min(n, q0 + BQ);
+  const int qend = min(n, q0 + kBQ);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int tw0 = q0 + wave * RW;  // first query row of this wave
+  const int tw0 = q0 + wave * 32;  // first query row of this wave
+  const int tq = tw0 + l32;        // this lane's query row
 
   // ---- Q fragments (B operand of S^T = K Q^T), rotated on load -----------
-  bf16x8 qf[QB][KSTEPS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int tq = tw0 + qb * 32 + l32;
+  bf16x8 qf[KSTEPS];
+  {
     const bool qvalid = tq < n;
     const uint16_t *qp = q + ((s0 + (qvalid ? tq : 0)) * Hq + h) * (long long)D + hh * 8;
 #pragma unroll
@@ -153,50 +152,52 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel
           }
         }
       }
-      qf[qb][kk] = as_bf16x8(w);
+      qf[kk] = as_bf16x8(w);
     }
   }
 
-  f32x16 o[QB][DBLK];
-  float m_run[QB], l_part[QB];
+  f32x16 o[DBLK];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-    for (int i = 0; i < DBLK; ++i) o[qb][i] = f32x16{};
-    m_run[qb] = -INFINITY;
-    l_part[qb] = 0.f;
-  }
+  for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY;
+  float l_part = 0.f;
 
-  // ---- staging maps ------------------------------------------------------
-  const int krow0 = tid / CH, kch = tid % CH;   // K: LDS row krow0 + KROWS*p, chunk kch
-  const int kkey0 = kperm(krow0);                // ... holding key kperm(row)
-  const int vkey = (tid & 15) * 4, vch = tid >> 4;  // V: keys vkey..vkey+3, chunk vch
+  // ---- staging: global -> registers -> LDS --------------------------------
+  const int krow0 = tid / CH, kch = tid % CH;       // K: LDS row krow0 + KROWS*p, chunk kch
+  const int kkey0 = kperm(krow0);                    // ... holding key kperm(row)
+  const int vkey = (tid & 15) * 4, vch = tid >> 4;   // V: keys vkey..vkey+3, chunk vch
   const bool vact = tid < VUNITS;
-  const long long rstride = (long long)Hkv * D;     // elements between key rows
+  const long long rstride = (long long)Hkv * D;      // elements between key rows
   const uint16_t *kseq = k + (s0 * Hkv + hk) * (long long)D;
   const uint16_t *vseq = v + (s0 * Hkv + hk) * (long long)D;
   const uint32_t rbytes = (uint32_t)(rstride * 2);
 
   u32x4 kreg[KPASS];
   u32x4 vreg[4];
-  auto gload = [&](int j) {
+  auto gload_k = [&](int j) {
     const int key0 = j * kBC;
-    const uint32_t valid = (uint32_t)min(kBC, n - key0) * rbytes;  // rows past n read as 0
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kseq + key0 * rstride, valid);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vseq + key0 * rstride, valid);
+    const __amdgpu_buffer_rsrc_t kr =
+        make_rsrc(kseq + key0 * rstride, (uint32_t)min(kBC, n - key0) * rbytes);  // rows past n read 0
 #pragma unroll
     for (int p = 0; p < KPASS; ++p)
       kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(kr, (kkey0 + p * KROWS) * rbytes + kch * 16, 0, 0);
+  };
+  auto gload_v = [&](int j) {
+    const int key0 = j * kBC;
+    const __amdgpu_buffer_rsrc_t vr =
+        make_rsrc(vseq + key0 * rstride, (uint32_t)min(kBC, n - key0) * rbytes);
     if (vact) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
         vreg[rr] = __builtin_amdgcn_raw_buffer_load_b128(vr, (vkey + rr) * rbytes + vch * 16, 0, 0);
     }
   };
-  auto swrite = [&](int buf) {
+  auto swrite_k = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p)
       *reinterpret_cast<u32x4 *>(&sm.k[buf][krow0 + p * KROWS][kch * 8]) = kreg[p];
+  };
+  auto swrite_v = [&](int buf) {
     if (vact) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -209,170 +210,206 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel
     }
   };
 
-  const int last_tile = (qend - 1) / kBC;
-  gload(0);
-  for (int j = 0; j <= last_tile; ++j) {
-    const int buf = j & 1;
-    swrite(buf);
-    __syncthreads();
-    if (j < last_tile) gload(j + 1);
+  // ---- per-tile work -------------------------------------------------------
+  // tile j has keys j*64 .. j*64+63; it is wholly above this wave's diagonal
+  // when its first key is past the wave's last query row
+  auto active = [&](int j) { return j * kBC <= tw0 + 31 && tw0 < n; };
 
-    const int key0 = j * kBC;
-    if (key0 > tw0 + RW - 1 || tw0 >= n) continue;  // tile wholly above this wave's diagonal
-
-    // ---- S^T = K Q^T : two 32-key blocks, each K fragment used QB times.
-    // All fragments of a block are read before its matrix instructions so the
-    // LDS reads overlap each other instead of one read per instruction.
-    f32x16 sc[QB][2];
+  // S^T = K Q^T for tile j (two 32-key blocks) from K buffer j & 1
+  auto scores = [&](int j, f32x16 (&s)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sc[qb][kb] = f32x16{};
-      const uint16_t *kr = &sm.k[buf][kb * 32 + l32][hh * 8];
-      bf16x8 a[KSTEPS];
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) a[kk] = as_bf16x8(*reinterpret_cast<const u32x4 *>(kr + kk * 16));
+      s[kb] = f32x16{};
+      const uint16_t *kr = &sm.k[j & 1][kb * 32 + l32][hh * 8];
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          sc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], qf[qb][kk], sc[qb][kb], 0, 0, 0);
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(kr + kk * 16));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
       }
     }
+  };
 
-    bf16x8 pf[QB][4];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qrow0 = tw0 + qb * 32;
-      const int tq = qrow0 + l32;
-      // ---- mask, row max (on raw scores: the scale is positive) --------
-      const bool need_mask = (key0 + kBC - 1 > qrow0) || (key0 + kBC > n);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int key = key0 + kb * 32 + (rr >> 3) * 16 + hh * 8 + ((rr >> 2) & 1) * 4 + (rr & 3);
-            if (key > tq || key >= n) sc[qb][kb][rr] = -INFINITY;
-          }
-        }
-      }
-      float mx = -INFINITY;
+  // softmax front half of tile j: mask (diagonal/tail tiles only), row max,
+  // lazy rescale of the running state; returns -m for the exp2 argument
+  auto softmax_front = [&](int j, f32x16 (&s)[2], bool may_mask) -> float {
+    const int key0 = j * kBC;
+    if (may_mask && ((key0 + kBC - 1 > tw0) || (key0 + kBC > n))) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, sc[qb][kb][rr]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
-
-      // ---- lazy rescale (see the header comment) ------------------------
-      const bool grow = mx > m_run[qb] + 8.0f;
-      if (__any(grow)) {
-        const float m_new = grow ? mx : m_run[qb];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);  // 0 when m_run = -inf
-        m_run[qb] = m_new;
-        l_part[qb] *= alpha;
-#pragma unroll
-        for (int i = 0; i < DBLK; ++i) o[qb][i] *= alpha;
-      }
-      const float neg_m = (m_run[qb] == -INFINITY) ? 0.f : -m_run[qb];
-
-      // ---- P^T in bf16, 4 k-steps of 16 keys ----------------------------
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[qb][ks >> 1][(ks & 1) * 8 + 2 * e], scale_log2, neg_m));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[qb][ks >> 1][(ks & 1) * 8 + 2 * e + 1], scale_log2, neg_m));
-          l_part[qb] += p0 + p1;
-          w[e] = pack_bf16x2(p0, p1);
+        for (int rr = 0; rr < 16; ++rr) {
+          const int key = key0 + kb * 32 + (rr >> 3) * 16 + hh * 8 + ((rr >> 2) & 1) * 4 + (rr & 3);
+          if (key > tq || key >= n) s[kb][rr] = -INFINITY;
         }
-        pf[qb][ks] = as_bf16x8(w);
       }
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;   // row max on raw scores (scale > 0)
+    const bool grow = mx > m_run + 8.0f;                 // lazy running max
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+      m_run = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
+    }
+    return (m_run == -INFINITY) ? 0.f : -m_run;
+  };
 
-    // ---- O^T += V^T P^T, each V^T fragment used QB times --------------------
+  // softmax back half: P = exp2(s*scale - m) in bf16, row sum
+  auto softmax_back = [&](f32x16 (&s)[2], float neg_m, bf16x8 (&pf)[4]) {
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-      const uint16_t *vrow = &sm.vt[buf][db * 32 + l32][hh * 8];
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 w;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 w = *reinterpret_cast<const u32x4 *>(vrow + ks * 16);
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][(ks & 1) * 8 + 2 * e], scale_log2, neg_m));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][(ks & 1) * 8 + 2 * e + 1], scale_log2, neg_m));
+        l_part += p0 + p1;
+        w[e] = pack_bf16x2(p0, p1);
+      }
+      pf[ks] = as_bf16x8(w);
+    }
+  };
+
+  // O^T += V^T P^T from V buffer j & 1 (k-step major: the MFMAs of k-step ks
+  // need only pf[ks], and consecutive MFMAs feed different accumulators)
+  auto pv = [&](int j, bf16x8 (&pf)[4]) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), pf[qb][ks], o[qb][db], 0, 0, 0);
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.vt[j & 1][db * 32 + l32][hh * 8 + ks * 16]);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), pf[ks], o[db], 0, 0, 0);
       }
     }
+  };
+
+  // One pipeline step j: stage K(j+2) and V(j+1) into the buffers freed by
+  // step j-1, start the loads of K(j+3) and V(j+2), then the score MFMAs of
+  // tile j+1 alongside the softmax of tile j, then the PV MFMAs of tile j.
+  const int last = (qend - 1) / kBC;
+  auto stage = [&](int j) {
+    __syncthreads();
+    if (j + 2 <= last) swrite_k(j & 1);
+    if (j + 1 <= last) swrite_v((j + 1) & 1);
+    if (j + 3 <= last) gload_k(j + 3);
+    if (j + 2 <= last) gload_v(j + 2);
+  };
+  // General step (diagonal and tail tiles, the last step): every check.
+  auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    stage(j);
+    if (j + 1 <= last && active(j + 1)) scores(j + 1, nxt);
+    if (active(j)) {
+      const float neg_m = softmax_front(j, cur, true);
+      bf16x8 pf[4];
+      softmax_back(cur, neg_m, pf);
+      pv(j, pf);
+    }
+  };
+  // Steady step: tiles j and j+1 lie wholly below every row of the workgroup
+  // (no mask, all waves active), so the score MFMAs of tile j+1, the exp /
+  // convert work of tile j and the PV MFMAs of tile j form one basic block,
+  // and the scheduler is told to interleave matrix and vector instructions.
+  auto step_steady = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    stage(j);
+    const float neg_m = softmax_front(j, cur, false);
+    scores(j + 1, nxt);
+    bf16x8 pf[4];
+    softmax_back(cur, neg_m, pf);
+    pv(j, pf);
+    // two operand reads ahead, then each MFMA followed by the next read and
+    // a share of the exp / convert work
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+#pragma unroll
+    for (int i = 0; i < 2 * KSTEPS + 4 * DBLK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+    }
+  };
+
+  // prologue: K(0), K(1), V(0) in LDS; K(2), V(1) in registers; S(0)
+  gload_k(0);
+  gload_v(0);
+  swrite_k(0);
+  swrite_v(0);
+  if (last >= 1) {
+    gload_k(1);
+    swrite_k(1);
+  }
+  if (last >= 2) gload_k(2);
+  if (last >= 1) gload_v(1);
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  if (active(0)) scores(0, sa);
+  // tiles below q0 (the workgroup's first row) need no mask for any wave
+  const int steady_end = q0 / kBC - 1;  // steps j with j + 1 < q0 / kBC
+  int j = 0;
+  for (; j + 1 < steady_end; j += 2) {
+    step_steady(j, sa, sb);
+    step_steady(j + 1, sb, sa);
+  }
+  for (; j <= last; j += 2) {
+    step(j, sa, sb);
+    if (j + 1 <= last) step(j + 1, sb, sa);
   }
 
   // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ---------------------
+  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  if (tq >= n) return;
+  const float inv = 1.f / l_tot;
+  const long long orow = ((s0 + tq) * Hq + h) * (long long)D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = l_part[qb] + __shfl_xor(l_part[qb], 32);
-    const int tq = tw0 + qb * 32 + l32;
-    if (tq >= n) continue;
-    const float inv = 1.f / l_tot;
-    const long long orow = ((s0 + tq) * Hq + h) * (long long)D;
+  for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d0 = db * 32 + jj * 8 + hh * 4;
-        const float y0 = o[qb][db][jj * 4 + 0] * inv, y1 = o[qb][db][jj * 4 + 1] * inv;
-        const float y2 = o[qb][db][jj * 4 + 2] * inv, y3 = o[qb][db][jj * 4 + 3] * inv;
-        if (OUT_F32) {
-          *reinterpret_cast<float4 *>((float *)out + orow + d0) = make_float4(y0, y1, y2, y3);
-        } else {
-          u32x2 pk;
-          pk[0] = pack_bf16x2(y0, y1);
-          pk[1] = pack_bf16x2(y2, y3);
-          *reinterpret_cast<u32x2 *>((uint16_t *)out + orow + d0) = pk;
-        }
+    for (int jj = 0; jj < 4; ++jj) {
+      const int d0 = db * 32 + jj * 8 + hh * 4;
+      const float y0 = o[db][jj * 4 + 0] * inv, y1 = o[db][jj * 4 + 1] * inv;
+      const float y2 = o[db][jj * 4 + 2] * inv, y3 = o[db][jj * 4 + 3] * inv;
+      if (OUT_F32) {
+        *reinterpret_cast<float4 *>((float *)out + orow + d0) = make_float4(y0, y1, y2, y3);
+      } else {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(y0, y1);
+        pk[1] = pack_bf16x2(y2, y3);
+        *reinterpret_cast<u32x2 *>((uint16_t *)out + orow + d0) = pk;
       }
     }
-    if (lse != nullptr && hh == 0)
-      lse[(long long)h * T + s0 + tq] = (m_run[qb] + __log2f(l_tot)) * kLn2;
   }
+  if (lse != nullptr && hh == 0) lse[(long long)h * T + s0 + tq] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
-template <int D, bool OUT_F32, bool ROT, int QB>
+template <int D, bool OUT_F32, bool ROT>
 hipError_t launch_one(const PrefillArgs &a, hipStream_t s) {
-  constexpr int BQ = 128 * QB;
-  const int ntiles = (a.max_seqlen + BQ - 1) / BQ;
+  const int ntiles = (a.max_seqlen + kBQ - 1) / kBQ;
   const long long blocks = (long long)ntiles * a.B * a.Hq;
   const float scale_log2 = (float)((double)a.softmax_scale * 1.4426950408889634074);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_F32, ROT, QB>), dim3((unsigned)blocks),
-                     dim3(kThreads), 0, s, (const uint16_t *)a.q, (const uint16_t *)a.k,
-                     (const uint16_t *)a.v, a.cu_seqlens, a.B, a.max_seqlen, a.T, a.Hq, a.Hkv,
-                     a.theta, scale_log2, a.out, a.lse, ntiles, a.dev_flag);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_F32, ROT>), dim3((unsigned)blocks), dim3(kThreads),
+                     0, s, (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
+                     a.cu_seqlens, a.B, a.max_seqlen, a.T, a.Hq, a.Hkv, a.theta, scale_log2, a.out,
+                     a.lse, ntiles, a.dev_flag);
   return hipGetLastError();
 }
 
-template <int D, int QB>
-hipError_t launch_q(const PrefillArgs &a, hipStream_t s) {
+template <int D>
+hipError_t launch_d(const PrefillArgs &a, hipStream_t s) {
   const bool f32 = a.out_dtype == YR_F32;
   const bool rot = a.theta != nullptr;
-  if (f32) return rot ? launch_one<D, true, true, QB>(a, s) : launch_one<D, true, false, QB>(a, s);
-  return rot ? launch_one<D, false, true, QB>(a, s) : launch_one<D, false, false, QB>(a, s);
+  if (f32) return rot ? launch_one<D, true, true>(a, s) : launch_one<D, true, false>(a, s);
+  return rot ? launch_one<D, false, true>(a, s) : launch_one<D, false, false>(a, s);
 }
 
 }  // namespace
 
-// Rows per wave.  64 (QB = 2) halves LDS traffic per FLOP but leaves one
-// wave per SIMD; measured on MI355X it is slower than two 32-row waves per
-// SIMD, which hide each other's LDS and exp latency, so 32 is used.
-int prefill_rows_per_wave(int B, int max_seqlen, int Hq) {
-  (void)B;
-  (void)max_seqlen;
-  (void)Hq;
-  return 32;
-}
-
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s) {
-  const bool wide = prefill_rows_per_wave(a.B, a.max_seqlen, a.Hq) == 64;
-  if (a.head_dim == 64) return wide ? launch_q<64, 2>(a, s) : launch_q<64, 1>(a, s);
-  return wide ? launch_q<128, 2>(a, s) : launch_q<128, 1>(a, s);
+  return a.head_dim == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
 }
 
 }  // namespace yr

@@ -77,8 +77,6 @@ struct DecodeArgs {
 hipError_t launch_rope(const RopeArgs &a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s);
-// Query rows per wave the bf16 prefill kernel uses for these sizes (32 or 64).
-int prefill_rows_per_wave(int B, int max_seqlen, int Hq);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 
 // Decode split geometry: keys per chunk and number of chunks for a cache
