@@ -217,7 +217,7 @@ def bench_decode(args, torch, ops, wl):
            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                         "traffic": traffic_from_profiles("decode", cfg.name, digest),
-                        "kernel": "decode_split_kernel + decode_merge_kernel (one call)",
+                        "kernel": "decode_mfma_kernel + decode_merge_kernel (one call)",
                         "kernel_ms": round(call_ms, 4), "bytes_per_launch": int(nbytes)},
            "source_digest": digest}
     state = {"seqlens": inp["seqlens"], "q": q, "kc": kc, "vc": vc}

@@ -196,7 +196,11 @@ size_t attn_decode_workspace_bytes(int B, int max_cache_len, int Hq, int head_di
  *   lse             device float[B, Hq] or NULL
  *   workspace       device, >= attn_decode_workspace_bytes(...) bytes,
  *                   256-byte aligned; holds the partials
- *   head_dim        64 or 128;  Hq % Hkv == 0;  Hq / Hkv <= 16
+ *   head_dim        64 or 128;  Hq % Hkv == 0;  Hq / Hkv <= 32 for YR_BF16
+ *                   inputs, <= 16 for YR_F32 inputs
+ * Returns YR_ERR_UNSUPPORTED beyond those limits, YR_ERR_WORKSPACE for a
+ * short or misaligned workspace, YR_ERR_INVALID for bad sizes; range errors
+ * in seqlens / q_pos are reported through the device error word.
  */
 int attn_decode(const void *q, const void *k_cache, const void *v_cache,
                 int in_dtype, const int *seqlens, const int *q_pos, int B,

@@ -145,7 +145,8 @@ def decode_call(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(D=80), ops.YR_ERR_UNSUPPORTED),
     (dict(Hq=8, Hkv=3), ops.YR_ERR_INVALID),
-    (dict(Hq=64, Hkv=2), ops.YR_ERR_UNSUPPORTED),
+    (dict(Hq=128, Hkv=2), ops.YR_ERR_UNSUPPORTED),                    # bf16: g <= 32
+    (dict(Hq=64, Hkv=2, in_dtype=ops.YR_F32, out_dtype=ops.YR_F32), ops.YR_ERR_UNSUPPORTED),  # fp32: g <= 16
     (dict(B=0), ops.YR_ERR_INVALID),
     (dict(Lmax=0), ops.YR_ERR_INVALID),
     (dict(scale=-1.0), ops.YR_ERR_INVALID),

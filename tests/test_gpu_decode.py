@@ -44,6 +44,9 @@ def _cfg(dtype, hq, hkv, D):
     ("bf16", 3, 5000, 1000, 32, 8, 128, ops.YR_F32),
     ("bf16", 4, 2100, 1, 4, 4, 64, ops.YR_BF16),
     ("bf16", 2, 700, 600, 16, 2, 128, ops.YR_BF16),
+    ("bf16", 6, 70, 1, 16, 1, 64, ops.YR_F32),
+    ("bf16", 3, 1100, 1, 2, 2, 128, ops.YR_F32),
+    ("bf16", 2, 4500, 2000, 32, 1, 128, ops.YR_BF16),
     ("f32", 4, 3000, 1, 8, 2, 128, ops.YR_F32),
     ("f32", 3, 257, 1, 4, 1, 64, ops.YR_F32),
 ])

@@ -219,7 +219,9 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, int in_
   if (!dims_ok(head_dim)) return fail(YR_ERR_UNSUPPORTED, "attn_decode: head_dim must be 64 or 128");
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
     return fail(YR_ERR_INVALID, "attn_decode: need Hq >= 1, Hkv >= 1, Hq % Hkv == 0");
-  if (Hq / Hkv > 16) return fail(YR_ERR_UNSUPPORTED, "attn_decode: at most 16 query heads per KV head");
+  if (Hq / Hkv > (in_dtype == YR_BF16 ? 32 : 16))
+    return fail(YR_ERR_UNSUPPORTED,
+                "attn_decode: at most 32 (bf16) or 16 (fp32) query heads per KV head");
   if (B < 1 || max_cache_len < 1) return fail(YR_ERR_INVALID, "attn_decode: need B >= 1, max_cache_len >= 1");
   if ((long long)B * max_cache_len > (1LL << 34))
     return fail(YR_ERR_INVALID, "attn_decode: cache too large");

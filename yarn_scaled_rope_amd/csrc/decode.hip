@@ -20,6 +20,8 @@
 #include "device_common.h"
 #include "yr_internal.h"
 
+#include <type_traits>
+
 namespace yr {
 namespace {
 
@@ -27,6 +29,8 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 8;  // keys per lane group per iteration (loads in flight)
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kMfmaWaves = 4;   // waves per workgroup, bf16 kernel
+constexpr int kMfmaStages = 1;  // LDS stages per wave, bf16 kernel (two workgroups fit a CU)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -119,18 +123,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   __shared__ float sm_l[kWaves][GM];
   __shared__ float sm_acc[kWaves][GM][D];
 
-  if (flag != nullptr && blockIdx.x == 0) {
-    __shared__ int bad;
-    if (threadIdx.x == 0) bad = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < B; i += kThreads) {
-      const int L = seqlens[i];
-      if (L < 1 || L > Lmax) atomicOr(&bad, YR_DEVERR_SEQLENS);
-      if (qpos != nullptr && qpos[i] < 0) atomicOr(&bad, YR_DEVERR_QPOS);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) *flag = bad;
-  }
+  if (flag != nullptr && blockIdx.x == 0) validate_decode_lens(seqlens, qpos, B, Lmax, flag);
 
   const int split = blockIdx.x % nsplit;
   const int rest = blockIdx.x / nsplit;
@@ -304,20 +297,393 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   }
 }
 
+// ---- bf16 inputs: matrix-core split kernel ----------------------------------
+// Per 32-key block a wave computes S^T = K Q^T (keys x query heads of the
+// group, v_mfma_f32_32x32x16_bf16 with the group's heads as the 32 columns)
+// and O^T += V^T P^T.  K and V blocks go straight from HBM into a ring of LDS
+// stages private to the wave (buffer_load ... lds: no staging registers, no
+// workgroup barriers in the sweep); the wave waits on exact vmcnt counts, so
+// the next blocks stream in while the current one is computed.
+//   K stage: row r holds key r; its 16-byte chunk c sits at slot c ^ (r & (CH-1)),
+//     so the A-operand reads (32 rows, one chunk each) hit distinct banks.
+//   V stage: row r holds key r; chunk c sits at slot c ^ vswz(r & 3).  The
+//     V^T operand comes from ds_read_b64_tr_b16: within 16 lanes, lane t reads
+//     4 elements of key row t>>2 and receives column t of 4 consecutive key
+//     rows.  Keys 4..7 of a k-step half sit in the other lane half, matching
+//     the order in which the score accumulator holds P (slot 4j+i of lane half
+//     h is key 8j + 4h + i).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#define YR_LDS __attribute__((address_space(3)))
+
+constexpr int kBlk = 32;  // keys per block (the MFMA row count)
+
+// V chunk swizzle by key row mod 4: bits 1-2 distinct (conflict-free for 16
+// lanes on 32 banks) and, with 16 chunks per row, bits 2-3 distinct too
+// (conflict-free for 32 lanes on 64 banks).
+template <int CH>
+__device__ __forceinline__ int vswz(int e) {
+  return CH >= 16 ? ((2 * e) ^ (8 * (e & 1))) : 2 * e;
+}
+
+template <int D, int W, int NB>
+struct MfmaSmem {
+  union {
+    uint16_t ring[W][NB][2][kBlk * D];  // [wave][stage][K|V][row * D + swizzled chunk]
+    struct {
+      float o[W][D][33];
+      float m[W][32];
+      float l[W][32];
+    } comb;
+  } u;
+  uint16_t qt[32][D + 8];  // rotated query heads of the group (bf16), one per row
+  float cs[D / 2], sn[D / 2];
+};
+
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+template <int H, int MAXHALVES>
+__device__ __forceinline__ void wait_halves(int halves) {
+  // halves is wave-uniform: a scalar branch picks the immediate
+  if (MAXHALVES >= 7 && halves >= 7) { wait_vm<7 * H>(); return; }
+  if (MAXHALVES >= 6 && halves == 6) { wait_vm<6 * H>(); return; }
+  if (MAXHALVES >= 5 && halves == 5) { wait_vm<5 * H>(); return; }
+  if (MAXHALVES >= 4 && halves == 4) { wait_vm<4 * H>(); return; }
+  if (MAXHALVES >= 3 && halves == 3) { wait_vm<3 * H>(); return; }
+  if (halves == 2) { wait_vm<2 * H>(); return; }
+  if (halves == 1) { wait_vm<H>(); return; }
+  wait_vm<0>();
+}
+// every LDS read issued so far has returned (before a DMA overwrites a stage)
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// LDS byte address of a shared-memory pointer
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const YR_LDS void *)p;
+}
+
+// The V^T operands of one k-step: for each 32-row block db, two transposing
+// reads (key rows +0 and +ROWSTEP bytes).  The reads and the wait for them
+// sit in one asm block, so no destination register is live in flight outside
+// it.  (Written as a builtin, each such read makes the compiler wait for every
+// outstanding LDS DMA of the wave, which would drain the prefetch.)
+template <int DBLK, int OFF, int ROWSTEP>
+__device__ __forceinline__ void tr_reads(u32x2 (&r)[DBLK][2], const uint32_t (&a)[DBLK]) {
+  static_assert(DBLK == 2 || DBLK == 4, "head_dim 64 or 128");
+  if constexpr (DBLK == 4) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(r[2][0]),
+          "=&v"(r[2][1]), "=&v"(r[3][0]), "=&v"(r[3][1])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF), "i"(OFF + ROWSTEP)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+        "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[1][0]), "=&v"(r[1][1])
+        : "v"(a[0]), "v"(a[1]), "i"(OFF), "i"(OFF + ROWSTEP)
+        : "memory");
+  }
+}
+
+template <int D, int W, int NB>
+__global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
+    const uint16_t *__restrict__ vc, const int *__restrict__ seqlens,
+    const int *__restrict__ qpos, int B, int Lmax, int Hq, int Hkv,
+    const double *__restrict__ theta, float scale_log2, int chunk, int nsplit,
+    float *__restrict__ part_o, float *__restrict__ part_lse, int *flag) {
+  constexpr int CH = D / 8;        // 16-byte chunks per row
+  constexpr int H = D / 16;        // DMA instructions per K or V block (1 KB each)
+  constexpr int RPI = 64 / CH;     // rows per DMA instruction
+  constexpr int KSTEPS = D / 16;   // score k-steps over the head dim
+  constexpr int DBLK = D / 32;     // 32-row blocks of O^T
+  constexpr int NT = W * 64;
+  static_assert((2 * NB - 1) * H < 64, "vmcnt range");
+
+  __shared__ __align__(16) MfmaSmem<D, W, NB> sm;
+
+  if (flag != nullptr && blockIdx.x == 0) validate_decode_lens(seqlens, qpos, B, Lmax, flag);
+
+  const int split = blockIdx.x % nsplit;
+  const int rest = blockIdx.x / nsplit;
+  const int hk = rest % Hkv;
+  const int b = rest / Hkv;
+  const int g = Hq / Hkv;
+  int L = seqlens[b];
+  L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+  const int c0 = split * chunk;
+  if (c0 >= L) return;
+  const int n = min(L, c0 + chunk) - c0;  // keys of this chunk
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const long long rstride = (long long)Hkv * D;  // elements between keys
+  const uint16_t *kbase = kc + (((long long)b * Lmax + c0) * Hkv + hk) * D;
+  const uint16_t *vbase = vc + (((long long)b * Lmax + c0) * Hkv + hk) * D;
+  const int nblk = (n + kBlk - 1) / kBlk;
+  const int nmine = nblk > wave ? (nblk - wave + W - 1) / W : 0;  // blocks of this wave
+
+  // DMA lane mapping: instruction p of a block fills LDS bytes [1024p, 1024p+1024)
+  // in lane order; lane l lands on row p*RPI + l/CH, slot l%CH, so it fetches
+  // the source chunk that belongs in that slot.
+  const int drow = lane / CH, dslot = lane % CH;
+  const uint32_t voff_v =
+      (uint32_t)((drow * rstride + 8 * (dslot ^ vswz<CH>(drow & 3))) * 2);
+  uint32_t voff_k[H];
+#pragma unroll
+  for (int p = 0; p < H; ++p) {
+    const int r = p * RPI + drow;
+    voff_k[p] = (uint32_t)((r * rstride + 8 * (dslot ^ (r & (CH - 1)))) * 2);
+  }
+  const uint32_t pstride = (uint32_t)(RPI * rstride * 2);
+
+  // t-th block of this wave -> stage; keys past the chunk read 0
+  auto issue = [&](int t, int stage, int which) {
+    const int key0 = (wave + t * W) * kBlk;
+    const int rows = min(kBlk, n - key0);
+    const uint32_t bytes = (uint32_t)(((rows - 1) * rstride + D) * 2);
+    const uint16_t *src = (which == 0 ? kbase : vbase) + key0 * rstride;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, bytes);
+    uint16_t *dst = sm.u.ring[wave][stage][which];
+#pragma unroll
+    for (int p = 0; p < H; ++p) {
+      const uint32_t vo = which == 0 ? voff_k[p] : voff_v + p * pstride;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (YR_LDS void *)(dst + p * 512), 16, (int)vo, 0,
+                                               0, 2 /* non-temporal */);
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < NB; ++s)
+    if (s < nmine) {
+      issue(s, s, 0);
+      issue(s, s, 1);
+    }
+
+  // ---- query heads of the group: rotate at the new token's position, round
+  // to bf16, one head per row of qt (rows past the group stay zero)
+  {
+    int m = qpos != nullptr ? qpos[b] : L;
+    m = m < 0 ? 0 : m;
+    for (int i = tid; i < D / 2; i += NT) {
+      float c = 1.f, s = 0.f;
+      if (theta != nullptr) rope_cos_sin((double)m, theta[i], &c, &s);
+      sm.cs[i] = c;
+      sm.sn[i] = s;
+    }
+    __syncthreads();
+    const int gc = min(g, 32);
+    for (int idx = tid; idx < 32 * (D / 2); idx += NT) {
+      const int col = idx / (D / 2), pr = idx % (D / 2);
+      float x0 = 0.f, x1 = 0.f;
+      if (col < gc) {
+        const uint16_t *qp = q + ((long long)b * Hq + hk * g + col) * D + 2 * pr;
+        x0 = bf16_to_f32(qp[0]);
+        x1 = bf16_to_f32(qp[1]);
+        rotate_pair(x0, x1, sm.cs[pr], sm.sn[pr]);
+      }
+      *reinterpret_cast<uint32_t *>(&sm.qt[col][2 * pr]) = pack_bf16x2(x0, x1);
+    }
+    __syncthreads();
+  }
+  bf16x8 qf[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk)
+    qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&sm.qt[l32][16 * kk + 8 * hh]));
+
+  f32x16 o[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  float mrun = -INFINITY;  // running max of the column, log2 units
+  float lsum = 0.f;        // this lane's share of the column's sum
+
+  // LDS read offsets (elements) within a stage
+  const int kx = l32 & (CH - 1);
+  // V^T operand addresses (LDS bytes, stage 0 of this wave; the stage, k-step
+  // and row-half offsets are immediates).  Lane t of a 16-lane group points at
+  // 4 elements of key row 4*hh + (t >> 2) (+16 ks + 8 r), column block 4*db +
+  // its chunk within the 16 columns of the group.
+  constexpr int kStageBytes = 2 * kBlk * D * 2;
+  uint32_t vaddr[DBLK];
+  {
+    const int t16 = lane & 15;
+    const int vrow = 4 * hh + (t16 >> 2);
+    const int vx = vswz<CH>(t16 >> 2);
+    const int vcol = 2 * ((lane >> 4) & 1) + ((t16 & 3) >> 1);
+    const uint32_t ring0 = lds_addr(sm.u.ring[wave][0][0]);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+      vaddr[db] = ring0 + (uint32_t)((vrow * D + 8 * ((4 * db + vcol) ^ vx) + 4 * (t16 & 1)) * 2);
+  }
+
+  auto block = [&](int t, auto stage_c) {
+    constexpr int S = decltype(stage_c)::value;
+    const int key0 = (wave + t * W) * kBlk;
+    const int ahead = min(NB - 1, nmine - 1 - t);  // later blocks already issued
+    const bool refill = t + NB < nmine;
+
+    wait_halves<H, 2 * NB - 1>(1 + 2 * ahead);  // K of block t has landed
+    const uint16_t *ks_ = sm.u.ring[wave][S][0];
+    f32x16 sc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sc[e] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const u32x4 a = *reinterpret_cast<const u32x4 *>(ks_ + l32 * D + 8 * ((2 * kk + hh) ^ kx));
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[kk], sc, 0, 0, 0);
+    }
+    if (refill) {
+      wait_lds();
+      issue(t + NB, S, 0);
+    }
+
+    // online softmax of the column (query head) l32 over this block
+    if (key0 + kBlk > n) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = key0 + 8 * (e >> 2) + 4 * hh + (e & 3);
+        sc[e] = key < n ? sc[e] : -INFINITY;
+      }
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(mrun, mx * scale_log2);
+    // lazy rescale: keep the reference max until some column's max has grown
+    // by more than 2^8 (p stays <= 256, exact in fp32 sums, fine in bf16)
+    if (__builtin_amdgcn_ballot_w64(mnew > mrun + 8.f) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+      mrun = mnew;
+    }
+    float p[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], scale_log2, -mrun));
+      lsum += p[e];
+    }
+    bf16x8 pf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[8 * ks + 2 * e], p[8 * ks + 2 * e + 1]);
+      pf[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+
+    wait_halves<H, 2 * NB - 1>(2 * ahead + (refill ? 1 : 0));  // V of block t has landed
+    auto pv_step = [&](auto ks_c) {
+      constexpr int KS = decltype(ks_c)::value;
+      u32x2 h2[DBLK][2];
+      tr_reads<DBLK, S * kStageBytes + kBlk * D * 2 + KS * 16 * D * 2, 8 * D * 2>(h2, vaddr);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const u32x4 a = {h2[db][0][0], h2[db][0][1], h2[db][1][0], h2[db][1][1]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[KS],
+                                                        o[db], 0, 0, 0);
+      }
+    };
+    pv_step(std::integral_constant<int, 0>{});
+    pv_step(std::integral_constant<int, 1>{});
+    if (refill) {
+      wait_lds();
+      issue(t + NB, S, 1);
+    }
+  };
+
+  for (int t = 0; t < nmine; t += NB) {
+    block(t, std::integral_constant<int, 0>{});
+    if (NB > 1 && t + 1 < nmine) block(t + 1, std::integral_constant<int, (NB > 1 ? 1 : 0)>{});
+    if (NB > 2 && t + 2 < nmine) block(t + 2, std::integral_constant<int, (NB > 2 ? 2 : 0)>{});
+    if (NB > 3 && t + 3 < nmine) block(t + 3, std::integral_constant<int, (NB > 3 ? 3 : 0)>{});
+  }
+
+  // ---- combine: the two lane halves of a column hold disjoint keys; then
+  // the waves, through LDS (the ring is free once every wave is here)
+  lsum += __shfl_xor(lsum, 32);
+  __syncthreads();
+  const int gc = min(g, 32);
+  if (l32 < gc) {
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        sm.u.comb.o[wave][32 * db + 8 * (e >> 2) + 4 * hh + (e & 3)][l32] = o[db][e];
+    if (hh == 0) {
+      sm.u.comb.m[wave][l32] = mrun;
+      sm.u.comb.l[wave][l32] = lsum;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < gc * D; idx += NT) {
+    const int gi = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, sm.u.comb.m[w][gi]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float mw = sm.u.comb.m[w][gi];
+      const float s = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      num += s * sm.u.comb.o[w][d][gi];
+      den += s * sm.u.comb.l[w][gi];
+    }
+    const long long row = ((long long)b * Hq + hk * g + gi) * nsplit + split;
+    part_o[row * D + d] = num / den;
+    if (d == 0) part_lse[row] = M + __log2f(den);
+  }
+}
+
 template <int D, bool OUT_F32>
-__global__ __launch_bounds__(64) void decode_merge_kernel(
+__global__ __launch_bounds__(256) void decode_merge_kernel(
     const float *__restrict__ part_o, const float *__restrict__ part_lse,
     const int *__restrict__ seqlens, int Hq, int Lmax, int chunk, int nsplit,
     void *__restrict__ out, float *__restrict__ lse) {
-  constexpr int PER = D / 64;
+  constexpr int PER = D / 64;  // output elements per lane
+  constexpr int MW = 4;        // waves; wave w takes partials w, w+4, ...
+  constexpr int U = 4;         // partials per wave in flight
+  __shared__ float sm_num[MW][D];
+  __shared__ float sm_den[MW];
   const int b = blockIdx.x / Hq;
   const int h = blockIdx.x % Hq;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   int L = seqlens[b];
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
   const int nv = (L + chunk - 1) / chunk;
   const long long row0 = ((long long)b * Hq + h) * nsplit;
 
+  // common reference: the largest partial log2-sum-exp (every wave computes it)
   float M = -INFINITY;
   for (int p = lane; p < nv; p += 64) M = fmaxf(M, part_lse[row0 + p]);
 #pragma unroll
@@ -326,16 +692,44 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   float num[PER], den = 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) num[i] = 0.f;
-  for (int p = 0; p < nv; ++p) {
-    const float w = __builtin_amdgcn_exp2f(part_lse[row0 + p] - M);
-    den += w;
+  int p = wave;
+  for (; p + (U - 1) * MW < nv; p += U * MW) {
+    float w[U], x[U][PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) num[i] += w * part_o[(row0 + p) * D + lane + 64 * i];
+    for (int u = 0; u < U; ++u) {
+      w[u] = part_lse[row0 + p + u * MW];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) x[u][i] = part_o[(row0 + p + u * MW) * D + lane + 64 * i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float e = __builtin_amdgcn_exp2f(w[u] - M);
+      den += e;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) num[i] = fmaf(e, x[u][i], num[i]);
+    }
   }
+  for (; p < nv; p += MW) {
+    const float e = __builtin_amdgcn_exp2f(part_lse[row0 + p] - M);
+    den += e;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) num[i] = fmaf(e, part_o[(row0 + p) * D + lane + 64 * i], num[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) sm_num[wave][lane + 64 * i] = num[i];
+  if (lane == 0) sm_den[wave] = den;
+  __syncthreads();
+  if (wave != 0) return;
+  den = 0.f;
+#pragma unroll
+  for (int w = 0; w < MW; ++w) den += sm_den[w];
   const long long orow = ((long long)b * Hq + h) * D;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const float y = nv > 0 ? num[i] / den : 0.f;
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < MW; ++w) t += sm_num[w][lane + 64 * i];
+    const float y = nv > 0 ? t / den : 0.f;
     if (OUT_F32)
       ((float *)out)[orow + lane + 64 * i] = y;
     else
@@ -367,8 +761,21 @@ hipError_t launch_split_g(const DecodeArgs &a, hipStream_t s) {
 }
 
 template <int D>
+hipError_t launch_mfma(const DecodeArgs &a, hipStream_t s) {
+  constexpr int W = kMfmaWaves, NB = kMfmaStages;
+  const long long blocks = (long long)a.B * a.Hkv * a.nsplit;
+  const float scale_log2 = (float)((double)a.softmax_scale * 1.4426950408889634074);
+  hipLaunchKernelGGL((decode_mfma_kernel<D, W, NB>), dim3((unsigned)blocks), dim3(W * 64), 0, s,
+                     (const uint16_t *)a.q, (const uint16_t *)a.k_cache,
+                     (const uint16_t *)a.v_cache, a.seqlens, a.q_pos, a.B, a.max_cache_len, a.Hq,
+                     a.Hkv, a.theta, scale_log2, a.chunk, a.nsplit, a.part_o, a.part_lse,
+                     a.dev_flag);
+  return hipGetLastError();
+}
+
+template <int D>
 hipError_t launch_merge(const DecodeArgs &a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.B * a.Hq)), block(64);
+  const dim3 grid((unsigned)(a.B * a.Hq)), block(256);
   if (a.out_dtype == YR_F32)
     hipLaunchKernelGGL((decode_merge_kernel<D, true>), grid, block, 0, s, a.part_o, a.part_lse,
                        a.seqlens, a.Hq, a.max_cache_len, a.chunk, a.nsplit, a.out, a.lse);
@@ -381,9 +788,11 @@ hipError_t launch_merge(const DecodeArgs &a, hipStream_t s) {
 }  // namespace
 
 int decode_chunk(int B, int max_cache_len, int Hkv) {
-  // Enough workgroups to fill 256 CUs several times over, with chunks a
-  // multiple of the 64 keys a workgroup covers per iteration.
-  int chunk = 1024;
+  // Enough workgroups to fill 256 CUs several times over; chunks are powers
+  // of two, at most 2048 keys (1 MiB of K and V at 128 bf16 elements per key
+  // and 8 KV heads) so that a workgroup's start-up and combine stay small
+  // next to its sweep.
+  int chunk = 2048;
   while (chunk > 64 && (long long)B * Hkv * decode_nsplit(max_cache_len, chunk) < 2048) chunk >>= 1;
   return chunk;
 }
@@ -391,7 +800,7 @@ int decode_chunk(int B, int max_cache_len, int Hkv) {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   hipError_t e;
   if (a.in_dtype == YR_BF16)
-    e = a.head_dim == 64 ? launch_split_g<uint16_t, 64>(a, s) : launch_split_g<uint16_t, 128>(a, s);
+    e = a.head_dim == 64 ? launch_mfma<64>(a, s) : launch_mfma<128>(a, s);
   else
     e = a.head_dim == 64 ? launch_split_g<float, 64>(a, s) : launch_split_g<float, 128>(a, s);
   if (e != hipSuccess) return e;

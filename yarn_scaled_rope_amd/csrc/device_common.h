@@ -100,4 +100,37 @@ __device__ inline void validate_cu_seqlens(const int *__restrict__ cu, int B, lo
   if (threadIdx.x == 0) *flag = bad;
 }
 
+// Buffer resource word 3 for a raw 32-bit buffer with range checking: a load
+// at or past the descriptor's byte count returns zero.
+constexpr uint32_t kRsrcWord3 = 0x00020000;
+
+// Buffer descriptor over [base, base + bytes).  Callers pass wave-uniform
+// values; readfirstlane puts them in scalar registers, where the descriptor
+// must live (otherwise the compiler wraps every load in a waterfall loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void *p = (void *)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           (int)kRsrcWord3);
+}
+
+// Check decode seqlens / q_pos (one workgroup, all threads call it; thread 0
+// writes the error word).
+__device__ inline void validate_decode_lens(const int *__restrict__ seqlens,
+                                            const int *__restrict__ qpos, int B, int Lmax,
+                                            int *flag) {
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < B; i += blockDim.x) {
+    const int L = seqlens[i];
+    if (L < 1 || L > Lmax) atomicOr(&bad, YR_DEVERR_SEQLENS);
+    if (qpos != nullptr && qpos[i] < 0) atomicOr(&bad, YR_DEVERR_QPOS);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = bad;
+}
+
 }  // namespace yr

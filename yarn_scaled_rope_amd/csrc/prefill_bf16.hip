@@ -54,7 +54,6 @@ constexpr int kKPad = 8;   // bf16 elements of padding per K row   (row = 68 dwo
 constexpr int kVPad = 8;   // bf16 elements of padding per V^T row (row = 36 dwords)
 constexpr int kXcds = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr uint32_t kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, range-checked
 
 template <int D>
 struct Smem {
@@ -72,18 +71,6 @@ __device__ __forceinline__ int kperm(int r) { return (r & ~12) | ((r & 4) << 1) 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
 __device__ __forceinline__ uint32_t sel16(uint32_t w, int hi) { return hi ? (w >> 16) : (w & 0xffffu); }
-
-// Buffer descriptor over [base, base + bytes).  Callers pass wave-uniform
-// values; readfirstlane puts them in scalar registers, where the descriptor
-// must live (otherwise the compiler wraps every load in a waterfall loop).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)base;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  void *p = (void *)(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
-                                           (int)kRsrcWord3);
-}
 
 template <int D, bool OUT_F32, bool ROTATE_Q>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
