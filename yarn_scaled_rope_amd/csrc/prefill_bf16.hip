@@ -39,6 +39,8 @@
 #include "device_common.h"
 #include "yr_internal.h"
 
+#include <type_traits>
+
 namespace yr {
 namespace {
 
@@ -46,31 +48,28 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define YR_LDS __attribute__((address_space(3)))
 
 constexpr int kThreads = 256;
 constexpr int kBQ = 128;   // query rows per workgroup (4 waves x 32)
 constexpr int kBC = 64;    // keys per tile
-constexpr int kKPad = 8;   // bf16 elements of padding per K row   (row = 68 dwords)
-constexpr int kVPad = 8;   // bf16 elements of padding per V^T row (row = 36 dwords)
 constexpr int kXcds = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
 
-template <int D>
-struct Smem {
-  uint16_t k[2][kBC][D + kKPad];
-  uint16_t vt[2][D][kBC + kVPad];
-};
-
-// LDS row r of a K tile holds key kperm(r): bits 2 and 3 of the row index
-// swapped within each 16.  The score accumulator slot 8j + 4h + i (lane half
-// h) then belongs to key 16(j >> 1) + 8h + 4(j & 1) + i, so the 8 accumulator
-// registers that form one 16-key k-step of P hold 8 CONSECUTIVE keys per lane
-// half, and the matching V^T operand is a single 16-byte LDS read.
-__device__ __forceinline__ int kperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+// V chunk swizzle by key row mod 4: for 16 lanes of a transposing read (4 key
+// rows x 2 chunks) the 8 slots are distinct mod 8 (32 banks) and, with 16
+// chunks per row, the 32 lanes of both 16-column halves are distinct mod 16
+// (64 banks).
+template <int CH>
+__device__ __forceinline__ int vswz(int e) {
+  return CH >= 16 ? ((2 * e) ^ (8 * (e & 1))) : 2 * e;
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-__device__ __forceinline__ uint32_t sel16(uint32_t w, int hi) { return hi ? (w >> 16) : (w & 0xffffu); }
+// s_waitcnt vmcnt(0) only: this wave's tile copies into LDS have landed
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int D, bool OUT_F32, bool ROTATE_Q>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
@@ -78,15 +77,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const uint16_t *__restrict__ v, const int *__restrict__ cu, int B, int max_seqlen,
     long long T, int Hq, int Hkv, const double *__restrict__ theta, float scale_log2,
     void *__restrict__ out, float *__restrict__ lse, int ntiles, int *flag) {
-  constexpr int KSTEPS = D / 16;        // MFMA k-steps over the head dim
-  constexpr int DBLK = D / 32;          // 32-row blocks of O^T
-  constexpr int CH = D / 8;             // 16-byte chunks per row
-  constexpr int KROWS = kThreads / CH;  // K rows per load pass
-  constexpr int KPASS = kBC / KROWS;
-  constexpr int VUNITS = CH * (kBC / 4);  // (4-key group, chunk) units of a V tile
-  static_assert(VUNITS <= kThreads, "V tile mapping");
+  constexpr int KSTEPS = D / 16;     // MFMA k-steps over the head dim
+  constexpr int DBLK = D / 32;       // 32-row blocks of O^T
+  constexpr int CH = D / 8;          // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;       // rows per 1 KB tile copy instruction
+  constexpr int DPW = kBC / RPI / 4; // copy instructions per wave per tile
+  constexpr int TILE = kBC * D;      // elements of a K or V tile
 
-  __shared__ __align__(16) Smem<D> sm;
+  // one array per stage: the compiler then tells a stage being read from the
+  // copies in flight into the other stage, and adds no wait for them
+  __shared__ __align__(16) uint16_t sk0[TILE], sk1[TILE], sv0[TILE], sv1[TILE];
 
   if (flag != nullptr && blockIdx.x == 0) validate_cu_seqlens(cu, B, T, max_seqlen, flag);
 
@@ -112,11 +112,54 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int tw0 = q0 + wave * 32;  // first query row of this wave
   const int tq = tw0 + l32;        // this lane's query row
+
+  // ---- tile copies HBM -> LDS (buffer_load ... lds, no registers) ---------
+  // Copy instruction p of a tile fills LDS bytes [1024p, 1024p + 1024) in lane
+  // order: lane l lands on row p*RPI + l/CH, slot l%CH, so it fetches the
+  // source chunk that belongs in that slot.  K: slot = chunk ^ (row % CH);
+  // V: slot = chunk ^ vswz(row % 4).  Rows past the sequence end read 0.
+  const long long rstride = (long long)Hkv * D;  // elements between key rows
+  const uint16_t *kseq = k + (s0 * Hkv + hk) * (long long)D;
+  const uint16_t *vseq = v + (s0 * Hkv + hk) * (long long)D;
+  const uint32_t rbytes = (uint32_t)(rstride * 2);
+  const int drow = lane / CH, dslot = lane % CH;
+  uint32_t koff[DPW];
+#pragma unroll
+  for (int i = 0; i < DPW; ++i) {
+    const int row = (wave * DPW + i) * RPI + drow;
+    koff[i] = drow * rbytes + 16 * (dslot ^ (row & (CH - 1)));
+  }
+  const uint32_t voff = drow * rbytes + 16 * (dslot ^ vswz<CH>(drow & 3));
+  auto copy_tile = [&](uint16_t *dst, const uint16_t *seq, int t, bool is_v) {
+    const int key0 = t * kBC;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(seq + key0 * rstride, (uint32_t)min(kBC, n - key0) * rbytes);
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+      const int p = wave * DPW + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (YR_LDS void *)(dst + p * 512), 16,
+                                               (int)(is_v ? voff : koff[i]),
+                                               (int)(p * RPI * rbytes), 0, 0);
+    }
+  };
+  auto kst = [&](auto par) -> uint16_t * {
+    if constexpr (decltype(par)::value == 0) return sk0; else return sk1;
+  };
+  auto vst = [&](auto par) -> uint16_t * {
+    if constexpr (decltype(par)::value == 0) return sv0; else return sv1;
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  const int last = (qend - 1) / kBC;
+  // prologue copies go out before the query work so that they are in flight
+  copy_tile(sk0, kseq, 0, false);
+  copy_tile(sv0, vseq, 0, true);
+  if (last >= 1) copy_tile(sk1, kseq, 1, false);
 
   // ---- Q fragments (B operand of S^T = K Q^T), rotated on load -----------
   bf16x8 qf[KSTEPS];
@@ -149,68 +192,38 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   float m_run = -INFINITY;
   float l_part = 0.f;
 
-  // ---- staging: global -> registers -> LDS --------------------------------
-  const int krow0 = tid / CH, kch = tid % CH;       // K: LDS row krow0 + KROWS*p, chunk kch
-  const int kkey0 = kperm(krow0);                    // ... holding key kperm(row)
-  const int vkey = (tid & 15) * 4, vch = tid >> 4;   // V: keys vkey..vkey+3, chunk vch
-  const bool vact = tid < VUNITS;
-  const long long rstride = (long long)Hkv * D;      // elements between key rows
-  const uint16_t *kseq = k + (s0 * Hkv + hk) * (long long)D;
-  const uint16_t *vseq = v + (s0 * Hkv + hk) * (long long)D;
-  const uint32_t rbytes = (uint32_t)(rstride * 2);
-
-  u32x4 kreg[KPASS];
-  u32x4 vreg[4];
-  auto gload_k = [&](int j) {
-    const int key0 = j * kBC;
-    const __amdgpu_buffer_rsrc_t kr =
-        make_rsrc(kseq + key0 * rstride, (uint32_t)min(kBC, n - key0) * rbytes);  // rows past n read 0
+  // LDS operand addresses (elements).  K: row kb*32 + l32, chunk 2kk + hh.
+  // V^T (transposing reads): lane t of a 16-lane group reads 4 elements of key
+  // row 4*hh + (t >> 2) (+32 kb + 16 ks' + 8 r) at columns 32*db + 16*group
+  // parity + 4*(t & 3), and receives column t of 4 consecutive key rows.
+  const int kx = l32 & (CH - 1);
+  int vbase[DBLK];
+  {
+    const int t16 = lane & 15;
+    const int vrow = 4 * hh + (t16 >> 2);
+    const int vx = vswz<CH>(t16 >> 2);
+    const int vcol = 2 * ((lane >> 4) & 1) + ((t16 & 3) >> 1);
 #pragma unroll
-    for (int p = 0; p < KPASS; ++p)
-      kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(kr, (kkey0 + p * KROWS) * rbytes + kch * 16, 0, 0);
-  };
-  auto gload_v = [&](int j) {
-    const int key0 = j * kBC;
-    const __amdgpu_buffer_rsrc_t vr =
-        make_rsrc(vseq + key0 * rstride, (uint32_t)min(kBC, n - key0) * rbytes);
-    if (vact) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        vreg[rr] = __builtin_amdgcn_raw_buffer_load_b128(vr, (vkey + rr) * rbytes + vch * 16, 0, 0);
-    }
-  };
-  auto swrite_k = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < KPASS; ++p)
-      *reinterpret_cast<u32x4 *>(&sm.k[buf][krow0 + p * KROWS][kch * 8]) = kreg[p];
-  };
-  auto swrite_v = [&](int buf) {
-    if (vact) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wsel = e >> 1, hi = e & 1;
-        u32x2 pk;
-        pk[0] = sel16(vreg[0][wsel], hi) | (sel16(vreg[1][wsel], hi) << 16);
-        pk[1] = sel16(vreg[2][wsel], hi) | (sel16(vreg[3][wsel], hi) << 16);
-        *reinterpret_cast<u32x2 *>(&sm.vt[buf][vch * 8 + e][vkey]) = pk;
-      }
-    }
-  };
+    for (int db = 0; db < DBLK; ++db)
+      vbase[db] = vrow * D + 8 * ((4 * db + vcol) ^ vx) + 4 * (t16 & 1);
+  }
 
   // ---- per-tile work -------------------------------------------------------
   // tile j has keys j*64 .. j*64+63; it is wholly above this wave's diagonal
   // when its first key is past the wave's last query row
   auto active = [&](int j) { return j * kBC <= tw0 + 31 && tw0 < n; };
 
-  // S^T = K Q^T for tile j (two 32-key blocks) from K buffer j & 1
-  auto scores = [&](int j, f32x16 (&s)[2]) {
+  // S^T = K Q^T for one tile (two 32-key blocks); accumulator slot rr of block
+  // kb (lane half hh) holds key 32 kb + 8 (rr >> 2) + 4 hh + (rr & 3)
+  auto scores = [&](auto par, f32x16 (&s)[2]) {
+    const uint16_t *ks = kst(par);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
-      const uint16_t *kr = &sm.k[j & 1][kb * 32 + l32][hh * 8];
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(kr + kk * 16));
+        const bf16x8 a = as_bf16x8(
+            *reinterpret_cast<const u32x4 *>(ks + (kb * 32 + l32) * D + 8 * ((2 * kk + hh) ^ kx)));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
       }
     }
@@ -225,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-          const int key = key0 + kb * 32 + (rr >> 3) * 16 + hh * 8 + ((rr >> 2) & 1) * 4 + (rr & 3);
+          const int key = key0 + kb * 32 + (rr >> 2) * 8 + hh * 4 + (rr & 3);
           if (key > tq || key >= n) s[kb][rr] = -INFINITY;
         }
       }
@@ -249,7 +262,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     return (m_run == -INFINITY) ? 0.f : -m_run;
   };
 
-  // softmax back half: P = exp2(s*scale - m) in bf16, row sum
+  // softmax back half: P = exp2(s*scale - m) in bf16, row sum.  The 8
+  // accumulator slots 8 (ks & 1) .. +7 of block ks >> 1 form k-step ks.
   auto softmax_back = [&](f32x16 (&s)[2], float neg_m, bf16x8 (&pf)[4]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -265,87 +279,75 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     }
   };
 
-  // O^T += V^T P^T from V buffer j & 1 (k-step major: the MFMAs of k-step ks
-  // need only pf[ks], and consecutive MFMAs feed different accumulators)
-  auto pv = [&](int j, bf16x8 (&pf)[4]) {
+  // O^T += V^T P^T (k-step major: the MFMAs of k-step ks need only pf[ks]).
+  // Element e of the operands is key 16 ks + 4 hh + 8 (e >> 2) + (e & 3), the
+  // order in which the score accumulator holds P.
+  auto pv = [&](auto par, bf16x8 (&pf)[4]) {
+    const uint16_t *vs = vst(par);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
-        const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.vt[j & 1][db * 32 + l32][hh * 8 + ks * 16]);
+        const uint16_t *ap = vs + vbase[db] + 16 * ks * D;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YR_LDS i16x4 *)(ap));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YR_LDS i16x4 *)(ap + 8 * D));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 w = {l2[0], l2[1], h2[0], h2[1]};
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), pf[ks], o[db], 0, 0, 0);
       }
     }
   };
 
-  // One pipeline step j: stage K(j+2) and V(j+1) into the buffers freed by
-  // step j-1, start the loads of K(j+3) and V(j+2), then the score MFMAs of
-  // tile j+1 alongside the softmax of tile j, then the PV MFMAs of tile j.
-  const int last = (qend - 1) / kBC;
-  auto stage = [&](int j) {
+  // One pipeline step j (par = j & 1): after the barrier the K stage of tile
+  // j and the V stage of tile j-1 are free; copy K(j+2) and V(j+1) into them,
+  // then the score MFMAs of tile j+1 alongside the softmax of tile j, then the
+  // PV MFMAs of tile j.  Each wave waits for its own copies before the
+  // barrier, so after it every copy issued one step earlier is visible.
+  auto flip = [](auto par) { return std::integral_constant<int, 1 - decltype(par)::value>{}; };
+  auto stage = [&](auto par, int j) {
+    wait_dma();
     __syncthreads();
-    if (j + 2 <= last) swrite_k(j & 1);
-    if (j + 1 <= last) swrite_v((j + 1) & 1);
-    if (j + 3 <= last) gload_k(j + 3);
-    if (j + 2 <= last) gload_v(j + 2);
+    if (j + 2 <= last) copy_tile(kst(par), kseq, j + 2, false);
+    if (j + 1 <= last) copy_tile(vst(flip(par)), vseq, j + 1, true);
   };
   // General step (diagonal and tail tiles, the last step): every check.
-  auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-    stage(j);
-    if (j + 1 <= last && active(j + 1)) scores(j + 1, nxt);
+  auto step = [&](auto par, int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    stage(par, j);
+    if (j + 1 <= last && active(j + 1)) scores(flip(par), nxt);
     if (active(j)) {
       const float neg_m = softmax_front(j, cur, true);
       bf16x8 pf[4];
       softmax_back(cur, neg_m, pf);
-      pv(j, pf);
+      pv(par, pf);
     }
   };
   // Steady step: tiles j and j+1 lie wholly below every row of the workgroup
   // (no mask, all waves active), so the score MFMAs of tile j+1, the exp /
-  // convert work of tile j and the PV MFMAs of tile j form one basic block,
-  // and the scheduler is told to interleave matrix and vector instructions.
-  auto step_steady = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-    stage(j);
+  // convert work of tile j and the PV MFMAs of tile j form one basic block.
+  auto step_steady = [&](auto par, int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    stage(par, j);
     const float neg_m = softmax_front(j, cur, false);
-    scores(j + 1, nxt);
+    scores(flip(par), nxt);
     bf16x8 pf[4];
     softmax_back(cur, neg_m, pf);
-    pv(j, pf);
-    // two operand reads ahead, then each MFMA followed by the next read and
-    // a share of the exp / convert work
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
-#pragma unroll
-    for (int i = 0; i < 2 * KSTEPS + 4 * DBLK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
-    }
+    pv(par, pf);
   };
 
-  // prologue: K(0), K(1), V(0) in LDS; K(2), V(1) in registers; S(0)
-  gload_k(0);
-  gload_v(0);
-  swrite_k(0);
-  swrite_v(0);
-  if (last >= 1) {
-    gload_k(1);
-    swrite_k(1);
-  }
-  if (last >= 2) gload_k(2);
-  if (last >= 1) gload_v(1);
+  // prologue: K(0), V(0), K(1) copied; S(0)
+  wait_dma();
   __syncthreads();
   f32x16 sa[2], sb[2];
-  if (active(0)) scores(0, sa);
+  if (active(0)) scores(P0{}, sa);
   // tiles below q0 (the workgroup's first row) need no mask for any wave
   const int steady_end = q0 / kBC - 1;  // steps j with j + 1 < q0 / kBC
   int j = 0;
   for (; j + 1 < steady_end; j += 2) {
-    step_steady(j, sa, sb);
-    step_steady(j + 1, sb, sa);
+    step_steady(P0{}, j, sa, sb);
+    step_steady(P1{}, j + 1, sb, sa);
   }
   for (; j <= last; j += 2) {
-    step(j, sa, sb);
-    if (j + 1 <= last) step(j + 1, sb, sa);
+    step(P0{}, j, sa, sb);
+    if (j + 1 <= last) step(P1{}, j + 1, sb, sa);
   }
 
   // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ---------------------
