@@ -28,6 +28,10 @@ Other modes:
     --copy-probe              also run a 1 GiB device copy (counter calibration)
     --summarize DIR --out F   turn rocprofv3 output (kernel stats or counter
                               CSVs under DIR) into a short text summary
+    --counters-json FETCH_DIR WRITE_DIR [--command "c1 ;; c2"]
+                              HBM bytes per launch of the prefill and decode
+                              kernels from FETCH_SIZE / WRITE_SIZE runs of
+                              `bench.py --copy-probe`, into profiles/
 """
 
 from __future__ import annotations
@@ -55,10 +59,16 @@ DECODE_SOURCES = ["yarn_scaled_rope_amd/csrc/decode.hip",
 
 
 def source_digest(paths) -> str:
+    """Digest of the kernel sources with comments and whitespace removed, so
+    that a counter summary stays valid across comment-only edits."""
+    import re
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -225,16 +235,21 @@ def bench_decode(args, torch, ops, wl):
 
 
 # ------------------------------------------------------------------ CPU baseline
+def oracle_threads() -> int:
+    """Threads the oracle's BLAS calls use (the host cores it runs on)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(cfg_name, state, wl, target_s: float):
     """The fp64 oracle, as it stands, on the first heads of the same prefill
     inputs (all rows of each head), until about target_s seconds of work."""
     from oracle import attention as oatt
     from oracle import freqs as ofreqs
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = oracle_threads()
     cfg = wl.PREFILL_CONFIGS[cfg_name]
     inp = state["inp"]
     th = ofreqs.yarn_theta(cfg.head_dim, cfg.base, cfg.factor, cfg.original_max_position)
@@ -262,31 +277,41 @@ def cpu_baseline(cfg_name, state, wl, target_s: float):
                       f"heads, all {cfg.total_tokens} rows each, same inputs"}
 
 
-def cpu_baseline_decode(state, wl, torch):
-    """The fp64 oracle on one sequence of the decode workload (its inputs
-    copied back from device memory)."""
+def cpu_baseline_decode(state, wl, torch, seconds: float = 10.0, nseq: int = 4):
+    """The fp64 oracle on the first `nseq` sequences of the decode workload
+    (inputs copied back from device memory and widened once), repeated in
+    whole passes until at least `seconds` have elapsed."""
     import numpy as np
     from oracle import attention as oatt
     from oracle import freqs as ofreqs
     cfg = wl.DECODE_B16
     th = ofreqs.yarn_theta(cfg.head_dim, cfg.base, cfg.factor, cfg.original_max_position)
     sc = ofreqs.softmax_scale(cfg.head_dim, ofreqs.attention_temperature(cfg.factor))
-    b = 0
-    L = int(state["seqlens"][b])
 
     def host(t):
         return wl.as_f64(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
 
-    kc = host(state["kc"][b:b + 1, :L])
-    vc = host(state["vc"][b:b + 1, :L])
-    q = host(state["q"][b:b + 1])
+    seqs = []
+    for b in range(min(nseq, len(state["seqlens"]))):
+        L = int(state["seqlens"][b])
+        seqs.append((host(state["q"][b:b + 1]), host(state["kc"][b:b + 1, :L]),
+                     host(state["vc"][b:b + 1, :L]), state["seqlens"][b:b + 1]))
+    lens = [int(x[3][0]) for x in seqs]
+    passes = 0
     t0 = time.perf_counter()
-    oatt.decode(q, kc, vc, state["seqlens"][b:b + 1], th, sc)
-    dt = time.perf_counter() - t0
-    nbytes = wl.decode_kv_bytes([L], cfg.hkv, cfg.head_dim)
-    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "kind": "oracle",
+    while True:
+        for q, kc, vc, sl in seqs:
+            oatt.decode(q, kc, vc, sl, th, sc)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    nbytes = wl.decode_kv_bytes(lens, cfg.hkv, cfg.head_dim) * passes
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": oracle_threads(),
+            "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"fp64 decode of sequence 0 (cache length {L}) of the same inputs"}
+            "sample": f"fp64 decode of sequences 0-{len(seqs) - 1} (cache lengths {lens}) of the "
+                      f"same inputs, {passes} whole passes"}
 
 
 # ------------------------------------------------------------------ rocprof summaries
@@ -323,6 +348,69 @@ def summarize(dirname: str, out_path: str, command: str):
     print(out_path)
 
 
+def counters_json(fetch_dir: str, write_dir: str, workload: str, commands):
+    """Per-launch HBM bytes of the prefill and decode kernels from two
+    rocprofv3 --pmc runs of `bench.py --copy-probe` (FETCH_SIZE, WRITE_SIZE;
+    KiB per dispatch).  Each counter is scaled by what it reads for the 1 GiB
+    device copy of the probe (WRITE_SIZE of that copy picks it out; FETCH_SIZE
+    is taken from the same kernel in the other run).  Writes
+    profiles/{kind}_{workload}_hbm_counters.json for both kernels."""
+    import csv
+
+    def load(d, counter):
+        out = []  # (dispatch id, kernel name, value) in dispatch order
+        acc = {}
+        for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(p)):
+                if r.get("Counter_Name") != counter:
+                    continue
+                i = int(r["Dispatch_Id"])
+                k, v = acc.get(i, (r["Kernel_Name"], 0.0))
+                acc[i] = (k, v + float(r["Counter_Value"] or 0))
+        for i in sorted(acc):
+            out.append((i, acc[i][0], acc[i][1]))
+        return out
+
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    gib_kib = (1 << 30) / 1024
+    copy = min((x for x in write if "yr::" not in x[1]), key=lambda x: abs(x[2] - gib_kib))
+    copy_fetch = [x[2] for x in fetch if x[1] == copy[1]]
+    copy_fetch = max(copy_fetch)  # the 1 GiB copy is the largest dispatch of that kernel
+    scale_fetch, scale_write = gib_kib / copy_fetch, gib_kib / copy[2]
+
+    def mean(rows, key):
+        v = [x[2] for x in rows if key in x[1]]
+        return sum(v) / len(v) if v else None
+
+    kinds = {
+        "prefill_bf16": (workload, ["prefill_bf16_kernel"], ATTN_SOURCES,
+                         "one attn_prefill_fwd launch (keys pre-rotated)"),
+        "decode": ("decode_b16_gqa_32k_128k", ["decode_mfma_kernel", "decode_merge_kernel"],
+                   DECODE_SOURCES, "split + merge kernels of one attn_decode call"),
+    }
+    written = []
+    for kind, (wname, keys, srcs, note) in kinds.items():
+        f_kib = [mean(fetch, k) for k in keys]
+        w_kib = [mean(write, k) for k in keys]
+        if any(x is None for x in f_kib + w_kib):
+            continue
+        per_kernel = {k: int(round((fk * scale_fetch + wk * scale_write) * 1024))
+                      for k, fk, wk in zip(keys, f_kib, w_kib)}
+        d = {"kernel": " + ".join(keys), "workload": wname, "source_digest": source_digest(srcs),
+             "fetch_kib_per_dispatch_raw": dict(zip(keys, f_kib)),
+             "write_kib_per_dispatch_raw": dict(zip(keys, w_kib)),
+             "copy_probe": {"kernel": copy[1][:100], "bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                            "fetch_kib": copy_fetch, "write_kib": copy[2]},
+             "scale_fetch": scale_fetch, "scale_write": scale_write,
+             "hbm_bytes_per_launch": sum(per_kernel.values()), "bytes_per_kernel": per_kernel,
+             "commands": list(commands), "note": note}
+        path = os.path.join(ROOT, "profiles", f"{kind}_{wname}_hbm_counters.json")
+        with open(path, "w") as fh:
+            json.dump(d, fh, indent=1)
+        written.append(path)
+    print("\n".join(written))
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -336,10 +424,15 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize", default=None)
+    ap.add_argument("--counters-json", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None)
     ap.add_argument("--out", default=None)
     ap.add_argument("--command", default="")
     args = ap.parse_args()
 
+    if args.counters_json:
+        counters_json(args.counters_json[0], args.counters_json[1], args.workload,
+                      args.command.split(" ;; ") if args.command else [])
+        return 0
     if args.summarize:
         summarize(args.summarize, args.out or "summary.txt", args.command)
         return 0

@@ -7,7 +7,7 @@
 // sums and output accumulators; "LLM context window mechanics": tiles kept on
 // chip).  Queries are rotated on load with fp64 angles; keys arrive rotated.
 //
-// Work decomposition (one workgroup = 4 waves = 128 query rows of one head):
+// Work decomposition (one workgroup = 8 waves = 256 query rows of one head):
 //   * Every wave owns 32 consecutive query rows.  Scores are formed
 //     transposed, S^T = K * Q^T, so the 32x32 accumulator of a lane holds ONE
 //     query (lane % 32) against 16 keys; the row max and row sum need only
@@ -15,20 +15,19 @@
 //   * The output is also formed transposed, O^T = V^T * P^T, so the lane that
 //     owns a query owns its output column and its rescale factor.
 //   * P^T goes straight from the score accumulator into the B operand: the
-//     8 consecutive accumulator registers 8*(ks%2)..+7 of key block ks/2 are
-//     one 16-key k-step.  K rows are permuted in LDS (kperm) so that those 8
-//     registers are 8 consecutive keys, read from V^T as one 16-byte load.
-//   * Software pipeline inside each wave: step j issues the score MFMAs of
-//     tile j+1 and, independent of them, the softmax of tile j (VALU and
-//     transcendental work), then the PV MFMAs of tile j.  The matrix cores
-//     and the vector ALUs of one wave therefore overlap without relying on
-//     the other wave of the SIMD being out of phase.
-//   * K tiles are staged two tiles ahead and V tiles one tile ahead in LDS
-//     (double-buffered each; K row-major, V transposed to V^T[d][key]), rows
-//     padded so that both the staging writes and the operand reads are free
-//     of bank conflicts; one barrier per step; the global loads of the next
-//     tiles are in flight while a step computes.  Loads are buffer loads
-//     whose range ends at the sequence end, so rows past it read as 0.
+//     8 accumulator registers 8*(ks%2)..+7 of key block ks/2 are one 16-key
+//     k-step.  The V^T operand comes from transposing LDS reads
+//     (ds_read_b64_tr_b16) whose key order matches that register order.
+//   * K and V tiles (64 keys) are copied from HBM straight into LDS
+//     (buffer_load ... lds): no staging registers, no VALU, no LDS writes.
+//     Each lane fetches the source chunk that belongs in its LDS slot, which
+//     realises the XOR swizzles that keep the operand reads free of bank
+//     conflicts.  Loads are buffer loads whose range ends at the sequence
+//     end, so rows past it read as 0.
+//   * Software pipeline inside each wave: step j copies the tiles two steps
+//     ahead, then issues the score MFMAs of tile j+1 and, independent of
+//     them, the softmax of tile j (VALU and transcendental work), then the PV
+//     MFMAs of tile j.  One barrier per step.
 //   * The running max is lazy: it moves only when a row max exceeds it by
 //     more than 2^8, so the O rescale is skipped on most tiles.
 //   * Tiles wholly above a wave's diagonal are skipped by that wave; masking
@@ -50,10 +49,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define YR_LDS __attribute__((address_space(3)))
+#define YR_INLINE __attribute__((always_inline))
 
-constexpr int kThreads = 256;
-constexpr int kBQ = 128;   // query rows per workgroup (4 waves x 32)
-constexpr int kBC = 64;    // keys per tile
+constexpr int kThreads = 512;
+constexpr int kBQ = kThreads / 2;  // query rows per workgroup (32 per wave)
+constexpr int kBC = 64;            // keys per tile
+constexpr int kStages = 2;         // LDS stages of K and of V (2 or 3; 3 measured no faster)
 constexpr int kXcds = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -68,8 +69,21 @@ __device__ __forceinline__ int vswz(int e) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-// s_waitcnt vmcnt(0) only: this wave's tile copies into LDS have landed
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N) only (gfx9 encoding): at most N of this wave's tile
+// copies into LDS are still in flight
+template <int N>
+__device__ __forceinline__ void wait_dma() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 template <int D, bool OUT_F32, bool ROTATE_Q>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
@@ -81,12 +95,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   constexpr int DBLK = D / 32;       // 32-row blocks of O^T
   constexpr int CH = D / 8;          // 16-byte chunks per row
   constexpr int RPI = 64 / CH;       // rows per 1 KB tile copy instruction
-  constexpr int DPW = kBC / RPI / 4; // copy instructions per wave per tile
+  constexpr int DPW = kBC / RPI / (kThreads / 64);  // copy instructions per wave per tile
   constexpr int TILE = kBC * D;      // elements of a K or V tile
 
+  constexpr int NS = kStages;
+  static_assert(NS == 2 || NS == 3, "two or three stages");
+  constexpr int TILE3 = NS > 2 ? TILE : 8;
   // one array per stage: the compiler then tells a stage being read from the
-  // copies in flight into the other stage, and adds no wait for them
-  __shared__ __align__(16) uint16_t sk0[TILE], sk1[TILE], sv0[TILE], sv1[TILE];
+  // copies in flight into the other stages, and adds no wait for them
+  __shared__ __align__(16) uint16_t sk0[TILE], sk1[TILE], sk2[TILE3];
+  __shared__ __align__(16) uint16_t sv0[TILE], sv1[TILE], sv2[TILE3];
 
   if (flag != nullptr && blockIdx.x == 0) validate_cu_seqlens(cu, B, T, max_seqlen, flag);
 
@@ -135,7 +153,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     koff[i] = drow * rbytes + 16 * (dslot ^ (row & (CH - 1)));
   }
   const uint32_t voff = drow * rbytes + 16 * (dslot ^ vswz<CH>(drow & 3));
-  auto copy_tile = [&](uint16_t *dst, const uint16_t *seq, int t, bool is_v) {
+  auto copy_tile = [&](uint16_t *dst, const uint16_t *seq, int t, bool is_v) YR_INLINE {
     const int key0 = t * kBC;
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(seq + key0 * rstride, (uint32_t)min(kBC, n - key0) * rbytes);
@@ -147,19 +165,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
                                                (int)(p * RPI * rbytes), 0, 0);
     }
   };
-  auto kst = [&](auto par) -> uint16_t * {
-    if constexpr (decltype(par)::value == 0) return sk0; else return sk1;
+  // tile t lives in stage t % NS; `par` below is that stage index
+  auto kst = [&](auto par) YR_INLINE -> uint16_t * {
+    constexpr int P = decltype(par)::value;
+    if constexpr (P == 0) return sk0; else if constexpr (P == 1) return sk1; else return sk2;
   };
-  auto vst = [&](auto par) -> uint16_t * {
-    if constexpr (decltype(par)::value == 0) return sv0; else return sv1;
+  auto vst = [&](auto par) YR_INLINE -> uint16_t * {
+    constexpr int P = decltype(par)::value;
+    if constexpr (P == 0) return sv0; else if constexpr (P == 1) return sv1; else return sv2;
   };
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
   const int last = (qend - 1) / kBC;
-  // prologue copies go out before the query work so that they are in flight
-  copy_tile(sk0, kseq, 0, false);
-  copy_tile(sv0, vseq, 0, true);
-  if (last >= 1) copy_tile(sk1, kseq, 1, false);
+  // prologue copies (K of tiles 0..NS-1, V of tiles 0..NS-2) go out before
+  // the query work so that they are in flight meanwhile
+  static_for<0, NS>([&](auto ic) YR_INLINE {
+    constexpr int I = decltype(ic)::value;
+    if (I <= last) copy_tile(kst(ic), kseq, I, false);
+    if (I + 1 < NS && I <= last) copy_tile(vst(ic), vseq, I, true);
+  });
 
   // ---- Q fragments (B operand of S^T = K Q^T), rotated on load -----------
   bf16x8 qf[KSTEPS];
@@ -211,11 +233,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   // ---- per-tile work -------------------------------------------------------
   // tile j has keys j*64 .. j*64+63; it is wholly above this wave's diagonal
   // when its first key is past the wave's last query row
-  auto active = [&](int j) { return j * kBC <= tw0 + 31 && tw0 < n; };
+  auto active = [&](int j) YR_INLINE { return j * kBC <= tw0 + 31 && tw0 < n; };
 
   // S^T = K Q^T for one tile (two 32-key blocks); accumulator slot rr of block
   // kb (lane half hh) holds key 32 kb + 8 (rr >> 2) + 4 hh + (rr & 3)
-  auto scores = [&](auto par, f32x16 (&s)[2]) {
+  auto scores = [&](auto par, f32x16 (&s)[2]) YR_INLINE {
     const uint16_t *ks = kst(par);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -231,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 
   // softmax front half of tile j: mask (diagonal/tail tiles only), row max,
   // lazy rescale of the running state; returns -m for the exp2 argument
-  auto softmax_front = [&](int j, f32x16 (&s)[2], bool may_mask) -> float {
+  auto softmax_front = [&](int j, f32x16 (&s)[2], bool may_mask) YR_INLINE -> float {
     const int key0 = j * kBC;
     if (may_mask && ((key0 + kBC - 1 > tw0) || (key0 + kBC > n))) {
 #pragma unroll
@@ -264,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 
   // softmax back half: P = exp2(s*scale - m) in bf16, row sum.  The 8
   // accumulator slots 8 (ks & 1) .. +7 of block ks >> 1 form k-step ks.
-  auto softmax_back = [&](f32x16 (&s)[2], float neg_m, bf16x8 (&pf)[4]) {
+  auto softmax_back = [&](f32x16 (&s)[2], float neg_m, bf16x8 (&pf)[4]) YR_INLINE {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       u32x4 w;
@@ -282,7 +304,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   // O^T += V^T P^T (k-step major: the MFMAs of k-step ks need only pf[ks]).
   // Element e of the operands is key 16 ks + 4 hh + 8 (e >> 2) + (e & 3), the
   // order in which the score accumulator holds P.
-  auto pv = [&](auto par, bf16x8 (&pf)[4]) {
+  auto pv = [&](auto par, bf16x8 (&pf)[4]) YR_INLINE {
     const uint16_t *vs = vst(par);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -298,22 +320,33 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     }
   };
 
-  // One pipeline step j (par = j & 1): after the barrier the K stage of tile
-  // j and the V stage of tile j-1 are free; copy K(j+2) and V(j+1) into them,
-  // then the score MFMAs of tile j+1 alongside the softmax of tile j, then the
-  // PV MFMAs of tile j.  Each wave waits for its own copies before the
-  // barrier, so after it every copy issued one step earlier is visible.
-  auto flip = [](auto par) { return std::integral_constant<int, 1 - decltype(par)::value>{}; };
-  auto stage = [&](auto par, int j) {
-    wait_dma();
+  // One pipeline step j (stage par = j % NS): after the barrier the K stage
+  // of tile j (read by the scores of step j-1) and the V stage of tile j-1
+  // are free; copy K(j+NS) and V(j+NS-1) into them, then run the score MFMAs
+  // of tile j+1 alongside the softmax of tile j, then the PV MFMAs of tile j.
+  // Before the barrier each wave waits for its own copies of K(j+1) and V(j),
+  // issued NS-1 steps earlier; the copies of the last NS-2 steps may still be
+  // in flight.
+  auto nextp = [](auto par) YR_INLINE { return std::integral_constant<int, (decltype(par)::value + 1) % NS>{}; };
+  auto prevp = [](auto par) YR_INLINE { return std::integral_constant<int, (decltype(par)::value + NS - 1) % NS>{}; };
+  auto stage = [&](auto par, int j) YR_INLINE {
+    if constexpr (NS == 2) {
+      wait_dma<0>();
+    } else {
+      // copies issued by step j-1: K(j+2) and V(j+1) when those tiles exist
+      const int pending = (j >= 1 && j + 2 <= last ? 1 : 0) + (j >= 1 && j + 1 <= last ? 1 : 0);
+      if (pending == 2) wait_dma<2 * DPW>();
+      else if (pending == 1) wait_dma<DPW>();
+      else wait_dma<0>();
+    }
     __syncthreads();
-    if (j + 2 <= last) copy_tile(kst(par), kseq, j + 2, false);
-    if (j + 1 <= last) copy_tile(vst(flip(par)), vseq, j + 1, true);
+    if (j + NS <= last) copy_tile(kst(par), kseq, j + NS, false);
+    if (j + NS - 1 <= last) copy_tile(vst(prevp(par)), vseq, j + NS - 1, true);
   };
   // General step (diagonal and tail tiles, the last step): every check.
-  auto step = [&](auto par, int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+  auto step = [&](auto par, int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) YR_INLINE {
     stage(par, j);
-    if (j + 1 <= last && active(j + 1)) scores(flip(par), nxt);
+    if (j + 1 <= last && active(j + 1)) scores(nextp(par), nxt);
     if (active(j)) {
       const float neg_m = softmax_front(j, cur, true);
       bf16x8 pf[4];
@@ -324,30 +357,43 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   // Steady step: tiles j and j+1 lie wholly below every row of the workgroup
   // (no mask, all waves active), so the score MFMAs of tile j+1, the exp /
   // convert work of tile j and the PV MFMAs of tile j form one basic block.
-  auto step_steady = [&](auto par, int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+  auto step_steady = [&](auto par, int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) YR_INLINE {
     stage(par, j);
     const float neg_m = softmax_front(j, cur, false);
-    scores(flip(par), nxt);
+    scores(nextp(par), nxt);
     bf16x8 pf[4];
     softmax_back(cur, neg_m, pf);
     pv(par, pf);
   };
 
-  // prologue: K(0), V(0), K(1) copied; S(0)
-  wait_dma();
+  // prologue: every prologue copy landed; S(0)
+  wait_dma<0>();
   __syncthreads();
   f32x16 sa[2], sb[2];
-  if (active(0)) scores(P0{}, sa);
+  if (active(0)) scores(std::integral_constant<int, 0>{}, sa);
+  // Steps are unrolled over the stage index (j % NS) and the score buffer
+  // (j % 2), so every LDS array and register array is picked at compile time.
+  constexpr int BL = NS == 2 ? 2 : 6;
+  auto sbuf = [&](auto ic) YR_INLINE -> f32x16(&)[2] {
+    if constexpr (decltype(ic)::value % 2 == 0) return sa; else return sb;
+  };
+  auto obuf = [&](auto ic) YR_INLINE -> f32x16(&)[2] {
+    if constexpr (decltype(ic)::value % 2 == 0) return sb; else return sa;
+  };
   // tiles below q0 (the workgroup's first row) need no mask for any wave
   const int steady_end = q0 / kBC - 1;  // steps j with j + 1 < q0 / kBC
   int j = 0;
-  for (; j + 1 < steady_end; j += 2) {
-    step_steady(P0{}, j, sa, sb);
-    step_steady(P1{}, j + 1, sb, sa);
+  for (; j + BL - 1 < steady_end; j += BL) {
+    static_for<0, BL>([&](auto ic) YR_INLINE {
+      constexpr int I = decltype(ic)::value;
+      step_steady(std::integral_constant<int, I % NS>{}, j + I, sbuf(ic), obuf(ic));
+    });
   }
-  for (; j <= last; j += 2) {
-    step(P0{}, j, sa, sb);
-    if (j + 1 <= last) step(P1{}, j + 1, sb, sa);
+  for (; j <= last; j += BL) {
+    static_for<0, BL>([&](auto ic) YR_INLINE {
+      constexpr int I = decltype(ic)::value;
+      if (j + I <= last) step(std::integral_constant<int, I % NS>{}, j + I, sbuf(ic), obuf(ic));
+    });
   }
 
   // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ---------------------
