@@ -23,6 +23,16 @@ Definitions followed:
   * Decode: one new query per sequence, rotated at its position (by default
     the cache length L_b), attends to cache entries 0 .. L_b-1 with no mask.
     Cached keys are taken as already rotated.
+  * Sliding window and sinks (optional): with a window of W tokens a query
+    at position m sees only the W most recent positions m-W+1 .. m ("Arch 03
+    -- Long Context", sliding-window slide); S sink tokens, positions
+    0 .. S-1, stay visible to every later query (StreamingLLM: keep the first
+    tokens and the last W; "Long context (engineering 100k+ tokens)",
+    attention sinks).  Positions are the original ones; W = 0 means no window.
+  * Chunked prefill: new tokens of a sequence whose first ctx_b tokens are
+    already cached sit at positions ctx_b + i and attend to cache entries
+    0 .. ctx_b + i (the chunk's own keys are in the cache too), so the causal
+    boundary moves to the bottom-right of the (chunk x cache) score block.
 
 Row blocking below only bounds memory: every row is still computed from its
 definition over its full set of visible keys, and rows are independent.
@@ -33,6 +43,18 @@ import numpy as np
 from .rope import rotate
 
 _ROW_BLOCK = 1024
+
+
+def visible(m, n, window: int = 0, sinks: int = 0):
+    """Key position n is visible to query position m (broadcasting arrays):
+    causal (n <= m), and inside the window of the W most recent positions or
+    among the first S positions when a window is set."""
+    m = np.asarray(m)
+    n = np.asarray(n)
+    ok = n <= m
+    if window > 0:
+        ok = ok & ((n > m - window) | (n < sinks))
+    return ok
 
 
 def attend(z: np.ndarray, v: np.ndarray):
@@ -58,7 +80,7 @@ def _group(hq: int, hkv: int) -> int:
     return hq // hkv
 
 
-def prefill(q, k, v, cu_seqlens, theta, scale):
+def prefill(q, k, v, cu_seqlens, theta, scale, window: int = 0, sinks: int = 0):
     """Causal prefill over a packed ragged batch.
 
     q: [T, Hq, D]; k, v: [T, Hkv, D] (unrotated; theta=None means q and k
@@ -92,14 +114,14 @@ def prefill(q, k, v, cu_seqlens, theta, scale):
                 z = scale * (qs[r0:r1, h, :] @ kh[:r1].T)     # [R, r1]
                 rows = np.arange(r0, r1)[:, None]
                 cols = np.arange(r1)[None, :]
-                z[cols > rows] = -np.inf
+                z[~visible(rows, cols, window, sinks)] = -np.inf
                 o, l = attend(z, vh[:r1])
                 out[s0 + r0:s0 + r1, h, :] = o
                 lse[h, s0 + r0:s0 + r1] = l
     return out, lse
 
 
-def prefill_rows(q, k, v, cu_seqlens, theta, scale, rows):
+def prefill_rows(q, k, v, cu_seqlens, theta, scale, rows, window: int = 0, sinks: int = 0):
     """Causal prefill evaluated only at the requested (token, head) pairs,
     each over its full causal prefix.  ``rows`` is an iterable of
     (global token index, query head).  Returns (out [R, D], lse [R]) in the
@@ -139,20 +161,23 @@ def prefill_rows(q, k, v, cu_seqlens, theta, scale, rows):
                 qr = rotate(qr, pos, theta)
             span = int(pos.max()) + 1
             z = scale * (qr @ kk[:span].T)
-            z[np.arange(span)[None, :] > pos[:, None]] = -np.inf
+            z[~visible(pos[:, None], np.arange(span)[None, :], window, sinks)] = -np.inf
             o, l = attend(z, vv[:span])
             out[part] = o
             lse[part] = l
     return out, lse
 
 
-def decode(q, k_cache, v_cache, seqlens, theta, scale, q_pos=None):
+def decode(q, k_cache, v_cache, seqlens, theta, scale, q_pos=None, window: int = 0,
+           sinks: int = 0):
     """One new query per sequence over a contiguous per-sequence cache.
 
     q: [B, Hq, D] (unrotated); k_cache, v_cache: [B, Lmax, Hkv, D] with keys
     already rotated; seqlens: [B] cache lengths L_b >= 1.  The query of
-    sequence b is rotated at q_pos[b] (default L_b) and attends to cache rows
-    0 .. L_b-1.  Returns out [B, Hq, D] and lse [B, Hq], fp64."""
+    sequence b is rotated at q_pos[b] (default L_b) and attends to the cache
+    rows 0 .. L_b-1 that the window / sinks leave visible from that position
+    (all of them without a window).  Returns out [B, Hq, D] and lse [B, Hq],
+    fp64."""
     q = np.asarray(q)
     B, hq, d = q.shape
     hkv = k_cache.shape[2]
@@ -170,9 +195,69 @@ def decode(q, k_cache, v_cache, seqlens, theta, scale, q_pos=None):
             vv = np.asarray(v_cache[b, :L, hk, :], dtype=np.float64)
             heads = list(range(hk * g, (hk + 1) * g))
             z = scale * (qr[heads] @ kk.T)                 # [g, L]
+            if window > 0:
+                z[:, ~((np.arange(L) > m - window) | (np.arange(L) < sinks))] = -np.inf
             o, l = attend(z, vv)
             out[b, heads] = o
             lse[b, heads] = l
+    return out, lse
+
+
+def prefill_chunk(q, k_cache, v_cache, cu_seqlens_q, ctx_lens, theta, scale, window: int = 0,
+                  sinks: int = 0, rows=None):
+    """Prefill of new tokens against a per-sequence cache (chunked prefill).
+
+    q: [Tq, Hq, D] unrotated, packed by cu_seqlens_q; k_cache, v_cache:
+    [B, Lmax, Hkv, D] holding, for sequence b, ctx_lens[b] earlier tokens and
+    then the n_b new ones (keys already rotated).  Token i of the chunk sits
+    at position ctx_b + i and attends to the visible cache rows 0 .. ctx_b + i.
+    Returns out [Tq, Hq, D] and lse [Hq, Tq], fp64; with ``rows`` (an
+    iterable of (token, query head)) only those are evaluated and
+    (out [R, D], lse [R]) come back in that order."""
+    hq, d = q.shape[1], q.shape[2]
+    hkv = k_cache.shape[2]
+    g = _group(hq, hkv)
+    bounds = _sequence_bounds(cu_seqlens_q)
+    if rows is None:
+        want = [(t, h) for s0, s1 in bounds for t in range(s0, s1) for h in range(hq)]
+    else:
+        want = [(int(t), int(h)) for t, h in rows]
+    starts = np.array([b[0] for b in bounds])
+    groups = {}
+    for idx, (t, h) in enumerate(want):
+        b = int(np.searchsorted(starts, t, side="right") - 1)
+        while bounds[b][1] <= t:
+            b += 1
+        groups.setdefault((b, h // g), []).append(idx)
+    out_r = np.zeros((len(want), d), dtype=np.float64)
+    lse_r = np.zeros(len(want), dtype=np.float64)
+    for (b, hk), idxs in groups.items():
+        s0 = bounds[b][0]
+        ctx = int(ctx_lens[b])
+        pos_all = np.array([ctx + want[i][0] - s0 for i in idxs])
+        span = int(pos_all.max()) + 1
+        kk = np.asarray(k_cache[b, :span, hk, :], dtype=np.float64)
+        vv = np.asarray(v_cache[b, :span, hk, :], dtype=np.float64)
+        for c0 in range(0, len(idxs), 256):
+            part = idxs[c0:c0 + 256]
+            pos = pos_all[c0:c0 + 256]
+            qr = np.stack([np.asarray(q[want[i][0], want[i][1], :], dtype=np.float64)
+                           for i in part])
+            if theta is not None:
+                qr = rotate(qr, pos, theta)
+            z = scale * (qr @ kk.T)
+            z[~visible(pos[:, None], np.arange(span)[None, :], window, sinks)] = -np.inf
+            o, l = attend(z, vv)
+            out_r[part] = o
+            lse_r[part] = l
+    if rows is not None:
+        return out_r, lse_r
+    Tq = q.shape[0]
+    out = np.zeros((Tq, hq, d), dtype=np.float64)
+    lse = np.zeros((hq, Tq), dtype=np.float64)
+    for i, (t, h) in enumerate(want):
+        out[t, h] = out_r[i]
+        lse[h, t] = lse_r[i]
     return out, lse
 
 
