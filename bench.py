@@ -13,9 +13,11 @@ synchronisations; the JSON line's `value` is the algorithmic causal FLOPs of
 one step over the wall time of one step.
 
 The same run then times the decode hot path (split-K sweep + LSE merge) over
-the 16-sequence 32K-128K cache workload and reports it as `decode`, and
-times the fp64 CPU checker on a bounded sample of the prefill workload as
-`cpu_baseline`.
+the 16-sequence 32K-128K cache workload and reports it as `decode`; under
+`next` it times chunked prefill (4 chunks of 4096 new tokens after 28K-124K
+cached ones) and a 4096-token sliding window with 4 sink tokens on the
+prefill and decode inputs; and it times the fp64 CPU checker on bounded
+samples of the prefill and decode workloads as `cpu_baseline`.
 
 Roofline: the attention kernel's own duration comes from HIP events on the
 launch stream around its launch inside every timed step.  `traffic` is filled
@@ -26,6 +28,8 @@ counters on a plain copy of known size); otherwise it is null.
 Other modes:
     --workload NAME           time another prefill workload (parity configs)
     --copy-probe              also run a 1 GiB device copy (counter calibration)
+    --no-next                 skip the lines of the chunked-prefill and
+                              sliding-window paths (under "next")
     --summarize DIR --out F   turn rocprofv3 output (kernel stats or counter
                               CSVs under DIR) into a short text summary
     --counters-json FETCH_DIR WRITE_DIR [--command "c1 ;; c2"]
@@ -166,7 +170,8 @@ def bench_prefill(args, torch, ops, wl):
             "hq": hq, "hkv": hkv, "head_dim": D, "rope": "yarn", "rope_base": cfg.base,
             "factor": cfg.factor, "original_max_position": cfg.original_max_position,
             "out_dtype": "bf16", "seed": 1000 + cfg.index}
-    state = {"inp": inp, "q": q, "k": k, "v": v, "theta_host": f64, "scale": scale}
+    state = {"inp": inp, "q": q, "k": k, "v": v, "krot": krot, "cu": cu, "theta": theta,
+             "theta_host": f64, "scale": scale, "maxlen": maxlen}
     return value, ms_per_step, roof, extra, conf, state
 
 
@@ -230,8 +235,113 @@ def bench_decode(args, torch, ops, wl):
                         "kernel": "decode_mfma_kernel + decode_merge_kernel (one call)",
                         "kernel_ms": round(call_ms, 4), "bytes_per_launch": int(nbytes)},
            "source_digest": digest}
-    state = {"seqlens": inp["seqlens"], "q": q, "kc": kc, "vc": vc}
+    state = {"seqlens": inp["seqlens"], "sl": sl, "q": q, "kc": kc, "vc": vc, "theta": theta,
+             "scale": scale, "ws": ws}
     return res, state
+
+
+# ------------------------------------------------------------------ next rows
+def _event_ms(torch, fn, warmup: int, steps: int, stream) -> float:
+    """Mean duration (ms) of fn() between HIP events on the launch stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record(stream)
+        fn()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    return sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+
+
+def bench_next(args, torch, ops, wl, pstate, dstate):
+    """Chunked prefill (4 chunks of 4096 tokens after 28K..124K cached
+    tokens), and a 4096-token window with 4 sinks on the prefill and decode
+    inputs already resident.  Each line: algorithmic work / mean call time."""
+    import numpy as np
+    stream = torch.cuda.current_stream()
+    res = {}
+
+    cfg = wl.CHUNK_4X4K
+    D = cfg.head_dim
+    _, f64, t = ops.yarn_rope_freqs(D, cfg.base, cfg.factor, cfg.original_max_position)
+    theta = torch.from_numpy(f64).cuda()
+    scale = t / math.sqrt(D)
+    log(f"generating {cfg.name} inputs")
+    inp = wl.make_chunk(cfg)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, kc = up(inp["q"]), up(inp["k_cache"])
+    del inp["k_cache"]
+    vc = up(inp["v_cache"])
+    del inp["v_cache"]
+    cu = torch.from_numpy(inp["cu_seqlens_q"]).cuda()
+    ctx = torch.from_numpy(inp["ctx_lens"]).cuda()
+    out = torch.empty((q.shape[0], cfg.hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((cfg.hq, q.shape[0]), dtype=torch.float32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    nq = max(cfg.chunk_lens)
+    log("chunked prefill timed")
+    ms = _event_ms(torch, lambda: ops.attn_prefill_chunk(q, kc, vc, cu, ctx, nq, theta, scale,
+                                                         out=out, lse=lse, workspace=ws,
+                                                         stream=stream),
+                   args.warmup, max(5, args.steps // 2), stream)
+    if ops.read_device_error(ws) != 0:
+        raise SystemExit("device range check failed (chunked prefill)")
+    flops = wl.prefill_visible_flops(cfg.chunk_lens, cfg.hq, D, ctx_lens=cfg.ctx_lens)
+    tf = flops / (ms * 1e-3) / 1e12
+    res["chunked_prefill"] = {
+        "metric": "chunked prefill TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
+        "ms_per_call": round(ms, 4), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+        "flops_per_launch": flops,
+        "config": {"workload": cfg.name, "ctx_lens": list(cfg.ctx_lens),
+                   "chunk_lens": list(cfg.chunk_lens), "max_cache_len": cfg.max_cache_len,
+                   "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": D, "seed": 1000 + cfg.index}}
+    del q, kc, vc, out, lse
+
+    pc = wl.LLAMA2_7B_16K_SWA
+    p = pstate
+    out = torch.empty_like(p["q"])
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    log("windowed prefill timed")
+    ms = _event_ms(torch, lambda: ops.attn_prefill_fwd(p["q"], p["krot"], p["v"], p["cu"],
+                                                       p["maxlen"], p["theta"], p["scale"],
+                                                       out=out, want_lse=False, workspace=ws,
+                                                       k_rotated=True, window=pc.window,
+                                                       sinks=pc.sinks, stream=stream),
+                   args.warmup, args.steps, stream)
+    flops = wl.prefill_visible_flops(pc.seq_lens, pc.hq, pc.head_dim, pc.window, pc.sinks)
+    tf = flops / (ms * 1e-3) / 1e12
+    res["window_prefill"] = {
+        "metric": "windowed prefill TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
+        "ms_per_call": round(ms, 4), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+        "flops_per_launch": flops,
+        "config": {"workload": pc.name, "inputs": "those of the prefill line",
+                   "window": pc.window, "sinks": pc.sinks}}
+
+    if dstate is not None:
+        dc = wl.DECODE_B16_SWA
+        d = dstate
+        out = torch.empty_like(d["q"])
+        log("windowed decode timed")
+        ms = _event_ms(torch, lambda: ops.attn_decode(d["q"], d["kc"], d["vc"], d["sl"],
+                                                      d["theta"], d["scale"], out=out,
+                                                      want_lse=False, workspace=d["ws"],
+                                                      window=dc.window, sinks=dc.sinks,
+                                                      stream=stream),
+                       args.warmup, args.decode_steps, stream)
+        nbytes = wl.decode_visible_bytes(d["seqlens"], dc.hkv, dc.head_dim, dc.window, dc.sinks)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res["window_decode"] = {
+            "metric": "windowed decode KV GB/s", "value": round(gbs, 2), "unit": "GB/s",
+            "ms_per_call": round(ms, 4), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "bytes_per_launch": int(nbytes),
+            "config": {"workload": dc.name, "inputs": "those of the decode line",
+                       "window": dc.window, "sinks": dc.sinks}}
+    return res
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -421,6 +531,7 @@ def main():
     ap.add_argument("--workload", default="llama2_7b_prefill_16k")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize", default=None)
@@ -467,9 +578,12 @@ def main():
         torch.cuda.synchronize()
         line["copy_probe_bytes"] = {"read": a.numel() * 2, "written": b.numel() * 2}
         del a, b
+    dstate = None
     if not args.no_decode:
         dres, dstate = bench_decode(args, torch, ops, wl)
         line["decode"] = dres
+    if not args.no_next:
+        line["next"] = bench_next(args, torch, ops, wl, pstate, dstate)
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline(args.workload, pstate, wl, args.cpu_seconds)

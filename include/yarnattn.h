@@ -63,6 +63,7 @@ extern "C" {
 #define YR_DEVERR_CU_SEQLENS 1 /* cu_seqlens not 0 = c0 <= c1 <= ... <= cB = T, or a length > max_seqlen */
 #define YR_DEVERR_SEQLENS 2    /* a decode seqlens[b] outside [1, max_cache_len] */
 #define YR_DEVERR_QPOS 4       /* a decode q_pos[b] < 0                           */
+#define YR_DEVERR_CTX_LENS 8   /* a chunked-prefill ctx_lens[b] < 0 or ctx_lens[b] + n_b > max_cache_len */
 
 /* Bytes at the start of every workspace reserved for the device error word. */
 #define YR_WORKSPACE_HEADER_BYTES 256
@@ -151,6 +152,14 @@ size_t attn_prefill_workspace_bytes(long long T, int Hkv, int head_dim, int in_d
  * sums and output accumulators); no T x T score matrix is ever stored.
  * Pass softmax_scale = t / sqrt(head_dim) for YaRN.
  *
+ * Sliding window and sinks: with window = W > 0 a query at position m sees
+ * only keys at m-W+1 .. m ("Arch 03 -- Long Context", sliding-window slide:
+ * each token attends to the W most recent tokens), plus the first `sinks`
+ * positions ("Long context (engineering 100k+ tokens)", attention sinks:
+ * keep the first tokens and the last W).  window = 0 is plain causal
+ * attention (sinks then change nothing).  Key tiles outside the window and
+ * the sinks are skipped, so the work is O(T * (W + sinks)).
+ *
  *   q              device [T, Hq, head_dim], unrotated
  *   k, v           device [T, Hkv, head_dim], k unrotated
  *   in_dtype       YR_BF16 (bf16 MFMA path) or YR_F32 (fp32 path)
@@ -159,6 +168,7 @@ size_t attn_prefill_workspace_bytes(long long T, int Hkv, int head_dim, int in_d
  *   inv_freq_f64   device double[head_dim/2], or NULL when q and k are already
  *                  rotated
  *   flags          0, or YR_PREFILL_K_ROTATED
+ *   window, sinks  >= 0 (see above)
  *   out            device [T, Hq, head_dim] of out_dtype (YR_F32 or YR_BF16;
  *                  YR_F32 inputs require YR_F32 out)
  *   lse            device float[Hq, T] or NULL
@@ -170,8 +180,43 @@ size_t attn_prefill_workspace_bytes(long long T, int Hkv, int head_dim, int in_d
 int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
                      const int *cu_seqlens, int B, int max_seqlen, long long T,
                      int Hq, int Hkv, int head_dim, const double *inv_freq_f64,
-                     int flags, float softmax_scale, void *out, int out_dtype, float *lse,
-                     void *workspace, size_t workspace_bytes, void *stream);
+                     int flags, float softmax_scale, int window, int sinks, void *out,
+                     int out_dtype, float *lse, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/*
+ * attn_prefill_chunk -- prefill of new tokens against a per-sequence KV cache
+ * (chunked prefill: a long prompt fed in pieces, or new turns after a cached
+ * prefix; "Long context (engineering 100k+ tokens)", chunked prefill).
+ *
+ * Sequence b has ctx_lens[b] tokens cached before this chunk and n_b new ones
+ * (q rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1).  The caller has already
+ * written the chunk's rotated keys and its values into cache rows
+ * ctx_lens[b] .. ctx_lens[b] + n_b - 1 (e.g. rope_apply with those
+ * positions).  New token i sits at position ctx_lens[b] + i: q is rotated
+ * there and attends to cache rows 0 .. ctx_lens[b] + i (the causal boundary
+ * at the bottom-right of the chunk x cache block), with the window / sinks
+ * rule of attn_prefill_fwd.  Same kernels as attn_prefill_fwd.
+ *
+ *   q                device [Tq, Hq, head_dim], unrotated
+ *   k_cache,v_cache  device [B, max_cache_len, Hkv, head_dim] (in_dtype),
+ *                    keys rotated
+ *   cu_seqlens_q     device int32[B+1]: 0, c1, ..., cB = Tq; n_b <= max_seqlen_q
+ *   ctx_lens         device int32[B]: 0 <= ctx_lens[b] <= max_cache_len - n_b
+ *                    (violations are clamped and reported as
+ *                    YR_DEVERR_CTX_LENS)
+ *   max_seqlen_q     1 .. max_cache_len
+ *   inv_freq_f64     device double[head_dim/2], or NULL when q is rotated
+ *   out, lse         as attn_prefill_fwd ([Tq, Hq, head_dim], float[Hq, Tq])
+ *   workspace        device, 256-byte aligned, >= YR_WORKSPACE_HEADER_BYTES
+ *                    (holds the device error word)
+ */
+int attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cache, int in_dtype,
+                       const int *cu_seqlens_q, const int *ctx_lens, int B, int max_seqlen_q,
+                       long long Tq, int max_cache_len, int Hq, int Hkv, int head_dim,
+                       const double *inv_freq_f64, float softmax_scale, int window, int sinks,
+                       void *out, int out_dtype, float *lse, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /* Workspace bytes attn_decode needs for these sizes. */
 size_t attn_decode_workspace_bytes(int B, int max_cache_len, int Hq, int head_dim);
@@ -185,6 +230,12 @@ size_t attn_decode_workspace_bytes(int B, int max_cache_len, int Hq, int head_di
  * swept in fixed-size key chunks in parallel; each chunk yields a partial
  * (out, LSE) and the partials are merged by log-sum-exp ("Long-context
  * models", "Context parallelism distributes exact attention").
+ * With window = W > 0 only the cache rows the query's window and sinks make
+ * visible are read (rows > m - W, and rows < sinks, m = its position): the
+ * rest of the cache costs no bandwidth.  The new token's own row is not in
+ * the cache, so a one-token window without sinks would see nothing and is
+ * rejected; a query placed (by q_pos) past every visible row gets out = 0
+ * and lse = -inf.
  *
  *   q               device [B, Hq, head_dim] (in_dtype), unrotated
  *   k_cache,v_cache device [B, max_cache_len, Hkv, head_dim] (in_dtype)
@@ -196,6 +247,7 @@ size_t attn_decode_workspace_bytes(int B, int max_cache_len, int Hq, int head_di
  *   lse             device float[B, Hq] or NULL
  *   workspace       device, >= attn_decode_workspace_bytes(...) bytes,
  *                   256-byte aligned; holds the partials
+ *   window, sinks   >= 0; window == 1 needs sinks >= 1
  *   head_dim        64 or 128;  Hq % Hkv == 0;  Hq / Hkv <= 32 for YR_BF16
  *                   inputs, <= 16 for YR_F32 inputs
  * Returns YR_ERR_UNSUPPORTED beyond those limits, YR_ERR_WORKSPACE for a
@@ -205,8 +257,8 @@ size_t attn_decode_workspace_bytes(int B, int max_cache_len, int Hq, int head_di
 int attn_decode(const void *q, const void *k_cache, const void *v_cache,
                 int in_dtype, const int *seqlens, const int *q_pos, int B,
                 int max_cache_len, int Hq, int Hkv, int head_dim,
-                const double *inv_freq_f64, float softmax_scale, void *out,
-                int out_dtype, float *lse, void *workspace,
+                const double *inv_freq_f64, float softmax_scale, int window, int sinks,
+                void *out, int out_dtype, float *lse, void *workspace,
                 size_t workspace_bytes, void *stream);
 
 /*

@@ -31,7 +31,8 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert {"yarn_rope_freqs", "rope_apply", "rope_apply_packed", "attn_prefill_fwd", "attn_decode",
+    assert {"yarn_rope_freqs", "rope_apply", "rope_apply_packed", "attn_prefill_fwd",
+            "attn_prefill_chunk", "attn_decode",
             "attn_prefill_workspace_bytes", "attn_decode_workspace_bytes",
             "yr_read_device_error", "yr_status_string", "yr_last_error", "yr_version"} <= set(names)
     raw = ctypes.CDLL(ops.LIB_PATH)
@@ -95,13 +96,13 @@ WS = ctypes.c_void_p(1 << 20)     # 256-byte aligned fake workspace
 
 def prefill_call(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, in_dtype=ops.YR_BF16, cu=FAKE, B=1, max_seqlen=16, T=16,
-             Hq=4, Hkv=2, D=128, theta=FAKE, flags=0, scale=0.1, out=FAKE, out_dtype=ops.YR_BF16,
-             lse=FAKE, ws=WS, ws_bytes=1 << 30, stream=None)
+             Hq=4, Hkv=2, D=128, theta=FAKE, flags=0, scale=0.1, window=0, sinks=0, out=FAKE,
+             out_dtype=ops.YR_BF16, lse=FAKE, ws=WS, ws_bytes=1 << 30, stream=None)
     a.update(kw)
     return lib.attn_prefill_fwd(a["q"], a["k"], a["v"], a["in_dtype"], a["cu"], a["B"],
                                 a["max_seqlen"], a["T"], a["Hq"], a["Hkv"], a["D"], a["theta"],
-                                a["flags"], a["scale"], a["out"], a["out_dtype"], a["lse"], a["ws"],
-                                a["ws_bytes"], a["stream"])
+                                a["flags"], a["scale"], a["window"], a["sinks"], a["out"],
+                                a["out_dtype"], a["lse"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -125,21 +126,55 @@ def prefill_call(lib, **kw):
     (dict(T=1 << 20, ws_bytes=(1 << 20) * 2 * 128 * 2), ops.YR_ERR_WORKSPACE),
     (dict(flags=2), ops.YR_ERR_INVALID),
     (dict(flags=ops.YR_PREFILL_K_ROTATED, ws_bytes=255), ops.YR_ERR_WORKSPACE),
+    (dict(window=-1), ops.YR_ERR_INVALID),
+    (dict(sinks=-4), ops.YR_ERR_INVALID),
 ])
 def test_prefill_rejects_before_launch(lib, kw, status):
     assert prefill_call(lib, **kw) == status
     assert lib.yr_last_error()
 
 
+def chunk_call(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, in_dtype=ops.YR_BF16, cu=FAKE, ctx=FAKE, B=2,
+             max_seqlen=64, Tq=100, Lmax=1024, Hq=8, Hkv=2, D=128, theta=FAKE, scale=0.1, window=0,
+             sinks=0, out=FAKE, out_dtype=ops.YR_BF16, lse=FAKE, ws=WS, ws_bytes=256, stream=None)
+    a.update(kw)
+    return lib.attn_prefill_chunk(a["q"], a["kc"], a["vc"], a["in_dtype"], a["cu"], a["ctx"],
+                                  a["B"], a["max_seqlen"], a["Tq"], a["Lmax"], a["Hq"], a["Hkv"],
+                                  a["D"], a["theta"], a["scale"], a["window"], a["sinks"],
+                                  a["out"], a["out_dtype"], a["lse"], a["ws"], a["ws_bytes"],
+                                  a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=80), ops.YR_ERR_UNSUPPORTED),
+    (dict(Hq=8, Hkv=3), ops.YR_ERR_INVALID),
+    (dict(max_seqlen=2048, Lmax=1024), ops.YR_ERR_INVALID),   # a chunk must fit the cache
+    (dict(max_seqlen=0), ops.YR_ERR_INVALID),
+    (dict(B=0), ops.YR_ERR_INVALID),
+    (dict(Tq=-1), ops.YR_ERR_INVALID),
+    (dict(scale=-1.0), ops.YR_ERR_INVALID),
+    (dict(window=-2), ops.YR_ERR_INVALID),
+    (dict(in_dtype=ops.YR_F32, out_dtype=ops.YR_BF16), ops.YR_ERR_UNSUPPORTED),
+    (dict(ctx=None), ops.YR_ERR_NULL),
+    (dict(kc=None), ops.YR_ERR_NULL),
+    (dict(ws_bytes=128), ops.YR_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 64)), ops.YR_ERR_WORKSPACE),
+])
+def test_chunk_rejects_before_launch(lib, kw, status):
+    assert chunk_call(lib, **kw) == status
+    assert lib.yr_last_error()
+
+
 def decode_call(lib, **kw):
     a = dict(q=FAKE, kc=FAKE, vc=FAKE, in_dtype=ops.YR_BF16, seqlens=FAKE, qpos=None, B=2,
-             Lmax=1024, Hq=8, Hkv=2, D=128, theta=FAKE, scale=0.1, out=FAKE,
+             Lmax=1024, Hq=8, Hkv=2, D=128, theta=FAKE, scale=0.1, window=0, sinks=0, out=FAKE,
              out_dtype=ops.YR_BF16, lse=FAKE, ws=WS, ws_bytes=1 << 30, stream=None)
     a.update(kw)
     return lib.attn_decode(a["q"], a["kc"], a["vc"], a["in_dtype"], a["seqlens"], a["qpos"],
                            a["B"], a["Lmax"], a["Hq"], a["Hkv"], a["D"], a["theta"], a["scale"],
-                           a["out"], a["out_dtype"], a["lse"], a["ws"], a["ws_bytes"],
-                           a["stream"])
+                           a["window"], a["sinks"], a["out"], a["out_dtype"], a["lse"], a["ws"],
+                           a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -155,6 +190,8 @@ def decode_call(lib, **kw):
     (dict(kc=None), ops.YR_ERR_NULL),
     (dict(ws_bytes=512), ops.YR_ERR_WORKSPACE),
     (dict(ws=ctypes.c_void_p((1 << 20) + 8)), ops.YR_ERR_WORKSPACE),
+    (dict(window=-1), ops.YR_ERR_INVALID),
+    (dict(window=1), ops.YR_ERR_INVALID),            # a one-token window sees no cache row
 ])
 def test_decode_rejects_before_launch(lib, kw, status):
     assert decode_call(lib, **kw) == status
@@ -186,3 +223,15 @@ def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "_lib", None)
     with pytest.raises(ops.YarnAttnError):
         ops.load_library(str(tmp_path / "nope.so"))
+
+
+def test_binding_constants_match_header():
+    text = open(HEADER).read()
+    macros = dict(re.findall(r"^#define\s+(YR_\w+)\s+(\d+)", text, flags=re.M))
+    assert len(macros) >= 15
+    for name, value in macros.items():
+        if hasattr(ops, name):
+            assert getattr(ops, name) == int(value), name
+    for name in ("YR_OK", "YR_F32", "YR_BF16", "YR_PREFILL_K_ROTATED", "YR_DEVERR_CU_SEQLENS",
+                 "YR_DEVERR_SEQLENS", "YR_DEVERR_QPOS", "YR_DEVERR_CTX_LENS"):
+        assert name in macros and hasattr(ops, name), name

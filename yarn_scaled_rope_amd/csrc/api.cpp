@@ -119,8 +119,8 @@ size_t attn_prefill_workspace_bytes(long long T, int Hkv, int head_dim, int in_d
 int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
                      const int *cu_seqlens, int B, int max_seqlen, long long T, int Hq, int Hkv,
                      int head_dim, const double *inv_freq_f64, int flags, float softmax_scale,
-                     void *out, int out_dtype, float *lse, void *workspace, size_t workspace_bytes,
-                     void *stream) {
+                     int window, int sinks, void *out, int out_dtype, float *lse, void *workspace,
+                     size_t workspace_bytes, void *stream) {
   if (flags & ~YR_PREFILL_K_ROTATED) return fail(YR_ERR_INVALID, "attn_prefill_fwd: unknown flags");
   if (in_dtype != YR_F32 && in_dtype != YR_BF16)
     return fail(YR_ERR_UNSUPPORTED, "attn_prefill_fwd: in_dtype must be YR_F32 or YR_BF16");
@@ -137,6 +137,7 @@ int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
     return fail(YR_ERR_INVALID, "attn_prefill_fwd: max_seqlen or T too large");
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
     return fail(YR_ERR_INVALID, "attn_prefill_fwd: softmax_scale must be finite and > 0");
+  if (window < 0 || sinks < 0) return fail(YR_ERR_INVALID, "attn_prefill_fwd: window and sinks must be >= 0");
   if (!q || !k || !v || !cu_seqlens || !out || !workspace)
     return fail(YR_ERR_NULL, "attn_prefill_fwd: q, k, v, cu_seqlens, out and workspace are required");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
@@ -168,6 +169,10 @@ int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
   p.out_dtype = out_dtype;
   p.lse = lse;
   p.dev_flag = flag;
+  p.kv_cache_len = 0;
+  p.ctx_lens = nullptr;
+  p.window = window;
+  p.sinks = sinks;
 
   if (key_pass && T > 0) {
     // rotate every key once into the workspace; the attention kernel rotates
@@ -197,6 +202,67 @@ int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
   return YR_OK;
 }
 
+int attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cache, int in_dtype,
+                       const int *cu_seqlens_q, const int *ctx_lens, int B, int max_seqlen_q,
+                       long long Tq, int max_cache_len, int Hq, int Hkv, int head_dim,
+                       const double *inv_freq_f64, float softmax_scale, int window, int sinks,
+                       void *out, int out_dtype, float *lse, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+  if (in_dtype != YR_F32 && in_dtype != YR_BF16)
+    return fail(YR_ERR_UNSUPPORTED, "attn_prefill_chunk: in_dtype must be YR_F32 or YR_BF16");
+  if (out_dtype != YR_F32 && out_dtype != YR_BF16)
+    return fail(YR_ERR_UNSUPPORTED, "attn_prefill_chunk: out_dtype must be YR_F32 or YR_BF16");
+  if (in_dtype == YR_F32 && out_dtype != YR_F32)
+    return fail(YR_ERR_UNSUPPORTED, "attn_prefill_chunk: fp32 inputs need fp32 output");
+  if (!dims_ok(head_dim)) return fail(YR_ERR_UNSUPPORTED, "attn_prefill_chunk: head_dim must be 64 or 128");
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return fail(YR_ERR_INVALID, "attn_prefill_chunk: need Hq >= 1, Hkv >= 1, Hq % Hkv == 0");
+  if (B < 1 || Tq < 0 || max_seqlen_q < 1 || max_cache_len < max_seqlen_q)
+    return fail(YR_ERR_INVALID,
+                "attn_prefill_chunk: need B >= 1, Tq >= 0, 1 <= max_seqlen_q <= max_cache_len");
+  if (max_cache_len > (1 << 24) || Tq > (1LL << 31) - 1 ||
+      (long long)B * max_cache_len > (1LL << 34))
+    return fail(YR_ERR_INVALID, "attn_prefill_chunk: sizes too large");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(YR_ERR_INVALID, "attn_prefill_chunk: softmax_scale must be finite and > 0");
+  if (window < 0 || sinks < 0) return fail(YR_ERR_INVALID, "attn_prefill_chunk: window and sinks must be >= 0");
+  if (!q || !k_cache || !v_cache || !cu_seqlens_q || !ctx_lens || !out || !workspace)
+    return fail(YR_ERR_NULL, "attn_prefill_chunk: q, caches, cu_seqlens_q, ctx_lens, out and "
+                             "workspace are required");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return fail(YR_ERR_WORKSPACE, "attn_prefill_chunk: workspace must be 256-byte aligned");
+  if (workspace_bytes < kHeader) return fail(YR_ERR_WORKSPACE, "attn_prefill_chunk: workspace too small");
+  const long long ntiles = (max_seqlen_q + 63) / 64;
+  if (ntiles * (long long)B * Hq > 0x7fffffffLL)
+    return fail(YR_ERR_INVALID, "attn_prefill_chunk: grid too large");
+  PrefillArgs p{};
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.in_dtype = in_dtype;
+  p.cu_seqlens = cu_seqlens_q;
+  p.B = B;
+  p.max_seqlen = max_seqlen_q;
+  p.T = Tq;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.head_dim = head_dim;
+  p.theta = inv_freq_f64;
+  p.softmax_scale = softmax_scale;
+  p.out = out;
+  p.out_dtype = out_dtype;
+  p.lse = lse;
+  p.dev_flag = flag_of(workspace);
+  p.kv_cache_len = max_cache_len;
+  p.ctx_lens = ctx_lens;
+  p.window = window;
+  p.sinks = sinks;
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = in_dtype == YR_F32 ? launch_prefill_f32(p, s) : launch_prefill_bf16(p, s);
+  if (e != hipSuccess) return fail_hip(e, "attn_prefill_chunk");
+  return YR_OK;
+}
+
 size_t attn_decode_workspace_bytes(int B, int max_cache_len, int Hq, int head_dim) {
   if (B < 1 || max_cache_len < 1 || Hq < 1 || head_dim < 1) return kHeader;
   // chunking depends on Hkv only through the split count heuristic; size for
@@ -209,9 +275,9 @@ size_t attn_decode_workspace_bytes(int B, int max_cache_len, int Hq, int head_di
 
 int attn_decode(const void *q, const void *k_cache, const void *v_cache, int in_dtype,
                 const int *seqlens, const int *q_pos, int B, int max_cache_len, int Hq, int Hkv,
-                int head_dim, const double *inv_freq_f64, float softmax_scale, void *out,
-                int out_dtype, float *lse, void *workspace, size_t workspace_bytes,
-                void *stream) {
+                int head_dim, const double *inv_freq_f64, float softmax_scale, int window,
+                int sinks, void *out, int out_dtype, float *lse, void *workspace,
+                size_t workspace_bytes, void *stream) {
   if (in_dtype != YR_F32 && in_dtype != YR_BF16)
     return fail(YR_ERR_UNSUPPORTED, "attn_decode: in_dtype must be YR_F32 or YR_BF16");
   if (out_dtype != YR_F32 && out_dtype != YR_BF16)
@@ -227,6 +293,9 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, int in_
     return fail(YR_ERR_INVALID, "attn_decode: cache too large");
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
     return fail(YR_ERR_INVALID, "attn_decode: softmax_scale must be finite and > 0");
+  if (window < 0 || sinks < 0) return fail(YR_ERR_INVALID, "attn_decode: window and sinks must be >= 0");
+  if (window == 1 && sinks == 0)
+    return fail(YR_ERR_INVALID, "attn_decode: a one-token window without sinks sees no cache row");
   if (!q || !k_cache || !v_cache || !seqlens || !out || !workspace)
     return fail(YR_ERR_NULL, "attn_decode: q, caches, seqlens, out and workspace are required");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
@@ -261,6 +330,8 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, int in_
   d.chunk = chunk;
   d.nsplit = nsplit;
   d.dev_flag = flag_of(workspace);
+  d.window = window;
+  d.sinks = sinks;
   const hipError_t e = launch_decode(d, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "attn_decode");
   return YR_OK;

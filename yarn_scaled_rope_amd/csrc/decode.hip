@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const T *__restrict__ q, const T *__restrict__ kc, const T *__restrict__ vc,
     const int *__restrict__ seqlens, const int *__restrict__ qpos, int B, int Lmax, int Hq,
     int Hkv, const double *__restrict__ theta, float scale_log2, int chunk, int nsplit,
-    float *__restrict__ part_o, float *__restrict__ part_lse, int *flag) {
+    float *__restrict__ part_o, float *__restrict__ part_lse, int *flag, int window, int sinks) {
   constexpr int LPK = D / 8;         // lanes per key row
   constexpr int GPW = 64 / LPK;      // key rows per wave load
   constexpr int KPW = GPW * kUnroll; // keys per wave per iteration
@@ -135,6 +135,24 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   const int c0 = split * chunk;
   if (c0 >= L) return;
   const int c1 = min(L, c0 + chunk);
+  int qm = qpos != nullptr ? qpos[b] : L;  // the query's position
+  qm = qm < 0 ? 0 : qm;
+  // visible cache rows: the sinks [0, se) and the window [lo, L)
+  int lo = 0, se = 0;
+  if (window > 0) {
+    lo = max(0, qm - window + 1);
+    se = min(sinks, lo);
+  }
+  if (!(c0 < se || max(c0, lo) < c1)) {
+    // nothing visible in this chunk: an empty partial (weight 0 in the merge)
+    for (int idx = threadIdx.x; idx < g * D; idx += kThreads) {
+      const int gi = idx / D, d = idx % D;
+      const long long row = ((long long)b * Hq + hk * g + gi) * nsplit + split;
+      part_o[row * D + d] = 0.f;
+      if (d == 0) part_lse[row] = -INFINITY;
+    }
+    return;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -147,14 +165,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   // angle of a pair is the same for every head of the group
   float qv[GM][8];
   {
-    int m = qpos != nullptr ? qpos[b] : L;
-    m = m < 0 ? 0 : m;
     float cs[4], sn[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       cs[e] = 1.f;
       sn[e] = 0.f;
-      if (theta != nullptr) rope_cos_sin((double)m, theta[(d0 >> 1) + e], &cs[e], &sn[e]);
+      if (theta != nullptr) rope_cos_sin((double)qm, theta[(d0 >> 1) + e], &cs[e], &sn[e]);
     }
 #pragma unroll
     for (int gi = 0; gi < GM; ++gi) {
@@ -193,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int key = base + u * GPW + grp;
-      ok[u] = key < c1;
+      ok[u] = key < c1 && (window == 0 || key >= lo || key < se);
       kr[u] = ok[u] ? Row8<T>::load(kb + key * rstride) : Row8<T>::zero();
       vr[u] = ok[u] ? Row8<T>::load(vb + key * rstride) : Row8<T>::zero();
     }
@@ -410,7 +426,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     const uint16_t *__restrict__ vc, const int *__restrict__ seqlens,
     const int *__restrict__ qpos, int B, int Lmax, int Hq, int Hkv,
     const double *__restrict__ theta, float scale_log2, int chunk, int nsplit,
-    float *__restrict__ part_o, float *__restrict__ part_lse, int *flag) {
+    float *__restrict__ part_o, float *__restrict__ part_lse, int *flag, int window, int sinks) {
   constexpr int CH = D / 8;        // 16-byte chunks per row
   constexpr int H = D / 16;        // DMA instructions per K or V block (1 KB each)
   constexpr int RPI = 64 / CH;     // rows per DMA instruction
@@ -432,18 +448,48 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
   const int c0 = split * chunk;
   if (c0 >= L) return;
-  const int n = min(L, c0 + chunk) - c0;  // keys of this chunk
+  const int c1 = min(L, c0 + chunk);
+  int qm = qpos != nullptr ? qpos[b] : L;  // the query's position
+  qm = qm < 0 ? 0 : qm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
+  const int gc = min(g, 32);
+
+  // Visible cache rows: the sinks [0, se) and the window [lo, L) (no window:
+  // all of [0, L)).  This chunk sweeps its share of each as 32-key blocks:
+  // blocks 0 .. nba-1 cover [c0, c0 + na), the rest cover [b0, b0 + nb).
+  int lo = 0, se = 0;
+  if (window > 0) {
+    lo = max(0, qm - window + 1);
+    se = min(sinks, lo);
+  }
+  const int na = max(0, min(c1, se) - c0);
+  const int b0 = max(c0, lo);
+  const int nb = max(0, c1 - b0);
+  const int nba = (na + kBlk - 1) / kBlk;
+  const int nblk = nba + (nb + kBlk - 1) / kBlk;
+  if (nblk == 0) {
+    // nothing visible here: an empty partial (weight 0 in the merge)
+    for (int idx = tid; idx < gc * D; idx += NT) {
+      const int gi = idx / D, d = idx % D;
+      const long long row = ((long long)b * Hq + hk * g + gi) * nsplit + split;
+      part_o[row * D + d] = 0.f;
+      if (d == 0) part_lse[row] = -INFINITY;
+    }
+    return;
+  }
+  auto blk_start = [&](int gb) { return gb < nba ? c0 + gb * kBlk : b0 + (gb - nba) * kBlk; };
+  auto blk_rows = [&](int gb) {
+    return gb < nba ? min(kBlk, na - gb * kBlk) : min(kBlk, nb - (gb - nba) * kBlk);
+  };
 
   const long long rstride = (long long)Hkv * D;  // elements between keys
-  const uint16_t *kbase = kc + (((long long)b * Lmax + c0) * Hkv + hk) * D;
-  const uint16_t *vbase = vc + (((long long)b * Lmax + c0) * Hkv + hk) * D;
-  const int nblk = (n + kBlk - 1) / kBlk;
+  const uint16_t *kbase = kc + ((long long)b * Lmax * Hkv + hk) * D;
+  const uint16_t *vbase = vc + ((long long)b * Lmax * Hkv + hk) * D;
   const int nmine = nblk > wave ? (nblk - wave + W - 1) / W : 0;  // blocks of this wave
 
   // DMA lane mapping: instruction p of a block fills LDS bytes [1024p, 1024p+1024)
@@ -460,10 +506,10 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
   }
   const uint32_t pstride = (uint32_t)(RPI * rstride * 2);
 
-  // t-th block of this wave -> stage; keys past the chunk read 0
+  // t-th block of this wave -> stage; rows past the block's share read 0
   auto issue = [&](int t, int stage, int which) {
-    const int key0 = (wave + t * W) * kBlk;
-    const int rows = min(kBlk, n - key0);
+    const int key0 = blk_start(wave + t * W);
+    const int rows = blk_rows(wave + t * W);
     const uint32_t bytes = (uint32_t)(((rows - 1) * rstride + D) * 2);
     const uint16_t *src = (which == 0 ? kbase : vbase) + key0 * rstride;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, bytes);
@@ -486,16 +532,13 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
   // ---- query heads of the group: rotate at the new token's position, round
   // to bf16, one head per row of qt (rows past the group stay zero)
   {
-    int m = qpos != nullptr ? qpos[b] : L;
-    m = m < 0 ? 0 : m;
     for (int i = tid; i < D / 2; i += NT) {
       float c = 1.f, s = 0.f;
-      if (theta != nullptr) rope_cos_sin((double)m, theta[i], &c, &s);
+      if (theta != nullptr) rope_cos_sin((double)qm, theta[i], &c, &s);
       sm.cs[i] = c;
       sm.sn[i] = s;
     }
     __syncthreads();
-    const int gc = min(g, 32);
     for (int idx = tid; idx < 32 * (D / 2); idx += NT) {
       const int col = idx / (D / 2), pr = idx % (D / 2);
       float x0 = 0.f, x1 = 0.f;
@@ -543,7 +586,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
 
   auto block = [&](int t, auto stage_c) {
     constexpr int S = decltype(stage_c)::value;
-    const int key0 = (wave + t * W) * kBlk;
+    const int rows = blk_rows(wave + t * W);
     const int ahead = min(NB - 1, nmine - 1 - t);  // later blocks already issued
     const bool refill = t + NB < nmine;
 
@@ -563,11 +606,11 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     }
 
     // online softmax of the column (query head) l32 over this block
-    if (key0 + kBlk > n) {
+    if (rows < kBlk) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int key = key0 + 8 * (e >> 2) + 4 * hh + (e & 3);
-        sc[e] = key < n ? sc[e] : -INFINITY;
+        const int r = 8 * (e >> 2) + 4 * hh + (e & 3);
+        sc[e] = r < rows ? sc[e] : -INFINITY;
       }
     }
     float mx = sc[0];
@@ -632,7 +675,6 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
   // the waves, through LDS (the ring is free once every wave is here)
   lsum += __shfl_xor(lsum, 32);
   __syncthreads();
-  const int gc = min(g, 32);
   if (l32 < gc) {
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
@@ -688,6 +730,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   for (int p = lane; p < nv; p += 64) M = fmaxf(M, part_lse[row0 + p]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  // no visible key in any chunk (a query placed past its window): empty result
+  const bool none = nv == 0 || M == -INFINITY;
+  if (none) M = 0.f;
 
   float num[PER], den = 0.f;
 #pragma unroll
@@ -729,14 +774,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     float t = 0.f;
 #pragma unroll
     for (int w = 0; w < MW; ++w) t += sm_num[w][lane + 64 * i];
-    const float y = nv > 0 ? t / den : 0.f;
+    const float y = none ? 0.f : t / den;
     if (OUT_F32)
       ((float *)out)[orow + lane + 64 * i] = y;
     else
       ((uint16_t *)out)[orow + lane + 64 * i] = (uint16_t)f32_to_bf16(y);
   }
   if (lse != nullptr && lane == 0)
-    lse[(long long)b * Hq + h] = nv > 0 ? (M + __log2f(den)) * kLn2 : -INFINITY;
+    lse[(long long)b * Hq + h] = none ? -INFINITY : (M + __log2f(den)) * kLn2;
 }
 
 template <typename T, int D, int GM>
@@ -746,7 +791,7 @@ hipError_t launch_split(const DecodeArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((decode_split_kernel<T, D, GM>), dim3((unsigned)blocks), dim3(kThreads), 0,
                      s, (const T *)a.q, (const T *)a.k_cache, (const T *)a.v_cache, a.seqlens,
                      a.q_pos, a.B, a.max_cache_len, a.Hq, a.Hkv, a.theta, scale_log2, a.chunk,
-                     a.nsplit, a.part_o, a.part_lse, a.dev_flag);
+                     a.nsplit, a.part_o, a.part_lse, a.dev_flag, a.window, a.sinks);
   return hipGetLastError();
 }
 
@@ -769,7 +814,7 @@ hipError_t launch_mfma(const DecodeArgs &a, hipStream_t s) {
                      (const uint16_t *)a.q, (const uint16_t *)a.k_cache,
                      (const uint16_t *)a.v_cache, a.seqlens, a.q_pos, a.B, a.max_cache_len, a.Hq,
                      a.Hkv, a.theta, scale_log2, a.chunk, a.nsplit, a.part_o, a.part_lse,
-                     a.dev_flag);
+                     a.dev_flag, a.window, a.sinks);
   return hipGetLastError();
 }
 

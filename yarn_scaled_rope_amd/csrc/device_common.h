@@ -78,10 +78,12 @@ __device__ __forceinline__ void seq_bounds(const int *__restrict__ cu, int b, lo
   *len = (int)n;
 }
 
-// Check cu_seqlens (one workgroup, all threads call it; thread 0 writes the
-// error word).
+// Check cu_seqlens and, for chunked prefill, ctx_lens (one workgroup, all
+// threads call it; thread 0 writes the error word).
 __device__ inline void validate_cu_seqlens(const int *__restrict__ cu, int B, long long T,
-                                           int max_seqlen, int *flag) {
+                                           int max_seqlen, int *flag,
+                                           const int *__restrict__ ctx = nullptr,
+                                           int max_cache_len = 0) {
   __shared__ int bad;
   if (threadIdx.x == 0) bad = 0;
   __syncthreads();
@@ -93,6 +95,10 @@ __device__ inline void validate_cu_seqlens(const int *__restrict__ cu, int B, lo
     if (b > 0) {
       const long long p = cu[b - 1];
       if (c < p || c - p > max_seqlen) e = 1;
+      if (ctx != nullptr) {
+        const long long x = ctx[b - 1];
+        if (x < 0 || x + (c - p) > max_cache_len) atomicOr(&bad, YR_DEVERR_CTX_LENS);
+      }
     }
     if (e) atomicOr(&bad, YR_DEVERR_CU_SEQLENS);
   }

@@ -90,7 +90,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int *__restrict__ cu, int B, int max_seqlen,
     long long T, int Hq, int Hkv, const double *__restrict__ theta, float scale_log2,
-    void *__restrict__ out, float *__restrict__ lse, int ntiles, int *flag) {
+    void *__restrict__ out, float *__restrict__ lse, int ntiles, int *flag, int kv_len,
+    const int *__restrict__ ctx, int window, int sinks) {
   constexpr int KSTEPS = D / 16;     // MFMA k-steps over the head dim
   constexpr int DBLK = D / 32;       // 32-row blocks of O^T
   constexpr int CH = D / 8;          // 16-byte chunks per row
@@ -106,7 +107,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   __shared__ __align__(16) uint16_t sk0[TILE], sk1[TILE], sk2[TILE3];
   __shared__ __align__(16) uint16_t sv0[TILE], sv1[TILE], sv2[TILE3];
 
-  if (flag != nullptr && blockIdx.x == 0) validate_cu_seqlens(cu, B, T, max_seqlen, flag);
+  if (flag != nullptr && blockIdx.x == 0)
+    validate_cu_seqlens(cu, B, T, max_seqlen, flag, kv_len > 0 ? ctx : nullptr, kv_len);
 
   // ---- block -> (q-tile, sequence, head): longest first, XCD-grouped heads
   const int per = B * Hq;
@@ -136,14 +138,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   const int tw0 = q0 + wave * 32;  // first query row of this wave
   const int tq = tw0 + l32;        // this lane's query row
 
+  // Keys: packed like q (kv_len == 0), or a [B, kv_len, Hkv, D] cache whose
+  // first P rows precede this chunk: query row i then sits at position P + i
+  // and sees cache rows up to P + i.  Positions below are cache rows.
+  const long long rstride = (long long)Hkv * D;  // elements between key rows
+  int P = 0;
+  long long krow0 = s0;
+  if (kv_len > 0) {
+    P = ctx != nullptr ? ctx[b] : 0;
+    P = P < 0 ? 0 : (P > kv_len - n ? kv_len - n : P);
+    P = __builtin_amdgcn_readfirstlane(P);
+    krow0 = (long long)b * kv_len;
+  }
+  const int nk = P + n;  // key rows of the sequence
+
   // ---- tile copies HBM -> LDS (buffer_load ... lds, no registers) ---------
   // Copy instruction p of a tile fills LDS bytes [1024p, 1024p + 1024) in lane
   // order: lane l lands on row p*RPI + l/CH, slot l%CH, so it fetches the
   // source chunk that belongs in that slot.  K: slot = chunk ^ (row % CH);
   // V: slot = chunk ^ vswz(row % 4).  Rows past the sequence end read 0.
-  const long long rstride = (long long)Hkv * D;  // elements between key rows
-  const uint16_t *kseq = k + (s0 * Hkv + hk) * (long long)D;
-  const uint16_t *vseq = v + (s0 * Hkv + hk) * (long long)D;
+  const uint16_t *kseq = k + (krow0 * Hkv + hk) * (long long)D;
+  const uint16_t *vseq = v + (krow0 * Hkv + hk) * (long long)D;
   const uint32_t rbytes = (uint32_t)(rstride * 2);
   const int drow = lane / CH, dslot = lane % CH;
   uint32_t koff[DPW];
@@ -156,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   auto copy_tile = [&](uint16_t *dst, const uint16_t *seq, int t, bool is_v) YR_INLINE {
     const int key0 = t * kBC;
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(seq + key0 * rstride, (uint32_t)min(kBC, n - key0) * rbytes);
+        make_rsrc(seq + key0 * rstride, (uint32_t)min(kBC, nk - key0) * rbytes);
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int p = wave * DPW + i;
@@ -174,13 +189,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     constexpr int P = decltype(par)::value;
     if constexpr (P == 0) return sv0; else if constexpr (P == 1) return sv1; else return sv2;
   };
-  const int last = (qend - 1) / kBC;
-  // prologue copies (K of tiles 0..NS-1, V of tiles 0..NS-2) go out before
-  // the query work so that they are in flight meanwhile
+  // Key tiles the workgroup visits, as a list: the sink tiles [0, js), then
+  // the tiles [jw, last] from the window start of its first row to the
+  // diagonal of its last row (without a window: every tile 0..last).
+  const int last = (P + qend - 1) / kBC;
+  int js = 0, jw = 0;
+  if (window > 0) {
+    const int lo = max(0, P + q0 - window + 1);
+    jw = lo / kBC;
+    js = min((min(sinks, lo) + kBC - 1) / kBC, jw);
+  }
+  const int count = js + (last - jw + 1);
+  auto tile_of = [&](int i) YR_INLINE { return i < js ? i : jw + (i - js); };
+  // prologue copies (K of tiles 0..NS-1, V of tiles 0..NS-2 of the list) go
+  // out before the query work so that they are in flight meanwhile
   static_for<0, NS>([&](auto ic) YR_INLINE {
     constexpr int I = decltype(ic)::value;
-    if (I <= last) copy_tile(kst(ic), kseq, I, false);
-    if (I + 1 < NS && I <= last) copy_tile(vst(ic), vseq, I, true);
+    if (I < count) copy_tile(kst(ic), kseq, tile_of(I), false);
+    if (I + 1 < NS && I < count) copy_tile(vst(ic), vseq, tile_of(I), true);
   });
 
   // ---- Q fragments (B operand of S^T = K Q^T), rotated on load -----------
@@ -198,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
           for (int e = 0; e < 4; ++e) {
             float x0 = bf16_to_f32(w[e] & 0xffffu), x1 = bf16_to_f32(w[e] >> 16);
             float c, s;
-            rope_cos_sin((double)tq, theta[kk * 8 + hh * 4 + e], &c, &s);
+            rope_cos_sin((double)(P + tq), theta[kk * 8 + hh * 4 + e], &c, &s);
             rotate_pair(x0, x1, c, s);
             w[e] = pack_bf16x2(x0, x1);
           }
@@ -231,9 +257,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   }
 
   // ---- per-tile work -------------------------------------------------------
-  // tile j has keys j*64 .. j*64+63; it is wholly above this wave's diagonal
-  // when its first key is past the wave's last query row
-  auto active = [&](int j) YR_INLINE { return j * kBC <= tw0 + 31 && tw0 < n; };
+  // Tile j has keys j*64 .. j*64+63.  The wave (rows tw0 .. tw0+31, positions
+  // P + row) skips it when it lies wholly above the wave's diagonal, or, with
+  // a window, wholly below the window of the wave's first row and past the
+  // sinks.
+  auto active = [&](int j) YR_INLINE {
+    if (tw0 >= n || j * kBC > P + tw0 + 31) return false;
+    return window == 0 || j * kBC + kBC - 1 > P + tw0 - window || j * kBC < sinks;
+  };
 
   // S^T = K Q^T for one tile (two 32-key blocks); accumulator slot rr of block
   // kb (lane half hh) holds key 32 kb + 8 (rr >> 2) + 4 hh + (rr & 3)
@@ -255,13 +286,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   // lazy rescale of the running state; returns -m for the exp2 argument
   auto softmax_front = [&](int j, f32x16 (&s)[2], bool may_mask) YR_INLINE -> float {
     const int key0 = j * kBC;
-    if (may_mask && ((key0 + kBC - 1 > tw0) || (key0 + kBC > n))) {
+    const bool wmask = window > 0 && key0 <= P + tw0 + 31 - window && key0 + kBC > sinks;
+    if (may_mask && ((key0 + kBC - 1 > P + tw0) || (key0 + kBC > nk) || wmask)) {
+      const int pos = P + tq;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           const int key = key0 + kb * 32 + (rr >> 2) * 8 + hh * 4 + (rr & 3);
-          if (key > tq || key >= n) s[kb][rr] = -INFINITY;
+          const bool hide = key > pos || key >= nk ||
+                            (window > 0 && key <= pos - window && key >= sinks);
+          if (hide) s[kb][rr] = -INFINITY;
         }
       }
     }
@@ -275,7 +310,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const bool grow = mx > m_run + 8.0f;                 // lazy running max
     if (__any(grow)) {
       const float m_new = grow ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+      // 0 when m_run = -inf; 1 for a row that has seen no visible key yet
+      // (with a window a row can meet tiles it does not see at all)
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_part *= alpha;
 #pragma unroll
@@ -320,59 +357,62 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     }
   };
 
-  // One pipeline step j (stage par = j % NS): after the barrier the K stage
-  // of tile j (read by the scores of step j-1) and the V stage of tile j-1
-  // are free; copy K(j+NS) and V(j+NS-1) into them, then run the score MFMAs
-  // of tile j+1 alongside the softmax of tile j, then the PV MFMAs of tile j.
-  // Before the barrier each wave waits for its own copies of K(j+1) and V(j),
-  // issued NS-1 steps earlier; the copies of the last NS-2 steps may still be
-  // in flight.
+  // One pipeline step i over the tile list (stage par = i % NS; tile(i) is
+  // the list's i-th tile): after the barrier the K stage of tile(i) (read by
+  // the scores of step i-1) and the V stage of tile(i-1) are free; copy
+  // K(tile(i+NS)) and V(tile(i+NS-1)) into them, then run the score MFMAs of
+  // tile(i+1) alongside the softmax of tile(i), then the PV MFMAs of tile(i).
+  // Before the barrier each wave waits for its own copies of K(tile(i+1)) and
+  // V(tile(i)), issued NS-1 steps earlier; the copies of the last NS-2 steps
+  // may still be in flight.
   auto nextp = [](auto par) YR_INLINE { return std::integral_constant<int, (decltype(par)::value + 1) % NS>{}; };
   auto prevp = [](auto par) YR_INLINE { return std::integral_constant<int, (decltype(par)::value + NS - 1) % NS>{}; };
-  auto stage = [&](auto par, int j) YR_INLINE {
+  auto stage = [&](auto par, int i) YR_INLINE {
     if constexpr (NS == 2) {
       wait_dma<0>();
     } else {
-      // copies issued by step j-1: K(j+2) and V(j+1) when those tiles exist
-      const int pending = (j >= 1 && j + 2 <= last ? 1 : 0) + (j >= 1 && j + 1 <= last ? 1 : 0);
+      // copies issued by step i-1: K(tile(i+2)) and V(tile(i+1)) when they exist
+      const int pending = (i >= 1 && i + 2 < count ? 1 : 0) + (i >= 1 && i + 1 < count ? 1 : 0);
       if (pending == 2) wait_dma<2 * DPW>();
       else if (pending == 1) wait_dma<DPW>();
       else wait_dma<0>();
     }
     __syncthreads();
-    if (j + NS <= last) copy_tile(kst(par), kseq, j + NS, false);
-    if (j + NS - 1 <= last) copy_tile(vst(prevp(par)), vseq, j + NS - 1, true);
+    if (i + NS < count) copy_tile(kst(par), kseq, tile_of(i + NS), false);
+    if (i + NS - 1 < count) copy_tile(vst(prevp(par)), vseq, tile_of(i + NS - 1), true);
   };
-  // General step (diagonal and tail tiles, the last step): every check.
-  auto step = [&](auto par, int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) YR_INLINE {
-    stage(par, j);
-    if (j + 1 <= last && active(j + 1)) scores(nextp(par), nxt);
-    if (active(j)) {
-      const float neg_m = softmax_front(j, cur, true);
+  // General step (diagonal, window-edge and tail tiles, the last step): every
+  // check.
+  auto step = [&](auto par, int i, f32x16 (&cur)[2], f32x16 (&nxt)[2]) YR_INLINE {
+    stage(par, i);
+    if (i + 1 < count && active(tile_of(i + 1))) scores(nextp(par), nxt);
+    if (active(tile_of(i))) {
+      const float neg_m = softmax_front(tile_of(i), cur, true);
       bf16x8 pf[4];
       softmax_back(cur, neg_m, pf);
       pv(par, pf);
     }
   };
-  // Steady step: tiles j and j+1 lie wholly below every row of the workgroup
-  // (no mask, all waves active), so the score MFMAs of tile j+1, the exp /
-  // convert work of tile j and the PV MFMAs of tile j form one basic block.
-  auto step_steady = [&](auto par, int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) YR_INLINE {
-    stage(par, j);
-    const float neg_m = softmax_front(j, cur, false);
+  // Clear step: tiles i and i+1 of the list need no mask for any row (below
+  // the diagonal of the workgroup's first row, inside the window of its last
+  // row) and every wave works on both, so the score MFMAs of tile i+1, the exp / convert work of tile i
+  // and the PV MFMAs of tile i form one basic block.
+  auto step_clear = [&](auto par, int i, f32x16 (&cur)[2], f32x16 (&nxt)[2]) YR_INLINE {
+    stage(par, i);
+    const float neg_m = softmax_front(tile_of(i), cur, false);
     scores(nextp(par), nxt);
     bf16x8 pf[4];
     softmax_back(cur, neg_m, pf);
     pv(par, pf);
   };
 
-  // prologue: every prologue copy landed; S(0)
+  // prologue: every prologue copy landed; S(tile(0))
   wait_dma<0>();
   __syncthreads();
   f32x16 sa[2], sb[2];
-  if (active(0)) scores(std::integral_constant<int, 0>{}, sa);
-  // Steps are unrolled over the stage index (j % NS) and the score buffer
-  // (j % 2), so every LDS array and register array is picked at compile time.
+  if (active(tile_of(0))) scores(std::integral_constant<int, 0>{}, sa);
+  // Steps are unrolled over the stage index (i % NS) and the score buffer
+  // (i % 2), so every LDS array and register array is picked at compile time.
   constexpr int BL = NS == 2 ? 2 : 6;
   auto sbuf = [&](auto ic) YR_INLINE -> f32x16(&)[2] {
     if constexpr (decltype(ic)::value % 2 == 0) return sa; else return sb;
@@ -380,21 +420,36 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   auto obuf = [&](auto ic) YR_INLINE -> f32x16(&)[2] {
     if constexpr (decltype(ic)::value % 2 == 0) return sb; else return sa;
   };
-  // tiles below q0 (the workgroup's first row) need no mask for any wave
-  const int steady_end = q0 / kBC - 1;  // steps j with j + 1 < q0 / kBC
-  int j = 0;
-  for (; j + BL - 1 < steady_end; j += BL) {
+  // The tiles that need no mask for any row form one run of the list: from
+  // the first tile at or past the window start of the workgroup's last row to
+  // the last tile below the diagonal of its first row (list positions
+  // [c0, c1)).  Steps before it and after it take the general body; a clear
+  // step i needs tiles i and i+1 in the run.  Separate loops keep each body's
+  // registers to itself.
+  int c0 = count, c1 = count;
+  {
+    const int jd = (P + q0 + 1) / kBC - 1;  // last tile wholly below the first row's diagonal
+    const int jc = window > 0 ? max(jw, (P + qend - window + kBC - 1) / kBC) : 0;
+    if (jd >= jc) {
+      c0 = js + (jc - jw);
+      c1 = js + (jd - jw) + 1;
+    }
+  }
+  auto general_block = [&](int i) YR_INLINE {
     static_for<0, BL>([&](auto ic) YR_INLINE {
       constexpr int I = decltype(ic)::value;
-      step_steady(std::integral_constant<int, I % NS>{}, j + I, sbuf(ic), obuf(ic));
+      if (i + I < count) step(std::integral_constant<int, I % NS>{}, i + I, sbuf(ic), obuf(ic));
     });
-  }
-  for (; j <= last; j += BL) {
+  };
+  int i = 0;
+  for (; i < c0; i += BL) general_block(i);
+  for (; i + BL < c1; i += BL) {
     static_for<0, BL>([&](auto ic) YR_INLINE {
       constexpr int I = decltype(ic)::value;
-      if (j + I <= last) step(std::integral_constant<int, I % NS>{}, j + I, sbuf(ic), obuf(ic));
+      step_clear(std::integral_constant<int, I % NS>{}, i + I, sbuf(ic), obuf(ic));
     });
   }
+  for (; i < count; i += BL) general_block(i);
 
   // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ---------------------
   const float l_tot = l_part + __shfl_xor(l_part, 32);
@@ -429,7 +484,7 @@ hipError_t launch_one(const PrefillArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_F32, ROT>), dim3((unsigned)blocks), dim3(kThreads),
                      0, s, (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                      a.cu_seqlens, a.B, a.max_seqlen, a.T, a.Hq, a.Hkv, a.theta, scale_log2, a.out,
-                     a.lse, ntiles, a.dev_flag);
+                     a.lse, ntiles, a.dev_flag, a.kv_cache_len, a.ctx_lens, a.window, a.sinks);
   return hipGetLastError();
 }
 

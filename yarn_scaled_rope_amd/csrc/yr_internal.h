@@ -47,7 +47,14 @@ struct PrefillArgs {
   void *out;
   int out_dtype;
   float *lse;
-  int *dev_flag;         // non-NULL: this launch validates cu_seqlens
+  int *dev_flag;         // non-NULL: this launch validates cu_seqlens (and ctx_lens)
+  // key source: kv_cache_len == 0: k/v packed like q ([T, Hkv, D], rows by
+  // cu_seqlens); kv_cache_len > 0: k/v are [B, kv_cache_len, Hkv, D] caches
+  // and sequence b's queries start at position ctx_lens[b]
+  int kv_cache_len;
+  const int *ctx_lens;   // NULL = no cached prefix
+  int window;            // 0 = plain causal
+  int sinks;
 };
 
 struct DecodeArgs {
@@ -72,6 +79,8 @@ struct DecodeArgs {
   int chunk;
   int nsplit;
   int *dev_flag;
+  int window;            // 0 = every cache row
+  int sinks;
 };
 
 hipError_t launch_rope(const RopeArgs &a, hipStream_t s);

@@ -37,6 +37,7 @@ YR_PREFILL_K_ROTATED = 1
 YR_DEVERR_CU_SEQLENS = 1
 YR_DEVERR_SEQLENS = 2
 YR_DEVERR_QPOS = 4
+YR_DEVERR_CTX_LENS = 8
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libyarnattn.so")
 
@@ -57,9 +58,12 @@ def _declare(lib):
         "rope_apply": (i, [vp, i, ll, i, i, vp, vp, vp]),
         "rope_apply_packed": (i, [vp, vp, i, vp, i, i, ll, i, i, vp, vp, vp]),
         "attn_prefill_workspace_bytes": (sz, [ll, i, i, i]),
-        "attn_prefill_fwd": (i, [vp, vp, vp, i, vp, i, i, ll, i, i, i, vp, i, f, vp, i, vp, vp, sz, vp]),
+        "attn_prefill_fwd": (i, [vp, vp, vp, i, vp, i, i, ll, i, i, i, vp, i, f, i, i, vp, i, vp, vp,
+                                 sz, vp]),
+        "attn_prefill_chunk": (i, [vp, vp, vp, i, vp, vp, i, i, ll, i, i, i, i, vp, f, i, i, vp, i,
+                                   vp, vp, sz, vp]),
         "attn_decode_workspace_bytes": (sz, [i, i, i, i]),
-        "attn_decode": (i, [vp, vp, vp, i, vp, vp, i, i, i, i, i, vp, f, vp, i, vp, vp, sz, vp]),
+        "attn_decode": (i, [vp, vp, vp, i, vp, vp, i, i, i, i, i, vp, f, i, i, vp, i, vp, vp, sz, vp]),
         "yr_read_device_error": (i, [vp, vp, vp]),
         "yr_status_string": (ctypes.c_char_p, [i]),
         "yr_last_error": (ctypes.c_char_p, []),
@@ -182,10 +186,11 @@ def attn_prefill_workspace_bytes(T: int, hkv: int, head_dim: int, in_dtype: int)
 
 def attn_prefill_fwd(q, k, v, cu_seqlens, max_seqlen: int, inv_freq_f64, softmax_scale: float,
                      out=None, out_dtype=None, lse=None, workspace=None, want_lse=True,
-                     k_rotated=False, stream=None):
+                     k_rotated=False, window: int = 0, sinks: int = 0, stream=None):
     """Causal prefill.  q [T, Hq, D], k/v [T, Hkv, D] unrotated (or rotated,
     with inv_freq_f64=None; or only k rotated, with k_rotated=True);
-    cu_seqlens int32 [B+1].  Returns (out, lse)."""
+    cu_seqlens int32 [B+1]; optional sliding window / sinks.  Returns
+    (out, lse)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n)
     _need(cu_seqlens, "cu_seqlens", torch.int32)
@@ -212,9 +217,51 @@ def attn_prefill_fwd(q, k, v, cu_seqlens, max_seqlen: int, inv_freq_f64, softmax
     _check(lib.attn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), in_code, _ptr(cu_seqlens), B,
                                 int(max_seqlen), T, hq, hkv, D, _ptr(inv_freq_f64),
                                 YR_PREFILL_K_ROTATED if k_rotated else 0,
-                                float(softmax_scale), _ptr(out), out_code, _ptr(lse),
+                                float(softmax_scale), int(window), int(sinks), _ptr(out), out_code,
+                                _ptr(lse),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 _stream(stream)))
+    return out, lse
+
+
+def attn_prefill_chunk(q, k_cache, v_cache, cu_seqlens_q, ctx_lens, max_seqlen_q: int,
+                       inv_freq_f64, softmax_scale: float, window: int = 0, sinks: int = 0,
+                       out=None, out_dtype=None, lse=None, workspace=None, want_lse=True,
+                       stream=None):
+    """Chunked prefill: new tokens q [Tq, Hq, D] (packed by cu_seqlens_q)
+    against caches [B, Lmax, Hkv, D] that already hold ctx_lens[b] earlier
+    tokens followed by the chunk's rotated keys and values.  Returns
+    (out, lse)."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    _need(ctx_lens, "ctx_lens", torch.int32)
+    if inv_freq_f64 is not None:
+        _need(inv_freq_f64, "inv_freq_f64", torch.float64)
+    Tq, hq, D = q.shape
+    B, lmax, hkv, _ = k_cache.shape
+    if k_cache.shape != (B, lmax, hkv, D) or v_cache.shape != k_cache.shape or \
+            k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise YarnAttnError(YR_ERR_INVALID, "caches must be [B, Lmax, Hkv, D] of q's dtype")
+    if cu_seqlens_q.numel() != B + 1 or ctx_lens.numel() != B:
+        raise YarnAttnError(YR_ERR_INVALID, "cu_seqlens_q must have B+1 and ctx_lens B entries")
+    in_code = _dtype_code(q)
+    out_code = (YR_F32 if in_code == YR_F32 else YR_BF16) if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((Tq, hq, D), dtype=_torch_dtype(out_code), device=q.device)
+    else:
+        _need(out, "out", _torch_dtype(out_code))
+    if lse is None and want_lse:
+        lse = torch.empty((hq, Tq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(256, dtype=torch.uint8, device=q.device)
+    lib = load_library()
+    _check(lib.attn_prefill_chunk(_ptr(q), _ptr(k_cache), _ptr(v_cache), in_code,
+                                  _ptr(cu_seqlens_q), _ptr(ctx_lens), B, int(max_seqlen_q), Tq,
+                                  lmax, hq, hkv, D, _ptr(inv_freq_f64), float(softmax_scale),
+                                  int(window), int(sinks), _ptr(out), out_code, _ptr(lse),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream)))
     return out, lse
 
 
@@ -224,9 +271,11 @@ def attn_decode_workspace_bytes(B: int, max_cache_len: int, hq: int, head_dim: i
 
 
 def attn_decode(q, k_cache, v_cache, seqlens, inv_freq_f64, softmax_scale: float, q_pos=None,
-                out=None, out_dtype=None, lse=None, workspace=None, want_lse=True, stream=None):
+                out=None, out_dtype=None, lse=None, workspace=None, want_lse=True,
+                window: int = 0, sinks: int = 0, stream=None):
     """One query per sequence over a contiguous cache.  q [B, Hq, D];
-    caches [B, Lmax, Hkv, D]; seqlens int32 [B].  Returns (out, lse)."""
+    caches [B, Lmax, Hkv, D]; seqlens int32 [B]; optional sliding window /
+    sinks.  Returns (out, lse)."""
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _need(t, n)
     _need(seqlens, "seqlens", torch.int32)
@@ -250,8 +299,9 @@ def attn_decode(q, k_cache, v_cache, seqlens, inv_freq_f64, softmax_scale: float
     lib = load_library()
     _check(lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), in_code, _ptr(seqlens),
                            _ptr(q_pos), B, lmax, hq, hkv, D, _ptr(inv_freq_f64),
-                           float(softmax_scale), _ptr(out), out_code, _ptr(lse), _ptr(workspace),
-                           workspace.numel() * workspace.element_size(), _stream(stream)))
+                           float(softmax_scale), int(window), int(sinks), _ptr(out), out_code,
+                           _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _stream(stream)))
     return out, lse
 
 

@@ -39,6 +39,8 @@ class PrefillConfig:
     base: float
     factor: float
     original_max_position: int
+    window: int = 0            # sliding window (0 = plain causal)
+    sinks: int = 0
 
     @property
     def total_tokens(self) -> int:
@@ -63,6 +65,28 @@ class DecodeConfig:
     base: float
     factor: float
     original_max_position: int
+    window: int = 0
+    sinks: int = 0
+
+
+@dataclasses.dataclass(frozen=True)
+class ChunkConfig:
+    """Chunked prefill: chunk_lens[b] new tokens after ctx_lens[b] cached ones,
+    caches [B, max_cache_len, Hkv, D]."""
+    name: str
+    index: int
+    ctx_lens: tuple
+    chunk_lens: tuple
+    max_cache_len: int
+    hq: int
+    hkv: int
+    head_dim: int
+    dtype: str
+    base: float
+    factor: float
+    original_max_position: int
+    window: int = 0
+    sinks: int = 0
 
 
 TINY_F32 = PrefillConfig("tiny_fp32_prefill", 0, (256,), 4, 2, 64, "f32",
@@ -77,9 +101,22 @@ LLAMA3_70B_RAGGED = PrefillConfig("llama3_70b_ragged_prefill", 4,
                                   (131072, 65537, 32000, 4097), 64, 8, 128,
                                   "bf16", 500000.0, 8.0, 16384)
 
+# Chunked prefill: 4 sequences, each a 4096-token chunk after a cached prefix
+# of 28K .. 124K tokens (Llama-3-8B GQA attention layer).
+CHUNK_4X4K = ChunkConfig("llama3_8b_chunked_prefill_4x4k", 5, (28672, 61440, 94208, 126976),
+                         (4096, 4096, 4096, 4096), 131072, 32, 8, 128, "bf16", 500000.0, 8.0,
+                         16384)
+# Sliding window of 4096 tokens plus 4 sink tokens ("effective context = 4 +
+# last 4096") on the 16K MHA prefill and on the 16-sequence decode.
+LLAMA2_7B_16K_SWA = PrefillConfig("llama2_7b_prefill_16k_window4k_sinks4", 6, (16384,), 32, 32,
+                                  128, "bf16", 10000.0, 4.0, 4096, window=4096, sinks=4)
+DECODE_B16_SWA = DecodeConfig("decode_b16_gqa_window4k_sinks4", 7, 16, 131072, 32768, 32, 8,
+                              128, "bf16", 500000.0, 8.0, 16384, window=4096, sinks=4)
+
 PREFILL_CONFIGS = {c.name: c for c in (TINY_F32, LLAMA2_7B_16K, LLAMA3_8B_128K,
-                                       LLAMA3_70B_RAGGED)}
-DECODE_CONFIGS = {DECODE_B16.name: DECODE_B16}
+                                       LLAMA3_70B_RAGGED, LLAMA2_7B_16K_SWA)}
+DECODE_CONFIGS = {c.name: c for c in (DECODE_B16, DECODE_B16_SWA)}
+CHUNK_CONFIGS = {CHUNK_4X4K.name: CHUNK_4X4K}
 
 
 # ---------------------------------------------------------------- bf16 bits
@@ -158,6 +195,34 @@ def make_decode(cfg: DecodeConfig, seed: int | None = None, batch=None,
             "seqlens": seqlens, "dtype": cfg.dtype}
 
 
+def make_chunk(cfg: ChunkConfig, seed: int | None = None, ctx_lens=None, chunk_lens=None,
+               max_cache_len=None):
+    """Chunked-prefill inputs: q [Tq, Hq, D] for the new tokens (packed);
+    k_cache, v_cache [B, Lmax, Hkv, D] whose rows 0 .. ctx_b + n_b - 1 are
+    drawn (K taken as already rotated) and the rest NaN.  Draw order: q, then
+    the K rows of sequence 0, 1, ..., then the V rows."""
+    ctx = tuple(cfg.ctx_lens if ctx_lens is None else ctx_lens)
+    lens = tuple(cfg.chunk_lens if chunk_lens is None else chunk_lens)
+    lmax = cfg.max_cache_len if max_cache_len is None else max_cache_len
+    B = len(lens)
+    rng = np.random.Generator(np.random.PCG64(1000 + cfg.index if seed is None else seed))
+    Tq = int(sum(lens))
+    q = _draw(rng, (Tq, cfg.hq, cfg.head_dim), cfg.dtype)
+    caches = []
+    for _ in range(2):
+        if cfg.dtype == "bf16":
+            c = np.full((B, lmax, cfg.hkv, cfg.head_dim), BF16_NAN_BITS, dtype=np.uint16)
+        else:
+            c = np.full((B, lmax, cfg.hkv, cfg.head_dim), np.nan, dtype=np.float32)
+        for b in range(B):
+            rows = ctx[b] + lens[b]
+            c[b, :rows] = _draw(rng, (rows, cfg.hkv, cfg.head_dim), cfg.dtype)
+        caches.append(c)
+    return {"q": q, "k_cache": caches[0], "v_cache": caches[1], "cu_seqlens_q": cu_seqlens_of(lens),
+            "ctx_lens": np.asarray(ctx, dtype=np.int32), "chunk_lens": lens, "dtype": cfg.dtype,
+            "max_cache_len": lmax}
+
+
 def sample_rows(seq_lens, hq: int, hkv: int, n_random: int = 32, seed: int = 7,
                 edge_tiles=(32, 64, 128, 256), edge_span: int = 4):
     """A seeded sample of (token, head) rows of a packed batch for checks at
@@ -200,6 +265,44 @@ def prefill_causal_flops(seq_lens, hq: int, head_dim: int) -> int:
     included: 4 * D * Hq * sum n(n+1)/2."""
     pairs = sum(int(n) * (int(n) + 1) // 2 for n in seq_lens)
     return 4 * int(head_dim) * int(hq) * pairs
+
+
+def visible_keys(positions, window: int = 0, sinks: int = 0) -> np.ndarray:
+    """Number of keys a query at each position attends to: every earlier
+    position and itself, or with a window W the min(m+1, W) most recent plus
+    the sinks that lie before the window."""
+    m = np.asarray(positions, dtype=np.int64)
+    if window <= 0:
+        return m + 1
+    return np.minimum(m + 1, window) + np.minimum(sinks, np.maximum(0, m - window + 1))
+
+
+def prefill_visible_flops(seq_lens, hq: int, head_dim: int, window: int = 0, sinks: int = 0,
+                          ctx_lens=None) -> int:
+    """Algorithmic FLOPs (4 * D per visible (query, key) pair per query head)
+    of prefill with a window / sinks, or of a chunk after ctx_lens cached
+    tokens (positions start there)."""
+    pairs = 0
+    for b, n in enumerate(seq_lens):
+        p0 = 0 if ctx_lens is None else int(ctx_lens[b])
+        pairs += int(np.sum(visible_keys(np.arange(p0, p0 + int(n)), window, sinks)))
+    return 4 * int(head_dim) * int(hq) * pairs
+
+
+def decode_visible_bytes(seqlens, hkv: int, head_dim: int, window: int = 0, sinks: int = 0,
+                         q_pos=None, elem_bytes: int = 2) -> int:
+    """K+V bytes a windowed decode step must read: the cache rows visible
+    from the query's position (default: the cache length)."""
+    rows = 0
+    for b, L in enumerate(seqlens):
+        L = int(L)
+        m = L if q_pos is None else int(q_pos[b])
+        if window <= 0:
+            rows += L
+        else:
+            lo = max(0, m - window + 1)
+            rows += max(0, L - lo) + min(sinks, lo, L)
+    return 2 * int(hkv) * int(head_dim) * int(elem_bytes) * rows
 
 
 def dense_attention_flops(seq_len: int, head_dim: int, heads: int = 1) -> int:
