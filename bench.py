@@ -15,8 +15,8 @@ one step over the wall time of one step.
 The same run then times the decode hot path (split-K sweep + LSE merge) over
 the 16-sequence 32K-128K cache workload and reports it as `decode`; under
 `next` it times chunked prefill (4 chunks of 4096 new tokens after 28K-124K
-cached ones) and a 4096-token sliding window with 4 sink tokens on the
-prefill and decode inputs; and it times the fp64 CPU checker on bounded
+cached ones), a 4096-token sliding window with 4 sink tokens on the prefill
+and decode inputs, and decode over an FP8 (E4M3) copy of the decode cache; and it times the fp64 CPU checker on bounded
 samples of the prefill and decode workloads as `cpu_baseline`.
 
 Roofline: the attention kernel's own duration comes from HIP events on the
@@ -341,6 +341,39 @@ def bench_next(args, torch, ops, wl, pstate, dstate):
             "bytes_per_launch": int(nbytes),
             "config": {"workload": dc.name, "inputs": "those of the decode line",
                        "window": dc.window, "sinks": dc.sinks}}
+        # FP8 (E4M3) copy of the same cache, one scale per KV head (amax / 448
+        # of its valid rows), quantised on the device
+        log("fp8 decode: quantising the cache")
+        scales, codes = [], []
+        L = torch.from_numpy(d["seqlens"].astype(np.int64)).cuda()
+        valid = (torch.arange(d["kc"].shape[1], device="cuda")[None, :] < L[:, None])
+        for c in (d["kc"], d["vc"]):
+            amax = torch.stack([c[:, :, h].float().abs().masked_fill(~valid[:, :, None], 0).amax()
+                                for h in range(c.shape[2])])
+            sc = (amax / 448.0).clamp_min(1e-12).float().contiguous()
+            q8 = torch.empty(c.shape, dtype=torch.uint8, device="cuda")
+            for b in range(c.shape[0]):  # per sequence, to bound the temporaries
+                q8[b] = (c[b].float() / sc[None, :, None]).nan_to_num(0.0).to(
+                    torch.float8_e4m3fn).view(torch.uint8)
+            scales.append(sc)
+            codes.append(q8)
+        out = torch.empty_like(d["q"])
+        log("fp8 decode timed")
+        ms = _event_ms(torch, lambda: ops.attn_decode_fp8(d["q"], codes[0], codes[1], scales[0],
+                                                          scales[1], d["sl"], d["theta"],
+                                                          d["scale"], out=out, want_lse=False,
+                                                          workspace=d["ws"], stream=stream),
+                       args.warmup, args.decode_steps, stream)
+        nbytes = wl.decode_kv_bytes(d["seqlens"], wl.DECODE_B16.hkv, wl.DECODE_B16.head_dim, 1)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res["fp8_decode"] = {
+            "metric": "FP8-cache decode KV GB/s", "value": round(gbs, 2), "unit": "GB/s",
+            "ms_per_call": round(ms, 4), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "bytes_per_launch": int(nbytes),
+            "config": {"workload": wl.DECODE_B16.name + "_fp8_e4m3",
+                       "inputs": "the decode line's cache, as E4M3 codes with per-KV-head "
+                                 "scales amax/448"}}
+        del codes
     return res
 
 

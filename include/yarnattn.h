@@ -52,6 +52,7 @@ extern "C" {
 /* ---- element types ----------------------------------------------------- */
 #define YR_F32 0
 #define YR_BF16 1
+#define YR_FP8_E4M3 2 /* OCP 8-bit float, 4 exponent / 3 mantissa bits (decode caches only) */
 
 /* ---- frequency rules --------------------------------------------------- */
 #define YR_ROPE_PLAIN 0 /* theta_i = base^(-2i/d)                          */
@@ -260,6 +261,32 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
                 const double *inv_freq_f64, float softmax_scale, int window, int sinks,
                 void *out, int out_dtype, float *lse, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode_fp8 -- attn_decode over an FP8 KV cache.
+ *
+ * The pages name an 8-bit cache as half the bf16 bytes per token ("Long
+ * context (engineering 100k+ tokens)", section 1; "Long-context models",
+ * "Memory grows even with efficient attention") but fix no format or scales.
+ * Convention here: every cache element is one OCP E4M3 byte (bias 7,
+ * subnormals, no infinities, NaN = S.1111.111, largest 448), and the value it
+ * stands for is decode(byte) * k_scale[h] (keys) or * v_scale[h] (values) for
+ * KV head h.  Keys are already rotated.  Everything else -- q (bf16,
+ * unrotated), positions, window / sinks, out, lse, workspace (sized by
+ * attn_decode_workspace_bytes) -- is as attn_decode.  The sweep reads the
+ * cache bytes once (half the bytes of a bf16 cache); the scales fold into the
+ * logit scale and the output.
+ *
+ *   k_cache, v_cache  device uint8 [B, max_cache_len, Hkv, head_dim], E4M3
+ *   k_scale, v_scale  device float[Hkv], finite and > 0
+ *   Hq / Hkv <= 32
+ */
+int attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
+                    const float *k_scale, const float *v_scale, const int *seqlens,
+                    const int *q_pos, int B, int max_cache_len, int Hq, int Hkv, int head_dim,
+                    const double *inv_freq_f64, float softmax_scale, int window, int sinks,
+                    void *out, int out_dtype, float *lse, void *workspace,
+                    size_t workspace_bytes, void *stream);
 
 /*
  * yr_read_device_error -- synchronise `stream`, read the device error word of

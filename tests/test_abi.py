@@ -197,6 +197,33 @@ def test_decode_rejects_before_launch(lib, kw, status):
     assert decode_call(lib, **kw) == status
 
 
+def decode_fp8_call(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, seqlens=FAKE, qpos=None, B=2, Lmax=1024,
+             Hq=8, Hkv=2, D=128, theta=FAKE, scale=0.1, window=0, sinks=0, out=FAKE,
+             out_dtype=ops.YR_BF16, lse=FAKE, ws=WS, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.attn_decode_fp8(a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["seqlens"],
+                               a["qpos"], a["B"], a["Lmax"], a["Hq"], a["Hkv"], a["D"],
+                               a["theta"], a["scale"], a["window"], a["sinks"], a["out"],
+                               a["out_dtype"], a["lse"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=None), ops.YR_ERR_NULL),
+    (dict(vs=None), ops.YR_ERR_NULL),
+    (dict(kc=None), ops.YR_ERR_NULL),
+    (dict(D=96), ops.YR_ERR_UNSUPPORTED),
+    (dict(Hq=128, Hkv=2), ops.YR_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), ops.YR_ERR_INVALID),
+    (dict(out_dtype=2), ops.YR_ERR_UNSUPPORTED),
+    (dict(window=1), ops.YR_ERR_INVALID),
+    (dict(ws_bytes=1024), ops.YR_ERR_WORKSPACE),
+])
+def test_decode_fp8_rejects_before_launch(lib, kw, status):
+    assert decode_fp8_call(lib, **kw) == status
+    assert lib.yr_last_error()
+
+
 def test_rope_rejects_and_empty(lib):
     assert lib.rope_apply(FAKE, ops.YR_BF16, 4, 2, 7, FAKE, FAKE, None) == ops.YR_ERR_INVALID
     assert lib.rope_apply(FAKE, 9, 4, 2, 8, FAKE, FAKE, None) == ops.YR_ERR_UNSUPPORTED

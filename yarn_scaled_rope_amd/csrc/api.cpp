@@ -273,46 +273,57 @@ size_t attn_decode_workspace_bytes(int B, int max_cache_len, int Hq, int head_di
   return kHeader + align_up(rows * head_dim * 4, 256) + align_up(rows * 4, 256);
 }
 
-int attn_decode(const void *q, const void *k_cache, const void *v_cache, int in_dtype,
-                const int *seqlens, const int *q_pos, int B, int max_cache_len, int Hq, int Hkv,
-                int head_dim, const double *inv_freq_f64, float softmax_scale, int window,
-                int sinks, void *out, int out_dtype, float *lse, void *workspace,
-                size_t workspace_bytes, void *stream) {
-  if (in_dtype != YR_F32 && in_dtype != YR_BF16)
-    return fail(YR_ERR_UNSUPPORTED, "attn_decode: in_dtype must be YR_F32 or YR_BF16");
+namespace {
+
+// attn_decode and attn_decode_fp8: validation, workspace layout and launch.
+// cache_dtype is the storage type of the caches (q is YR_F32 with an fp32
+// cache, else YR_BF16).
+int decode_impl(const char *fn, const void *q, const void *k_cache, const void *v_cache,
+                int cache_dtype, const float *k_scale, const float *v_scale, const int *seqlens,
+                const int *q_pos, int B, int max_cache_len, int Hq, int Hkv, int head_dim,
+                const double *inv_freq_f64, float softmax_scale, int window, int sinks,
+                void *out, int out_dtype, float *lse, void *workspace, size_t workspace_bytes,
+                void *stream) {
+  char msg[160];
+  auto bad = [&](int st, const char *what) {
+    std::snprintf(msg, sizeof msg, "%s: %s", fn, what);
+    return fail(st, msg);
+  };
+  if (cache_dtype != YR_F32 && cache_dtype != YR_BF16 && cache_dtype != YR_FP8_E4M3)
+    return bad(YR_ERR_UNSUPPORTED, "in_dtype must be YR_F32 or YR_BF16");
   if (out_dtype != YR_F32 && out_dtype != YR_BF16)
-    return fail(YR_ERR_UNSUPPORTED, "attn_decode: out_dtype must be YR_F32 or YR_BF16");
-  if (!dims_ok(head_dim)) return fail(YR_ERR_UNSUPPORTED, "attn_decode: head_dim must be 64 or 128");
+    return bad(YR_ERR_UNSUPPORTED, "out_dtype must be YR_F32 or YR_BF16");
+  if (!dims_ok(head_dim)) return bad(YR_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
-    return fail(YR_ERR_INVALID, "attn_decode: need Hq >= 1, Hkv >= 1, Hq % Hkv == 0");
-  if (Hq / Hkv > (in_dtype == YR_BF16 ? 32 : 16))
-    return fail(YR_ERR_UNSUPPORTED,
-                "attn_decode: at most 32 (bf16) or 16 (fp32) query heads per KV head");
-  if (B < 1 || max_cache_len < 1) return fail(YR_ERR_INVALID, "attn_decode: need B >= 1, max_cache_len >= 1");
-  if ((long long)B * max_cache_len > (1LL << 34))
-    return fail(YR_ERR_INVALID, "attn_decode: cache too large");
+    return bad(YR_ERR_INVALID, "need Hq >= 1, Hkv >= 1, Hq % Hkv == 0");
+  if (Hq / Hkv > (cache_dtype == YR_F32 ? 16 : 32))
+    return bad(YR_ERR_UNSUPPORTED, "at most 32 (bf16, fp8) or 16 (fp32) query heads per KV head");
+  if (B < 1 || max_cache_len < 1) return bad(YR_ERR_INVALID, "need B >= 1, max_cache_len >= 1");
+  if ((long long)B * max_cache_len > (1LL << 34)) return bad(YR_ERR_INVALID, "cache too large");
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
-    return fail(YR_ERR_INVALID, "attn_decode: softmax_scale must be finite and > 0");
-  if (window < 0 || sinks < 0) return fail(YR_ERR_INVALID, "attn_decode: window and sinks must be >= 0");
+    return bad(YR_ERR_INVALID, "softmax_scale must be finite and > 0");
+  if (window < 0 || sinks < 0) return bad(YR_ERR_INVALID, "window and sinks must be >= 0");
   if (window == 1 && sinks == 0)
-    return fail(YR_ERR_INVALID, "attn_decode: a one-token window without sinks sees no cache row");
+    return bad(YR_ERR_INVALID, "a one-token window without sinks sees no cache row");
   if (!q || !k_cache || !v_cache || !seqlens || !out || !workspace)
-    return fail(YR_ERR_NULL, "attn_decode: q, caches, seqlens, out and workspace are required");
+    return bad(YR_ERR_NULL, "q, caches, seqlens, out and workspace are required");
+  if (cache_dtype == YR_FP8_E4M3 && (!k_scale || !v_scale))
+    return bad(YR_ERR_NULL, "k_scale and v_scale are required");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
-    return fail(YR_ERR_WORKSPACE, "attn_decode: workspace must be 256-byte aligned");
+    return bad(YR_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   const size_t need = attn_decode_workspace_bytes(B, max_cache_len, Hq, head_dim);
-  if (workspace_bytes < need) return fail(YR_ERR_WORKSPACE, "attn_decode: workspace too small");
+  if (workspace_bytes < need) return bad(YR_ERR_WORKSPACE, "workspace too small");
 
   const int chunk = decode_chunk(B, max_cache_len, Hkv);
   const int nsplit = decode_nsplit(max_cache_len, chunk);
-  if ((long long)B * Hkv * nsplit > 0x7fffffffLL) return fail(YR_ERR_INVALID, "attn_decode: grid too large");
+  if ((long long)B * Hkv * nsplit > 0x7fffffffLL) return bad(YR_ERR_INVALID, "grid too large");
   const size_t rows = (size_t)B * Hq * nsplit;
   char *ws = static_cast<char *>(workspace);
   DecodeArgs d{};
   d.q = q;
   d.k_cache = k_cache;
   d.v_cache = v_cache;
-  d.in_dtype = in_dtype;
+  d.in_dtype = cache_dtype;
   d.seqlens = seqlens;
   d.q_pos = q_pos;
   d.B = B;
@@ -332,9 +343,37 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, int in_
   d.dev_flag = flag_of(workspace);
   d.window = window;
   d.sinks = sinks;
+  d.k_scale = k_scale;
+  d.v_scale = v_scale;
   const hipError_t e = launch_decode(d, (hipStream_t)stream);
-  if (e != hipSuccess) return fail_hip(e, "attn_decode");
+  if (e != hipSuccess) return fail_hip(e, fn);
   return YR_OK;
+}
+
+}  // namespace
+
+int attn_decode(const void *q, const void *k_cache, const void *v_cache, int in_dtype,
+                const int *seqlens, const int *q_pos, int B, int max_cache_len, int Hq, int Hkv,
+                int head_dim, const double *inv_freq_f64, float softmax_scale, int window,
+                int sinks, void *out, int out_dtype, float *lse, void *workspace,
+                size_t workspace_bytes, void *stream) {
+  if (in_dtype != YR_F32 && in_dtype != YR_BF16)
+    return fail(YR_ERR_UNSUPPORTED, "attn_decode: in_dtype must be YR_F32 or YR_BF16");
+  return decode_impl("attn_decode", q, k_cache, v_cache, in_dtype, nullptr, nullptr, seqlens,
+                     q_pos, B, max_cache_len, Hq, Hkv, head_dim, inv_freq_f64, softmax_scale,
+                     window, sinks, out, out_dtype, lse, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
+                    const float *k_scale, const float *v_scale, const int *seqlens,
+                    const int *q_pos, int B, int max_cache_len, int Hq, int Hkv, int head_dim,
+                    const double *inv_freq_f64, float softmax_scale, int window, int sinks,
+                    void *out, int out_dtype, float *lse, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+  return decode_impl("attn_decode_fp8", q, k_cache, v_cache, YR_FP8_E4M3, k_scale, v_scale,
+                     seqlens, q_pos, B, max_cache_len, Hq, Hkv, head_dim, inv_freq_f64,
+                     softmax_scale, window, sinks, out, out_dtype, lse, workspace,
+                     workspace_bytes, stream);
 }
 
 int yr_read_device_error(const void *workspace, void *stream, int *flags) {

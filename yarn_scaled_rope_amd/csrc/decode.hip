@@ -344,10 +344,33 @@ __device__ __forceinline__ int vswz(int e) {
   return CH >= 16 ? ((2 * e) ^ (8 * (e & 1))) : 2 * e;
 }
 
-template <int D, int W, int NB>
+// FP8 (E4M3) cache rows: 16-byte slot swizzles that keep the K reads (8
+// rows x one 16-byte chunk per pass) and the 8-bit transposing V reads (8 key
+// rows 0-3, 8-11 (+4) x one chunk per 16 lanes) on distinct banks.
+template <int D>
+__device__ __forceinline__ int kswz8(int row) {
+  return D >= 128 ? (row & 7) : ((row >> 1) & 3);
+}
+template <int D>
+__device__ __forceinline__ int vswz8(int row) {
+  return D >= 128 ? ((row & 3) | (((row >> 3) & 1) << 2)) : (((row >> 1) & 1) | (((row >> 3) & 1) << 1));
+}
+
+// Cache element bytes -> bf16 pairs: E4M3 values are exact in bf16.
+// HI picks bytes 2-3 of the word instead of 0-1.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return u32x4{fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
+               fp8x2_to_bf16x2<true>(w1)};
+}
+
+template <int D, int W, int NB, int EB>
 struct MfmaSmem {
   union {
-    uint16_t ring[W][NB][2][kBlk * D];  // [wave][stage][K|V][row * D + swizzled chunk]
+    uint8_t ring[W][NB][2][kBlk * D * EB];  // [wave][stage][K|V][row bytes, swizzled chunks]
     struct {
       float o[W][D][33];
       float m[W][32];
@@ -420,22 +443,53 @@ __device__ __forceinline__ void tr_reads(u32x2 (&r)[DBLK][2], const uint32_t (&a
   }
 }
 
-template <int D, int W, int NB>
+// The 8-bit V^T operands of one k-step: one transposing read per 32-row block
+// db (within 16 lanes, lane t receives byte t & 7 of the 8 bytes addressed by
+// lane 2e + (t >> 3) as element e: 8 keys of one column), reads and wait in one
+// asm block as above.
+template <int DBLK, int OFF>
+__device__ __forceinline__ void tr8_reads(u32x2 (&r)[DBLK], const uint32_t (&a)[DBLK]) {
+  static_assert(DBLK == 2 || DBLK == 4, "head_dim 64 or 128");
+  if constexpr (DBLK == 4) {
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %4 offset:%8\n\t"
+        "ds_read_b64_tr_b8 %1, %5 offset:%8\n\t"
+        "ds_read_b64_tr_b8 %2, %6 offset:%8\n\t"
+        "ds_read_b64_tr_b8 %3, %7 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %2 offset:%4\n\t"
+        "ds_read_b64_tr_b8 %1, %3 offset:%4\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1])
+        : "v"(a[0]), "v"(a[1]), "i"(OFF)
+        : "memory");
+  }
+}
+
+template <int D, int W, int NB, bool FP8>
 __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
-    const uint16_t *__restrict__ vc, const int *__restrict__ seqlens,
+    const uint16_t *__restrict__ q, const void *__restrict__ kc,
+    const void *__restrict__ vc, const int *__restrict__ seqlens,
     const int *__restrict__ qpos, int B, int Lmax, int Hq, int Hkv,
     const double *__restrict__ theta, float scale_log2, int chunk, int nsplit,
-    float *__restrict__ part_o, float *__restrict__ part_lse, int *flag, int window, int sinks) {
-  constexpr int CH = D / 8;        // 16-byte chunks per row
-  constexpr int H = D / 16;        // DMA instructions per K or V block (1 KB each)
+    float *__restrict__ part_o, float *__restrict__ part_lse, int *flag, int window, int sinks,
+    const float *__restrict__ k_scale, const float *__restrict__ v_scale) {
+  constexpr int EB = FP8 ? 1 : 2;  // bytes per cached element
+  constexpr int ROWB = D * EB;     // bytes per cached key row
+  constexpr int CH = ROWB / 16;    // 16-byte chunks per row
+  constexpr int H = kBlk * ROWB / 1024;  // DMA instructions per K or V block (1 KB each)
   constexpr int RPI = 64 / CH;     // rows per DMA instruction
   constexpr int KSTEPS = D / 16;   // score k-steps over the head dim
   constexpr int DBLK = D / 32;     // 32-row blocks of O^T
   constexpr int NT = W * 64;
   static_assert((2 * NB - 1) * H < 64, "vmcnt range");
 
-  __shared__ __align__(16) MfmaSmem<D, W, NB> sm;
+  __shared__ __align__(16) MfmaSmem<D, W, NB, EB> sm;
 
   if (flag != nullptr && blockIdx.x == 0) validate_decode_lens(seqlens, qpos, B, Lmax, flag);
 
@@ -487,37 +541,43 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     return gb < nba ? min(kBlk, na - gb * kBlk) : min(kBlk, nb - (gb - nba) * kBlk);
   };
 
-  const long long rstride = (long long)Hkv * D;  // elements between keys
-  const uint16_t *kbase = kc + ((long long)b * Lmax * Hkv + hk) * D;
-  const uint16_t *vbase = vc + ((long long)b * Lmax * Hkv + hk) * D;
+  const long long rstride = (long long)Hkv * ROWB;  // bytes between keys
+  const uint8_t *kbase = (const uint8_t *)kc + ((long long)b * Lmax * Hkv + hk) * ROWB;
+  const uint8_t *vbase = (const uint8_t *)vc + ((long long)b * Lmax * Hkv + hk) * ROWB;
   const int nmine = nblk > wave ? (nblk - wave + W - 1) / W : 0;  // blocks of this wave
+  // FP8: the per-head scales fold into the logit scale and the output
+  float sl = scale_log2, vsc = 1.f;
+  if constexpr (FP8) {
+    sl = scale_log2 * k_scale[hk];
+    vsc = v_scale[hk];
+  }
 
   // DMA lane mapping: instruction p of a block fills LDS bytes [1024p, 1024p+1024)
   // in lane order; lane l lands on row p*RPI + l/CH, slot l%CH, so it fetches
   // the source chunk that belongs in that slot.
   const int drow = lane / CH, dslot = lane % CH;
-  const uint32_t voff_v =
-      (uint32_t)((drow * rstride + 8 * (dslot ^ vswz<CH>(drow & 3))) * 2);
-  uint32_t voff_k[H];
+  uint32_t voff_k[H], voff_v[H];
 #pragma unroll
   for (int p = 0; p < H; ++p) {
     const int r = p * RPI + drow;
-    voff_k[p] = (uint32_t)((r * rstride + 8 * (dslot ^ (r & (CH - 1)))) * 2);
+    const int kx = FP8 ? kswz8<D>(r) : (r & (CH - 1));
+    const int vx = FP8 ? vswz8<D>(r) : vswz<CH>(r & 3);
+    voff_k[p] = (uint32_t)(r * rstride + 16 * (dslot ^ kx));
+    voff_v[p] = (uint32_t)(r * rstride + 16 * (dslot ^ vx));
   }
-  const uint32_t pstride = (uint32_t)(RPI * rstride * 2);
 
   // t-th block of this wave -> stage; rows past the block's share read 0
   auto issue = [&](int t, int stage, int which) {
     const int key0 = blk_start(wave + t * W);
     const int rows = blk_rows(wave + t * W);
-    const uint32_t bytes = (uint32_t)(((rows - 1) * rstride + D) * 2);
-    const uint16_t *src = (which == 0 ? kbase : vbase) + key0 * rstride;
+    const uint32_t bytes = (uint32_t)((rows - 1) * rstride + ROWB);
+    const uint8_t *src = (which == 0 ? kbase : vbase) + key0 * rstride;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, bytes);
-    uint16_t *dst = sm.u.ring[wave][stage][which];
+    uint8_t *dst = sm.u.ring[wave][stage][which];
 #pragma unroll
     for (int p = 0; p < H; ++p) {
-      const uint32_t vo = which == 0 ? voff_k[p] : voff_v + p * pstride;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (YR_LDS void *)(dst + p * 512), 16, (int)vo, 0,
+      const uint32_t vo = which == 0 ? voff_k[p] : voff_v[p];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (YR_LDS void *)(dst + p * 1024), 16, (int)vo, 0,
                                                0, 2 /* non-temporal */);
     }
   };
@@ -552,10 +612,15 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     }
     __syncthreads();
   }
+  // k-step kk, lane half hh covers head dims 16 kk + 8 hh .. +7; with an FP8
+  // cache one 16-byte read of a K row serves two k-steps, so there lane half
+  // hh covers 16 (2 (kk / 2) + hh) + 8 (kk % 2) .. +7 (Q follows the same order)
   bf16x8 qf[KSTEPS];
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk)
-    qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&sm.qt[l32][16 * kk + 8 * hh]));
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    const int d0 = FP8 ? 16 * (2 * (kk / 2) + hh) + 8 * (kk % 2) : 16 * kk + 8 * hh;
+    qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&sm.qt[l32][d0]));
+  }
 
   f32x16 o[DBLK];
 #pragma unroll
@@ -565,23 +630,36 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
   float mrun = -INFINITY;  // running max of the column, log2 units
   float lsum = 0.f;        // this lane's share of the column's sum
 
-  // LDS read offsets (elements) within a stage
-  const int kx = l32 & (CH - 1);
+  // LDS read offsets within a stage: K row l32, 16-byte chunk slot c ^ kx
+  const int kx = FP8 ? kswz8<D>(l32) : (l32 & (CH - 1));
   // V^T operand addresses (LDS bytes, stage 0 of this wave; the stage, k-step
-  // and row-half offsets are immediates).  Lane t of a 16-lane group points at
-  // 4 elements of key row 4*hh + (t >> 2) (+16 ks + 8 r), column block 4*db +
-  // its chunk within the 16 columns of the group.
-  constexpr int kStageBytes = 2 * kBlk * D * 2;
+  // and row-half offsets are immediates).
+  //   bf16: lane t of a 16-lane group points at 4 elements of key row
+  //     4*hh + (t >> 2) (+16 ks + 8 r), column block 4*db + its chunk within the
+  //     16 columns of the group.
+  //   FP8: lane t points at the 8 bytes of key row 8 (e >> 2) + 4 hh + (e & 3),
+  //     e = t >> 1 (+16 ks), columns 32 db + 16 (group parity) + 8 (t & 1).
+  constexpr int kStageBytes = 2 * kBlk * ROWB;
   uint32_t vaddr[DBLK];
   {
     const int t16 = lane & 15;
-    const int vrow = 4 * hh + (t16 >> 2);
-    const int vx = vswz<CH>(t16 >> 2);
-    const int vcol = 2 * ((lane >> 4) & 1) + ((t16 & 3) >> 1);
     const uint32_t ring0 = lds_addr(sm.u.ring[wave][0][0]);
+    if constexpr (FP8) {
+      const int e = t16 >> 1;
+      const int vrow = 8 * (e >> 2) + 4 * hh + (e & 3);
+      const int vx = vswz8<D>(vrow);
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db)
-      vaddr[db] = ring0 + (uint32_t)((vrow * D + 8 * ((4 * db + vcol) ^ vx) + 4 * (t16 & 1)) * 2);
+      for (int db = 0; db < DBLK; ++db)
+        vaddr[db] = ring0 + (uint32_t)(vrow * ROWB + 16 * ((2 * db + ((lane >> 4) & 1)) ^ vx) +
+                                       8 * (t16 & 1));
+    } else {
+      const int vrow = 4 * hh + (t16 >> 2);
+      const int vx = vswz<CH>(t16 >> 2);
+      const int vcol = 2 * ((lane >> 4) & 1) + ((t16 & 3) >> 1);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+        vaddr[db] = ring0 + (uint32_t)((vrow * D + 8 * ((4 * db + vcol) ^ vx) + 4 * (t16 & 1)) * 2);
+    }
   }
 
   auto block = [&](int t, auto stage_c) {
@@ -591,14 +669,25 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     const bool refill = t + NB < nmine;
 
     wait_halves<H, 2 * NB - 1>(1 + 2 * ahead);  // K of block t has landed
-    const uint16_t *ks_ = sm.u.ring[wave][S][0];
+    const uint8_t *ks_ = sm.u.ring[wave][S][0];
     f32x16 sc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sc[e] = 0.f;
+    if constexpr (FP8) {
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const u32x4 a = *reinterpret_cast<const u32x4 *>(ks_ + l32 * D + 8 * ((2 * kk + hh) ^ kx));
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[kk], sc, 0, 0, 0);
+      for (int kp = 0; kp < KSTEPS / 2; ++kp) {
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(ks_ + l32 * ROWB + 16 * ((2 * kp + hh) ^ kx));
+        const u32x4 a0 = fp8x8_to_bf16x8(w[0], w[1]);
+        const u32x4 a1 = fp8x8_to_bf16x8(w[2], w[3]);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), qf[2 * kp], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), qf[2 * kp + 1], sc, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(ks_ + l32 * ROWB + 16 * ((2 * kk + hh) ^ kx));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[kk], sc, 0, 0, 0);
+      }
     }
     if (refill) {
       wait_lds();
@@ -617,7 +706,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
 #pragma unroll
     for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(mrun, mx * scale_log2);
+    const float mnew = fmaxf(mrun, mx * sl);
     // lazy rescale: keep the reference max until some column's max has grown
     // by more than 2^8 (p stays <= 256, exact in fp32 sums, fine in bf16)
     if (__builtin_amdgcn_ballot_w64(mnew > mrun + 8.f) != 0) {
@@ -632,7 +721,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     float p[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], scale_log2, -mrun));
+      p[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], sl, -mrun));
       lsum += p[e];
     }
     bf16x8 pf[2];
@@ -647,13 +736,24 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     wait_halves<H, 2 * NB - 1>(2 * ahead + (refill ? 1 : 0));  // V of block t has landed
     auto pv_step = [&](auto ks_c) {
       constexpr int KS = decltype(ks_c)::value;
-      u32x2 h2[DBLK][2];
-      tr_reads<DBLK, S * kStageBytes + kBlk * D * 2 + KS * 16 * D * 2, 8 * D * 2>(h2, vaddr);
+      if constexpr (FP8) {
+        u32x2 b8[DBLK];
+        tr8_reads<DBLK, S * kStageBytes + kBlk * ROWB + KS * 16 * ROWB>(b8, vaddr);
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const u32x4 a = {h2[db][0][0], h2[db][0][1], h2[db][1][0], h2[db][1][1]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[KS],
-                                                        o[db], 0, 0, 0);
+        for (int db = 0; db < DBLK; ++db) {
+          const u32x4 a = fp8x8_to_bf16x8(b8[db][0], b8[db][1]);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[KS],
+                                                          o[db], 0, 0, 0);
+        }
+      } else {
+        u32x2 h2[DBLK][2];
+        tr_reads<DBLK, S * kStageBytes + kBlk * ROWB + KS * 16 * ROWB, 8 * ROWB>(h2, vaddr);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          const u32x4 a = {h2[db][0][0], h2[db][0][1], h2[db][1][0], h2[db][1][1]};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[KS],
+                                                          o[db], 0, 0, 0);
+        }
       }
     };
     pv_step(std::integral_constant<int, 0>{});
@@ -701,7 +801,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
       den += s * sm.u.comb.l[w][gi];
     }
     const long long row = ((long long)b * Hq + hk * g + gi) * nsplit + split;
-    part_o[row * D + d] = num / den;
+    part_o[row * D + d] = num / den * vsc;
     if (d == 0) part_lse[row] = M + __log2f(den);
   }
 }
@@ -805,16 +905,15 @@ hipError_t launch_split_g(const DecodeArgs &a, hipStream_t s) {
   return launch_split<T, D, 16>(a, s);
 }
 
-template <int D>
+template <int D, bool FP8>
 hipError_t launch_mfma(const DecodeArgs &a, hipStream_t s) {
   constexpr int W = kMfmaWaves, NB = kMfmaStages;
   const long long blocks = (long long)a.B * a.Hkv * a.nsplit;
   const float scale_log2 = (float)((double)a.softmax_scale * 1.4426950408889634074);
-  hipLaunchKernelGGL((decode_mfma_kernel<D, W, NB>), dim3((unsigned)blocks), dim3(W * 64), 0, s,
-                     (const uint16_t *)a.q, (const uint16_t *)a.k_cache,
-                     (const uint16_t *)a.v_cache, a.seqlens, a.q_pos, a.B, a.max_cache_len, a.Hq,
-                     a.Hkv, a.theta, scale_log2, a.chunk, a.nsplit, a.part_o, a.part_lse,
-                     a.dev_flag, a.window, a.sinks);
+  hipLaunchKernelGGL((decode_mfma_kernel<D, W, NB, FP8>), dim3((unsigned)blocks), dim3(W * 64), 0,
+                     s, (const uint16_t *)a.q, a.k_cache, a.v_cache, a.seqlens, a.q_pos, a.B,
+                     a.max_cache_len, a.Hq, a.Hkv, a.theta, scale_log2, a.chunk, a.nsplit,
+                     a.part_o, a.part_lse, a.dev_flag, a.window, a.sinks, a.k_scale, a.v_scale);
   return hipGetLastError();
 }
 
@@ -844,8 +943,10 @@ int decode_chunk(int B, int max_cache_len, int Hkv) {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   hipError_t e;
-  if (a.in_dtype == YR_BF16)
-    e = a.head_dim == 64 ? launch_mfma<64>(a, s) : launch_mfma<128>(a, s);
+  if (a.in_dtype == YR_FP8_E4M3)
+    e = a.head_dim == 64 ? launch_mfma<64, true>(a, s) : launch_mfma<128, true>(a, s);
+  else if (a.in_dtype == YR_BF16)
+    e = a.head_dim == 64 ? launch_mfma<64, false>(a, s) : launch_mfma<128, false>(a, s);
   else
     e = a.head_dim == 64 ? launch_split_g<float, 64>(a, s) : launch_split_g<float, 128>(a, s);
   if (e != hipSuccess) return e;

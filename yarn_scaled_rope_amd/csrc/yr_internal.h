@@ -81,6 +81,8 @@ struct DecodeArgs {
   int *dev_flag;
   int window;            // 0 = every cache row
   int sinks;
+  const float *k_scale;  // YR_FP8_E4M3 caches: per-KV-head scales
+  const float *v_scale;
 };
 
 hipError_t launch_rope(const RopeArgs &a, hipStream_t s);

@@ -25,6 +25,7 @@ YR_ERR_DEVICE_RANGE = 6
 
 YR_F32 = 0
 YR_BF16 = 1
+YR_FP8_E4M3 = 2
 
 YR_ROPE_PLAIN = 0
 YR_ROPE_PI = 1
@@ -64,6 +65,8 @@ def _declare(lib):
                                    vp, vp, sz, vp]),
         "attn_decode_workspace_bytes": (sz, [i, i, i, i]),
         "attn_decode": (i, [vp, vp, vp, i, vp, vp, i, i, i, i, i, vp, f, i, i, vp, i, vp, vp, sz, vp]),
+        "attn_decode_fp8": (i, [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, f, i, i, vp, i, vp, vp,
+                                sz, vp]),
         "yr_read_device_error": (i, [vp, vp, vp]),
         "yr_status_string": (ctypes.c_char_p, [i]),
         "yr_last_error": (ctypes.c_char_p, []),
@@ -302,6 +305,45 @@ def attn_decode(q, k_cache, v_cache, seqlens, inv_freq_f64, softmax_scale: float
                            float(softmax_scale), int(window), int(sinks), _ptr(out), out_code,
                            _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
                            _stream(stream)))
+    return out, lse
+
+
+def attn_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, seqlens, inv_freq_f64,
+                    softmax_scale: float, q_pos=None, out=None, out_dtype=None, lse=None,
+                    workspace=None, want_lse=True, window: int = 0, sinks: int = 0, stream=None):
+    """attn_decode over an FP8 (E4M3) cache: q bf16 [B, Hq, D]; caches uint8
+    [B, Lmax, Hkv, D] of E4M3 codes standing for code * k_scale[h] /
+    code * v_scale[h] (float32 [Hkv]).  Returns (out, lse)."""
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.uint8)
+    _need(v_cache, "v_cache", torch.uint8)
+    _need(k_scale, "k_scale", torch.float32)
+    _need(v_scale, "v_scale", torch.float32)
+    _need(seqlens, "seqlens", torch.int32)
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int32)
+    if inv_freq_f64 is not None:
+        _need(inv_freq_f64, "inv_freq_f64", torch.float64)
+    B, hq, D = q.shape
+    _, lmax, hkv, _ = k_cache.shape
+    if k_cache.shape != (B, lmax, hkv, D) or v_cache.shape != k_cache.shape:
+        raise YarnAttnError(YR_ERR_INVALID, "caches must be [B, Lmax, Hkv, D]")
+    if k_scale.numel() != hkv or v_scale.numel() != hkv:
+        raise YarnAttnError(YR_ERR_INVALID, "k_scale and v_scale need Hkv entries")
+    out_code = YR_BF16 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, hq, D), dtype=_torch_dtype(out_code), device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(attn_decode_workspace_bytes(B, lmax, hq, D), dtype=torch.uint8,
+                                device=q.device)
+    lib = load_library()
+    _check(lib.attn_decode_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                               _ptr(v_scale), _ptr(seqlens), _ptr(q_pos), B, lmax, hq, hkv, D,
+                               _ptr(inv_freq_f64), float(softmax_scale), int(window), int(sinks),
+                               _ptr(out), out_code, _ptr(lse), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
 
 

@@ -195,6 +195,44 @@ def make_decode(cfg: DecodeConfig, seed: int | None = None, batch=None,
             "seqlens": seqlens, "dtype": cfg.dtype}
 
 
+E4M3_NAN_CODE = 0x7F
+
+
+def e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """float32 values -> OCP E4M3 byte codes (round to nearest even, by
+    torch's float8_e4m3fn conversion); callers keep |x| <= 448."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def make_decode_fp8(cfg: DecodeConfig, seed: int | None = None, batch=None, max_cache_len=None,
+                    min_cache_len=None):
+    """FP8-cache decode inputs: the cache lengths, q (bf16) and K/V values
+    drawn like make_decode; per-KV-head scales 2^-6 * (1 + h/4) for K and
+    2^-6 * (1 + h/8) for V; each cache element stored as the E4M3 code of
+    value / scale; rows past a sequence's length hold the NaN code."""
+    B = cfg.batch if batch is None else batch
+    lmax = cfg.max_cache_len if max_cache_len is None else max_cache_len
+    lmin = cfg.min_cache_len if min_cache_len is None else min_cache_len
+    rng = np.random.Generator(np.random.PCG64(1000 + cfg.index if seed is None else seed))
+    seqlens = rng.integers(lmin, lmax, size=B, endpoint=True).astype(np.int32)
+    q = _draw(rng, (B, cfg.hq, cfg.head_dim), "bf16")
+    h = np.arange(cfg.hkv, dtype=np.float32)
+    scales = [(np.float32(2.0 ** -6) * (1.0 + h / 4.0)).astype(np.float32),
+              (np.float32(2.0 ** -6) * (1.0 + h / 8.0)).astype(np.float32)]
+    caches = []
+    for sc in scales:
+        c = np.full((B, lmax, cfg.hkv, cfg.head_dim), E4M3_NAN_CODE, dtype=np.uint8)
+        for b in range(B):
+            L = int(seqlens[b])
+            x = _draw(rng, (L, cfg.hkv, cfg.head_dim), "f32")
+            c[b, :L] = e4m3_codes(x / sc[None, :, None])
+        caches.append(c)
+    return {"q": q, "k_cache": caches[0], "v_cache": caches[1], "k_scale": scales[0],
+            "v_scale": scales[1], "seqlens": seqlens, "dtype": "bf16"}
+
+
 def make_chunk(cfg: ChunkConfig, seed: int | None = None, ctx_lens=None, chunk_lens=None,
                max_cache_len=None):
     """Chunked-prefill inputs: q [Tq, Hq, D] for the new tokens (packed);
