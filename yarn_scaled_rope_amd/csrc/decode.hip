@@ -471,7 +471,8 @@ __device__ __forceinline__ void tr8_reads(u32x2 (&r)[DBLK], const uint32_t (&a)[
   }
 }
 
-template <int D, int W, int NB, bool FP8>
+// WIN: sliding window / sinks (compiled out without it)
+template <int D, int W, int NB, bool FP8, bool WIN>
 __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     const uint16_t *__restrict__ q, const void *__restrict__ kc,
     const void *__restrict__ vc, const int *__restrict__ seqlens,
@@ -479,6 +480,10 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     const double *__restrict__ theta, float scale_log2, int chunk, int nsplit,
     float *__restrict__ part_o, float *__restrict__ part_lse, int *flag, int window, int sinks,
     const float *__restrict__ k_scale, const float *__restrict__ v_scale) {
+  if constexpr (!WIN) {
+    window = 0;
+    sinks = 0;
+  }
   constexpr int EB = FP8 ? 1 : 2;  // bytes per cached element
   constexpr int ROWB = D * EB;     // bytes per cached key row
   constexpr int CH = ROWB / 16;    // 16-byte chunks per row
@@ -905,12 +910,12 @@ hipError_t launch_split_g(const DecodeArgs &a, hipStream_t s) {
   return launch_split<T, D, 16>(a, s);
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool WIN>
 hipError_t launch_mfma(const DecodeArgs &a, hipStream_t s) {
   constexpr int W = kMfmaWaves, NB = kMfmaStages;
   const long long blocks = (long long)a.B * a.Hkv * a.nsplit;
   const float scale_log2 = (float)((double)a.softmax_scale * 1.4426950408889634074);
-  hipLaunchKernelGGL((decode_mfma_kernel<D, W, NB, FP8>), dim3((unsigned)blocks), dim3(W * 64), 0,
+  hipLaunchKernelGGL((decode_mfma_kernel<D, W, NB, FP8, WIN>), dim3((unsigned)blocks), dim3(W * 64), 0,
                      s, (const uint16_t *)a.q, a.k_cache, a.v_cache, a.seqlens, a.q_pos, a.B,
                      a.max_cache_len, a.Hq, a.Hkv, a.theta, scale_log2, a.chunk, a.nsplit,
                      a.part_o, a.part_lse, a.dev_flag, a.window, a.sinks, a.k_scale, a.v_scale);
@@ -943,10 +948,13 @@ int decode_chunk(int B, int max_cache_len, int Hkv) {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   hipError_t e;
+  const bool win = a.window > 0;
   if (a.in_dtype == YR_FP8_E4M3)
-    e = a.head_dim == 64 ? launch_mfma<64, true>(a, s) : launch_mfma<128, true>(a, s);
+    e = a.head_dim == 64 ? (win ? launch_mfma<64, true, true>(a, s) : launch_mfma<64, true, false>(a, s))
+                         : (win ? launch_mfma<128, true, true>(a, s) : launch_mfma<128, true, false>(a, s));
   else if (a.in_dtype == YR_BF16)
-    e = a.head_dim == 64 ? launch_mfma<64, false>(a, s) : launch_mfma<128, false>(a, s);
+    e = a.head_dim == 64 ? (win ? launch_mfma<64, false, true>(a, s) : launch_mfma<64, false, false>(a, s))
+                         : (win ? launch_mfma<128, false, true>(a, s) : launch_mfma<128, false, false>(a, s));
   else
     e = a.head_dim == 64 ? launch_split_g<float, 64>(a, s) : launch_split_g<float, 128>(a, s);
   if (e != hipSuccess) return e;

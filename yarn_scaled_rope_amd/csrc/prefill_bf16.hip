@@ -56,6 +56,7 @@ constexpr int kBQ = kThreads / 2;  // query rows per workgroup (32 per wave)
 constexpr int kBC = 64;            // keys per tile
 constexpr int kStages = 2;         // LDS stages of K and of V (2 or 3; 3 measured no faster)
 constexpr int kXcds = 8;
+constexpr int kMaxRankedSeqs = 64;  // chunked prefill orders up to this many sequences
 constexpr float kLn2 = 0.69314718055994530942f;
 
 // V chunk swizzle by key row mod 4: for 16 lanes of a transposing read (4 key
@@ -85,7 +86,9 @@ __device__ __forceinline__ void static_for(F &&f) {
   }
 }
 
-template <int D, bool OUT_F32, bool ROTATE_Q>
+// EXT: keys from a cache with a prefix (chunked prefill) and / or a sliding
+// window with sinks; without it those are compiled out (plain causal).
+template <int D, bool OUT_F32, bool ROTATE_Q, bool EXT>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int *__restrict__ cu, int B, int max_seqlen,
@@ -99,6 +102,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   constexpr int DPW = kBC / RPI / (kThreads / 64);  // copy instructions per wave per tile
   constexpr int TILE = kBC * D;      // elements of a K or V tile
 
+  if constexpr (!EXT) {
+    kv_len = 0;
+    ctx = nullptr;
+    window = 0;
+    sinks = 0;
+  }
   constexpr int NS = kStages;
   static_assert(NS == 2 || NS == 3, "two or three stages");
   constexpr int TILE3 = NS > 2 ? TILE : 8;
@@ -111,12 +120,48 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     validate_cu_seqlens(cu, B, T, max_seqlen, flag, kv_len > 0 ? ctx : nullptr, kv_len);
 
   // ---- block -> (q-tile, sequence, head): longest first, XCD-grouped heads
-  const int per = B * Hq;
-  const int tile = ntiles - 1 - (int)(blockIdx.x / per);
-  int r = (int)(blockIdx.x % per);
-  if (per % kXcds == 0) r = (r % kXcds) * (per / kXcds) + r / kXcds;
-  const int b = r / Hq;
-  const int h = r % Hq;
+  // Packed prefill: q-tiles from the last (the work of a tile grows with its
+  // index), every sequence and head at each tile index.  Chunked prefill:
+  // a tile's work is dominated by its sequence's cached prefix, so the
+  // sequences go longest first (by prefix + chunk keys), each with all its
+  // q-tiles and heads; consecutive blocks spread a tile's heads over the XCDs
+  // so that the heads of one KV head share an L2.
+  int tile, b, h;
+  if (kv_len > 0 && B <= kMaxRankedSeqs) {
+    __shared__ int ranked_b;
+    const int per = ntiles * Hq;
+    const int rank = (int)(blockIdx.x / per);
+    const int rem = (int)(blockIdx.x % per);
+    tile = ntiles - 1 - rem / Hq;
+    int hr = rem % Hq;
+    if (Hq % kXcds == 0) hr = (hr % kXcds) * (Hq / kXcds) + hr / kXcds;
+    h = hr;
+    if (threadIdx.x == 0) ranked_b = B;  // rank past the last sequence: no work
+    __syncthreads();
+    for (int i = threadIdx.x; i < B; i += blockDim.x) {
+      auto keys = [&](int j) {
+        const int c = ctx != nullptr ? ctx[j] : 0;
+        return (long long)(c < 0 ? 0 : c) + (cu[j + 1] - cu[j]);
+      };
+      const long long ki = keys(i);
+      int rk = 0;
+      for (int j = 0; j < B; ++j) {
+        const long long kj = keys(j);
+        rk += (kj > ki) || (kj == ki && j < i);
+      }
+      if (rk == rank) ranked_b = i;
+    }
+    __syncthreads();
+    b = ranked_b;
+    if (b >= B) return;
+  } else {
+    const int per = B * Hq;
+    tile = ntiles - 1 - (int)(blockIdx.x / per);
+    int r = (int)(blockIdx.x % per);
+    if (per % kXcds == 0) r = (r % kXcds) * (per / kXcds) + r / kXcds;
+    b = r / Hq;
+    h = r % Hq;
+  }
   const int hk = h / (Hq / Hkv);
   long long s0;
   int n;
@@ -476,30 +521,32 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   if (lse != nullptr && hh == 0) lse[(long long)h * T + s0 + tq] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
-template <int D, bool OUT_F32, bool ROT>
+template <int D, bool OUT_F32, bool ROT, bool EXT>
 hipError_t launch_one(const PrefillArgs &a, hipStream_t s) {
   const int ntiles = (a.max_seqlen + kBQ - 1) / kBQ;
   const long long blocks = (long long)ntiles * a.B * a.Hq;
   const float scale_log2 = (float)((double)a.softmax_scale * 1.4426950408889634074);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_F32, ROT>), dim3((unsigned)blocks), dim3(kThreads),
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_F32, ROT, EXT>), dim3((unsigned)blocks), dim3(kThreads),
                      0, s, (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                      a.cu_seqlens, a.B, a.max_seqlen, a.T, a.Hq, a.Hkv, a.theta, scale_log2, a.out,
                      a.lse, ntiles, a.dev_flag, a.kv_cache_len, a.ctx_lens, a.window, a.sinks);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool EXT>
 hipError_t launch_d(const PrefillArgs &a, hipStream_t s) {
   const bool f32 = a.out_dtype == YR_F32;
   const bool rot = a.theta != nullptr;
-  if (f32) return rot ? launch_one<D, true, true>(a, s) : launch_one<D, true, false>(a, s);
-  return rot ? launch_one<D, false, true>(a, s) : launch_one<D, false, false>(a, s);
+  if (f32) return rot ? launch_one<D, true, true, EXT>(a, s) : launch_one<D, true, false, EXT>(a, s);
+  return rot ? launch_one<D, false, true, EXT>(a, s) : launch_one<D, false, false, EXT>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s) {
-  return a.head_dim == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
+  if (a.kv_cache_len > 0 || a.window > 0)
+    return a.head_dim == 64 ? launch_d<64, true>(a, s) : launch_d<128, true>(a, s);
+  return a.head_dim == 64 ? launch_d<64, false>(a, s) : launch_d<128, false>(a, s);
 }
 
 }  // namespace yr
