@@ -162,7 +162,7 @@ def bench_prefill(args, torch, ops, wl):
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_from_profiles("prefill_bf16", cfg.name, digest),
-            "kernel": "prefill_bf16_kernel<128,false,true>", "kernel_ms": round(attn_ms, 4),
+            "kernel": "prefill_bf16_kernel<128,false,true,false>", "kernel_ms": round(attn_ms, 4),
             "flops_per_launch": flops}
     extra = {"rope_pass_ms": round(rope_ms, 4), "freqs_host_us": round(a1_us, 2),
              "wall_ms_per_step": round(ms_per_step, 4), "source_digest": digest}
@@ -232,7 +232,7 @@ def bench_decode(args, torch, ops, wl):
            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                         "traffic": traffic_from_profiles("decode", cfg.name, digest),
-                        "kernel": "decode_mfma_kernel + decode_merge_kernel (one call)",
+                        "kernel": "decode_mfma_kernel<128,4,1,false,false> + decode_merge_kernel<128,false> (one call)",
                         "kernel_ms": round(call_ms, 4), "bytes_per_launch": int(nbytes)},
            "source_digest": digest}
     state = {"seqlens": inp["seqlens"], "sl": sl, "q": q, "kc": kc, "vc": vc, "theta": theta,
