@@ -234,6 +234,7 @@ def _decode_oracle(inp, cfg, window, sinks, q_pos=None):
     ("bf16", 5, 3000, 1, 8, 2, 128, 700, 4),
     ("bf16", 4, 5000, 2500, 32, 8, 128, 2100, 40),   # window across chunk edges
     ("bf16", 3, 900, 1, 16, 1, 64, 64, 1),
+    ("bf16", 5, 3000, 1, 8, 2, 128, 5000, 2),  # window past the cache: chunks over [0, L)
     ("f32", 4, 3000, 1, 8, 2, 128, 500, 3),
     ("f32", 3, 257, 1, 4, 1, 64, 2, 0),
 ])
@@ -262,6 +263,22 @@ def test_decode_window_q_pos_and_empty():
     ro, rl = _decode_oracle(inp, cfg, 300, 0, q_pos=q_pos[:2].tolist() + [0])
     assert max_abs(out[:2], ro[:2]) <= BF16_TOL and max_abs(lse[:2], rl[:2]) <= BF16_TOL
     assert np.all(out[2] == 0.0) and np.all(np.isneginf(lse[2]))
+
+
+def test_decode_window_q_pos_sinks():
+    """Queries placed well inside the cache with sinks: the visible rows run
+    past the usual window length, so the last chunk of the visible rows takes
+    the long tail."""
+    cfg = wl.DecodeConfig("t", 88, 0, 0, 0, 8, 2, 128, "bf16", 500000.0, 8.0, 16384)
+    inp = wl.make_decode(cfg, seed=88, batch=3, max_cache_len=4000, min_cache_len=3000)
+    L = inp["seqlens"]
+    q_pos = np.array([L[0] // 3, 10, L[2] - 1], dtype=np.int32)
+    say(f"windowed decode q_pos={list(q_pos)} seqlens={list(L)} W=256 S=7")
+    out, lse = _decode_run(inp, cfg, 256, 7, q_pos=q_pos)
+    ro, rl = _decode_oracle(inp, cfg, 256, 7, q_pos=q_pos.tolist())
+    e_out, e_lse = max_abs(out, ro), max_abs(lse, rl)
+    print(f"max-abs out {e_out:.3e} lse {e_lse:.3e}")
+    assert e_out <= BF16_TOL and e_lse <= BF16_TOL
 
 
 def test_decode_window_workload_full():

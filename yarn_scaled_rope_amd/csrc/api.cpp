@@ -1,6 +1,7 @@
 // C-ABI entry points of libyarnattn.so: host-side validation, workspace
 // layout and kernel launches.  Every entry point checks its arguments before
 // touching the device, returns a status and never throws.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -314,8 +315,23 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
   const size_t need = attn_decode_workspace_bytes(B, max_cache_len, Hq, head_dim);
   if (workspace_bytes < need) return bad(YR_ERR_WORKSPACE, "workspace too small");
 
-  const int chunk = decode_chunk(B, max_cache_len, Hkv);
-  const int nsplit = decode_nsplit(max_cache_len, chunk);
+  int chunk = decode_chunk(B, max_cache_len, Hkv);
+  int nsplit = decode_nsplit(max_cache_len, chunk);
+  // With a window the matrix-core sweep can split the visible rows alone
+  // (normally window - 1 + sinks of them) instead of the whole cache, so that
+  // no workgroup starts on rows nobody reads; the workspace is sized for the
+  // finer split of the whole cache, so this applies when it needs fewer chunks.
+  int vis_split = 0;
+  if (window > 0 && cache_dtype != YR_F32) {
+    const int span = (int)std::min<long long>(max_cache_len, (long long)window + sinks);
+    const int cw = decode_chunk(B, span, Hkv);
+    const int nw = decode_nsplit(span, cw);
+    if (nw < nsplit) {
+      chunk = cw;
+      nsplit = nw;
+      vis_split = 1;
+    }
+  }
   if ((long long)B * Hkv * nsplit > 0x7fffffffLL) return bad(YR_ERR_INVALID, "grid too large");
   const size_t rows = (size_t)B * Hq * nsplit;
   char *ws = static_cast<char *>(workspace);
@@ -345,6 +361,7 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
   d.sinks = sinks;
   d.k_scale = k_scale;
   d.v_scale = v_scale;
+  d.vis_split = vis_split;
   const hipError_t e = launch_decode(d, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, fn);
   return YR_OK;

@@ -479,10 +479,11 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     const int *__restrict__ qpos, int B, int Lmax, int Hq, int Hkv,
     const double *__restrict__ theta, float scale_log2, int chunk, int nsplit,
     float *__restrict__ part_o, float *__restrict__ part_lse, int *flag, int window, int sinks,
-    const float *__restrict__ k_scale, const float *__restrict__ v_scale) {
+    const float *__restrict__ k_scale, const float *__restrict__ v_scale, int vis_split) {
   if constexpr (!WIN) {
     window = 0;
     sinks = 0;
+    vis_split = 0;
   }
   constexpr int EB = FP8 ? 1 : 2;  // bytes per cached element
   constexpr int ROWB = D * EB;     // bytes per cached key row
@@ -505,9 +506,8 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
   const int g = Hq / Hkv;
   int L = seqlens[b];
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-  const int c0 = split * chunk;
-  if (c0 >= L) return;
-  const int c1 = min(L, c0 + chunk);
+  int c0 = split * chunk;
+  if (vis_split == 0 && c0 >= L) return;
   int qm = qpos != nullptr ? qpos[b] : L;  // the query's position
   qm = qm < 0 ? 0 : qm;
 
@@ -521,14 +521,28 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
   // Visible cache rows: the sinks [0, se) and the window [lo, L) (no window:
   // all of [0, L)).  This chunk sweeps its share of each as 32-key blocks:
   // blocks 0 .. nba-1 cover [c0, c0 + na), the rest cover [b0, b0 + nb).
+  // Chunks split the cache rows [0, L), or (vis_split) the visible rows
+  // alone, counted in order: the sinks, then the window; the last chunk then
+  // takes every visible row from its start on, so any query position is
+  // covered.
   int lo = 0, se = 0;
   if (window > 0) {
     lo = max(0, qm - window + 1);
     se = min(sinks, lo);
   }
-  const int na = max(0, min(c1, se) - c0);
-  const int b0 = max(c0, lo);
-  const int nb = max(0, c1 - b0);
+  int na, b0, nb;
+  if (vis_split != 0) {
+    const int nvis = se + max(0, L - lo);
+    const int v1 = split == nsplit - 1 ? nvis : min(nvis, c0 + chunk);
+    na = max(0, min(v1, se) - c0);
+    b0 = lo + max(c0, se) - se;
+    nb = max(0, v1 - max(c0, se));
+  } else {
+    const int c1 = min(L, c0 + chunk);
+    na = max(0, min(c1, se) - c0);
+    b0 = max(c0, lo);
+    nb = max(0, c1 - b0);
+  }
   const int nba = (na + kBlk - 1) / kBlk;
   const int nblk = nba + (nb + kBlk - 1) / kBlk;
   if (nblk == 0) {
@@ -814,7 +828,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float *__restrict__ part_o, const float *__restrict__ part_lse,
-    const int *__restrict__ seqlens, int Hq, int Lmax, int chunk, int nsplit,
+    const int *__restrict__ seqlens, int Hq, int Lmax, int chunk, int nsplit, int vis_split,
     void *__restrict__ out, float *__restrict__ lse) {
   constexpr int PER = D / 64;  // output elements per lane
   constexpr int MW = 4;        // waves; wave w takes partials w, w+4, ...
@@ -827,7 +841,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int wave = threadIdx.x >> 6;
   int L = seqlens[b];
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-  const int nv = (L + chunk - 1) / chunk;
+  // partials written: every chunk of the visible rows, or the chunks of
+  // [0, L) (those starting past L exit without one)
+  const int nv = vis_split != 0 ? nsplit : (L + chunk - 1) / chunk;
   const long long row0 = ((long long)b * Hq + h) * nsplit;
 
   // common reference: the largest partial log2-sum-exp (every wave computes it)
@@ -918,7 +934,8 @@ hipError_t launch_mfma(const DecodeArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((decode_mfma_kernel<D, W, NB, FP8, WIN>), dim3((unsigned)blocks), dim3(W * 64), 0,
                      s, (const uint16_t *)a.q, a.k_cache, a.v_cache, a.seqlens, a.q_pos, a.B,
                      a.max_cache_len, a.Hq, a.Hkv, a.theta, scale_log2, a.chunk, a.nsplit,
-                     a.part_o, a.part_lse, a.dev_flag, a.window, a.sinks, a.k_scale, a.v_scale);
+                     a.part_o, a.part_lse, a.dev_flag, a.window, a.sinks, a.k_scale, a.v_scale,
+                     a.vis_split);
   return hipGetLastError();
 }
 
@@ -927,10 +944,12 @@ hipError_t launch_merge(const DecodeArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.Hq)), block(256);
   if (a.out_dtype == YR_F32)
     hipLaunchKernelGGL((decode_merge_kernel<D, true>), grid, block, 0, s, a.part_o, a.part_lse,
-                       a.seqlens, a.Hq, a.max_cache_len, a.chunk, a.nsplit, a.out, a.lse);
+                       a.seqlens, a.Hq, a.max_cache_len, a.chunk, a.nsplit, a.vis_split, a.out,
+                       a.lse);
   else
     hipLaunchKernelGGL((decode_merge_kernel<D, false>), grid, block, 0, s, a.part_o, a.part_lse,
-                       a.seqlens, a.Hq, a.max_cache_len, a.chunk, a.nsplit, a.out, a.lse);
+                       a.seqlens, a.Hq, a.max_cache_len, a.chunk, a.nsplit, a.vis_split, a.out,
+                       a.lse);
   return hipGetLastError();
 }
 

@@ -83,6 +83,7 @@ struct DecodeArgs {
   int sinks;
   const float *k_scale;  // YR_FP8_E4M3 caches: per-KV-head scales
   const float *v_scale;
+  int vis_split;         // 1: chunks split the visible rows (window), not [0, L)
 };
 
 hipError_t launch_rope(const RopeArgs &a, hipStream_t s);
