@@ -44,6 +44,33 @@ def test_rope_apply_matches_oracle(dtype, T, H, D, base, s, L):
         assert np.all(np.abs(got - ref) <= ulp + 1e-6)
 
 
+@pytest.mark.parametrize("dtype,off", [("bf16", 2), ("f32", 1), ("bf16", 8)])
+def test_rope_apply_unaligned_buffer(dtype, off):
+    """A buffer that is not 16-byte aligned (a view at an element offset) takes
+    the per-pair kernel; off = 8 bf16 elements is 16-byte aligned again and
+    takes the 16-byte one: both match the oracle and each other bit for bit."""
+    T, H, D = 300, 6, 128
+    rng = np.random.Generator(np.random.PCG64(7 + off))
+    x32 = rng.standard_normal((T, H, D), dtype=np.float32)
+    x = wl.round_to_bf16_bits(x32) if dtype == "bf16" else x32
+    pos = rng.integers(0, 70000, size=T).astype(np.int32)
+    th_dev, _ = lib_theta(D, 500000.0, 8.0, 16384)
+    th_ref, _ = oracle_theta(D, 500000.0, 8.0, 16384)
+    say(f"rope_apply {dtype} at element offset {off}")
+    base = to_dev(x, dtype)
+    flat = torch.zeros(T * H * D + off, dtype=base.dtype, device="cuda")
+    view = flat[off:].view(T, H, D)
+    view.copy_(base)
+    pos_d = torch.from_numpy(pos).cuda()
+    ops.rope_apply(view, pos_d, th_dev)
+    ops.rope_apply(base, pos_d, th_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(view, base)
+    assert torch.all(flat[:off] == 0)
+    err = max_abs(to_f64(view), orope.rotate(wl.as_f64(x, dtype), pos, th_ref))
+    assert err <= (F32_TOL if dtype == "f32" else BF16_TOL), err
+
+
 def test_rope_apply_position_zero_is_identity():
     D = 128
     th_dev, _ = lib_theta(D, 500000.0, 8.0, 16384)
