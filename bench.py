@@ -274,6 +274,11 @@ def bench_next(args, torch, ops, wl, pstate, dstate):
     def up(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
 
+    # host copy of sequence 0 (its cached rows and new tokens) for the oracle
+    # sample, before the full caches are dropped
+    n0, ctx0 = int(cfg.chunk_lens[0]), int(cfg.ctx_lens[0])
+    chunk_host = {"q": np.array(inp["q"][:n0]), "k": np.array(inp["k_cache"][0:1, :ctx0 + n0]),
+                  "v": np.array(inp["v_cache"][0:1, :ctx0 + n0]), "n": n0, "ctx": ctx0}
     q, kc = up(inp["q"]), up(inp["k_cache"])
     del inp["k_cache"]
     vc = up(inp["v_cache"])
@@ -373,8 +378,124 @@ def bench_next(args, torch, ops, wl, pstate, dstate):
             "config": {"workload": wl.DECODE_B16.name + "_fp8_e4m3",
                        "inputs": "the decode line's cache, as E4M3 codes with per-KV-head "
                                  "scales amax/448"}}
-        del codes
+        fp8_state = {"codes": codes, "scales": scales}
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle on bounded samples of the next rows")
+        cpu_next(res, chunk_host, pstate, dstate, fp8_state if dstate is not None else None,
+                 wl, torch, args.cpu_next_seconds)
+    if dstate is not None:
+        del codes, fp8_state
     return res
+
+
+def cpu_next(res, chunk_host, pstate, dstate, fp8_state, wl, torch, seconds):
+    """The fp64 oracle, as it stands, beside each next row: a bounded sample of
+    the same inputs (about `seconds` of host work each), in the row's unit."""
+    import numpy as np
+    from oracle import attention as oatt
+    from oracle import fp8 as ofp8
+    from oracle import freqs as ofreqs
+    threads = oracle_threads()
+
+    def entry(value, unit, dt, sample):
+        return {"value": round(value, 5 if unit == "TFLOP/s" else 3), "unit": unit,
+                "cores": int(threads), "kind": "oracle", "seconds": round(dt, 2),
+                "sample": sample}
+
+    # chunked prefill: query heads of sequence 0's chunk, all its rows
+    cfg = wl.CHUNK_4X4K
+    th = ofreqs.yarn_theta(cfg.head_dim, cfg.base, cfg.factor, cfg.original_max_position)
+    sc = ofreqs.softmax_scale(cfg.head_dim, ofreqs.attention_temperature(cfg.factor))
+    h = chunk_host
+    q = wl.as_f64(h["q"], "bf16")
+    kc, vc = wl.as_f64(h["k"], "bf16"), wl.as_f64(h["v"], "bf16")
+    cu = np.array([0, h["n"]], dtype=np.int32)
+    ctx = np.array([h["ctx"]], dtype=np.int32)
+    heads, flops, t0 = 0, 0, time.perf_counter()
+    while heads < cfg.hq and time.perf_counter() - t0 < seconds:
+        oatt.prefill_chunk(q, kc, vc, cu, ctx, th, sc, rows=[(t, heads) for t in range(h["n"])])
+        flops += wl.prefill_visible_flops([h["n"]], 1, cfg.head_dim, ctx_lens=[h["ctx"]])
+        heads += 1
+    dt = time.perf_counter() - t0
+    res["chunked_prefill"]["cpu_baseline"] = entry(
+        flops / dt / 1e12, "TFLOP/s", dt,
+        f"fp64 chunked prefill of sequence 0 ({h['n']} new tokens after {h['ctx']} cached), "
+        f"query heads 0-{heads - 1}, same inputs")
+
+    # windowed prefill: the first query heads of the prefill inputs, all rows
+    pc = wl.LLAMA2_7B_16K_SWA
+    th = ofreqs.yarn_theta(pc.head_dim, pc.base, pc.factor, pc.original_max_position)
+    sc = ofreqs.softmax_scale(pc.head_dim, ofreqs.attention_temperature(pc.factor))
+    g = pc.hq // pc.hkv
+    qh = pstate["q"].view(torch.int16).cpu().numpy()
+    kh = pstate["k"].view(torch.int16).cpu().numpy()
+    vh = pstate["v"].view(torch.int16).cpu().numpy()
+    heads, flops, t0 = 0, 0, time.perf_counter()
+    while heads < pc.hq and time.perf_counter() - t0 < seconds:
+        hk = heads // g
+        oatt.prefill(wl.as_f64(qh[:, heads:heads + 1].view("uint16"), "bf16"),
+                     wl.as_f64(kh[:, hk:hk + 1].view("uint16"), "bf16"),
+                     wl.as_f64(vh[:, hk:hk + 1].view("uint16"), "bf16"),
+                     pstate["inp"]["cu_seqlens"], th, sc, window=pc.window, sinks=pc.sinks)
+        flops += wl.prefill_visible_flops(pc.seq_lens, 1, pc.head_dim, pc.window, pc.sinks)
+        heads += 1
+    dt = time.perf_counter() - t0
+    res["window_prefill"]["cpu_baseline"] = entry(
+        flops / dt / 1e12, "TFLOP/s", dt,
+        f"fp64 windowed prefill of query heads 0-{heads - 1}, all {pc.total_tokens} rows, "
+        f"same inputs")
+    if dstate is None:
+        return
+
+    # decode rows: sequences 0-3 of the decode inputs, whole passes
+    dc = wl.DECODE_B16
+    th = ofreqs.yarn_theta(dc.head_dim, dc.base, dc.factor, dc.original_max_position)
+    sc = ofreqs.softmax_scale(dc.head_dim, ofreqs.attention_temperature(dc.factor))
+    nseq = min(4, len(dstate["seqlens"]))
+    lens = [int(x) for x in dstate["seqlens"][:nseq]]
+
+    def host_bf16(t):
+        return wl.as_f64(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+
+    qs = [host_bf16(dstate["q"][b:b + 1]) for b in range(nseq)]
+    sw = wl.DECODE_B16_SWA
+    kv = [(host_bf16(dstate["kc"][b:b + 1, :lens[b]]), host_bf16(dstate["vc"][b:b + 1, :lens[b]]))
+          for b in range(nseq)]
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        for b in range(nseq):
+            oatt.decode(qs[b], kv[b][0], kv[b][1], dstate["seqlens"][b:b + 1], th, sc,
+                        window=sw.window, sinks=sw.sinks)
+        passes += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    nbytes = wl.decode_visible_bytes(dstate["seqlens"][:nseq], sw.hkv, sw.head_dim, sw.window,
+                                     sw.sinks) * passes
+    res["window_decode"]["cpu_baseline"] = entry(
+        nbytes / dt / 1e9, "GB/s", dt,
+        f"fp64 windowed decode of sequences 0-{nseq - 1} (cache lengths {lens}), {passes} "
+        f"whole passes, same inputs")
+    del kv
+
+    codes, scales = fp8_state["codes"], fp8_state["scales"]
+    ks, vs = scales[0].cpu().numpy(), scales[1].cpu().numpy()
+    c8 = [(codes[0][b:b + 1, :lens[b]].cpu().numpy(), codes[1][b:b + 1, :lens[b]].cpu().numpy())
+          for b in range(nseq)]
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        for b in range(nseq):
+            oatt.decode(qs[b], ofp8.dequantize_cache(c8[b][0], ks),
+                        ofp8.dequantize_cache(c8[b][1], vs), dstate["seqlens"][b:b + 1], th, sc)
+        passes += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    nbytes = wl.decode_kv_bytes(lens, dc.hkv, dc.head_dim, 1) * passes
+    res["fp8_decode"]["cpu_baseline"] = entry(
+        nbytes / dt / 1e9, "GB/s", dt,
+        f"fp64 decode of sequences 0-{nseq - 1} from their E4M3 caches (decoding included), "
+        f"{passes} whole passes, same inputs")
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -566,6 +687,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-next-seconds", type=float, default=3.0)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize", default=None)
     ap.add_argument("--counters-json", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None)
