@@ -385,6 +385,15 @@ def bench_next(args, torch, ops, wl, pstate, dstate):
                  wl, torch, args.cpu_next_seconds)
     if dstate is not None:
         del codes, fp8_state
+    # the roofline object of each row, in the main line's form (no counters
+    # are taken for these paths: traffic null)
+    for row in res.values():
+        hbm = row["unit"] == "GB/s"
+        row["roofline"] = {"bound": "hbm" if hbm else "mfma", "achieved": row["value"],
+                           "peak": PEAK_HBM_GBS if hbm else PEAK_BF16_TFLOPS,
+                           "unit": row["unit"],
+                           "frac": row["frac_hbm_peak" if hbm else "frac_mfma_peak"],
+                           "traffic": None}
     return res
 
 
