@@ -440,12 +440,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   };
   // Clear step: tiles i and i+1 of the list need no mask for any row (below
   // the diagonal of the workgroup's first row, inside the window of its last
-  // row) and every wave works on both, so the score MFMAs of tile i+1, the exp / convert work of tile i
-  // and the PV MFMAs of tile i form one basic block.
+  // row) and every wave works on both, so the score MFMAs of tile i+1 go out
+  // first, right after the barrier, and the row max, exp / convert work of
+  // tile i and its PV MFMAs follow (measured 1-1.5% faster than issuing the
+  // scores after the row max).
   auto step_clear = [&](auto par, int i, f32x16 (&cur)[2], f32x16 (&nxt)[2]) YR_INLINE {
     stage(par, i);
-    const float neg_m = softmax_front(tile_of(i), cur, false);
     scores(nextp(par), nxt);
+    const float neg_m = softmax_front(tile_of(i), cur, false);
     bf16x8 pf[4];
     softmax_back(cur, neg_m, pf);
     pv(par, pf);
