@@ -34,6 +34,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // reduced angle, in [-pi/4, pi/4], goes through the single-precision minimax
 // polynomials of the Cephes library (sinf/cosf), and the quadrant picks the
 // signs.  Max abs error ~1e-7 (about 1.5 fp32 ulp of 1.0).
+// The two halves of a wave combined lane by lane: lane l and lane l ^ 32 both
+// get max / sum of their two values.  v_permlane32_swap(x, x) hands lanes
+// 0-31 their partner's value in the second result and lanes 32-63 theirs in
+// the first (each keeps its own in the other), so one VALU swap replaces the
+// LDS-crossbar exchange.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ void rope_cos_sin(double pos, double theta, float *c, float *s) {
   constexpr double kTwoOverPi = 0.63661977236758134308;
   constexpr double kPio2Hi = 1.5707963267948966192;    // nearest double to pi/2

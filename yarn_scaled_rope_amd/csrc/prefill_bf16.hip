@@ -351,7 +351,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;   // row max on raw scores (scale > 0)
+    mx = half_max(mx) * scale_log2;   // row max on raw scores (scale > 0)
     const bool grow = mx > m_run + 8.0f;                 // lazy running max
     if (__any(grow)) {
       const float m_new = grow ? mx : m_run;
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   for (; i < count; i += BL) general_block(i);
 
   // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ---------------------
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  const float l_tot = half_sum(l_part);
   if (tq >= n) return;
   const float inv = 1.f / l_tot;
   const long long orow = ((s0 + tq) * Hq + h) * (long long)D;
