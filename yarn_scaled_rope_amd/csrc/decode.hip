@@ -724,7 +724,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     float mx = sc[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = half_max(mx);
     const float mnew = fmaxf(mrun, mx * sl);
     // lazy rescale: keep the reference max until some column's max has grown
     // by more than 2^8 (p stays <= 256, exact in fp32 sums, fine in bf16)
@@ -792,7 +792,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
 
   // ---- combine: the two lane halves of a column hold disjoint keys; then
   // the waves, through LDS (the ring is free once every wave is here)
-  lsum += __shfl_xor(lsum, 32);
+  lsum = half_sum(lsum);
   __syncthreads();
   if (l32 < gc) {
 #pragma unroll
