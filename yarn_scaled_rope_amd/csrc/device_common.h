@@ -29,11 +29,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// cos and sin of (pos * theta).  The product and its Cody-Waite reduction by
-// pi/2 are done in fp64 (exact to ~1e-11 rad for positions up to 2^20); the
-// reduced angle, in [-pi/4, pi/4], goes through the single-precision minimax
-// polynomials of the Cephes library (sinf/cosf), and the quadrant picks the
-// signs.  Max abs error ~1e-7 (about 1.5 fp32 ulp of 1.0).
 // The two halves of a wave combined lane by lane: lane l and lane l ^ 32 both
 // get max / sum of their two values.  v_permlane32_swap(x, x) hands lanes
 // 0-31 their partner's value in the second result and lanes 32-63 theirs in
@@ -50,6 +45,11 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// cos and sin of (pos * theta).  The product and its Cody-Waite reduction by
+// pi/2 are done in fp64 (exact to ~1e-11 rad for positions up to 2^20); the
+// reduced angle, in [-pi/4, pi/4], goes through the single-precision minimax
+// polynomials of the Cephes library (sinf/cosf), and the quadrant picks the
+// signs.  Max abs error ~1e-7 (about 1.5 fp32 ulp of 1.0).
 __device__ __forceinline__ void rope_cos_sin(double pos, double theta, float *c, float *s) {
   constexpr double kTwoOverPi = 0.63661977236758134308;
   constexpr double kPio2Hi = 1.5707963267948966192;    // nearest double to pi/2
