@@ -54,7 +54,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 512;
 constexpr int kBQ = kThreads / 2;  // query rows per workgroup (32 per wave)
 constexpr int kBC = 64;            // keys per tile
-constexpr int kStages = 2;         // LDS stages of K and of V (2 or 3; 3 measured no faster)
 constexpr int kXcds = 8;
 constexpr int kMaxRankedSeqs = 64;  // chunked prefill orders up to this many sequences
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -108,13 +107,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     window = 0;
     sinks = 0;
   }
-  constexpr int NS = kStages;
-  static_assert(NS == 2 || NS == 3, "two or three stages");
-  constexpr int TILE3 = NS > 2 ? TILE : 8;
-  // one array per stage: the compiler then tells a stage being read from the
-  // copies in flight into the other stages, and adds no wait for them
-  __shared__ __align__(16) uint16_t sk0[TILE], sk1[TILE], sk2[TILE3];
-  __shared__ __align__(16) uint16_t sv0[TILE], sv1[TILE], sv2[TILE3];
+  // Two LDS stages of K and of V (a third measured no faster, and spills).
+  // One array per stage: the compiler then tells a stage being read from the
+  // copies in flight into the other stage, and adds no wait for them.
+  constexpr int NS = 2;
+  __shared__ __align__(16) uint16_t sk0[TILE], sk1[TILE];
+  __shared__ __align__(16) uint16_t sv0[TILE], sv1[TILE];
 
   if (flag != nullptr && blockIdx.x == 0)
     validate_cu_seqlens(cu, B, T, max_seqlen, flag, kv_len > 0 ? ctx : nullptr, kv_len);
@@ -228,11 +226,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   // tile t lives in stage t % NS; `par` below is that stage index
   auto kst = [&](auto par) YR_INLINE -> uint16_t * {
     constexpr int P = decltype(par)::value;
-    if constexpr (P == 0) return sk0; else if constexpr (P == 1) return sk1; else return sk2;
+    if constexpr (P == 0) return sk0; else return sk1;
   };
   auto vst = [&](auto par) YR_INLINE -> uint16_t * {
     constexpr int P = decltype(par)::value;
-    if constexpr (P == 0) return sv0; else if constexpr (P == 1) return sv1; else return sv2;
+    if constexpr (P == 0) return sv0; else return sv1;
   };
   // Key tiles the workgroup visits, as a list: the sink tiles [0, js), then
   // the tiles [jw, last] from the window start of its first row to the
@@ -402,26 +400,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     }
   };
 
-  // One pipeline step i over the tile list (stage par = i % NS; tile(i) is
+  // One pipeline step i over the tile list (stage par = i % 2; tile(i) is
   // the list's i-th tile): after the barrier the K stage of tile(i) (read by
   // the scores of step i-1) and the V stage of tile(i-1) are free; copy
-  // K(tile(i+NS)) and V(tile(i+NS-1)) into them, then run the score MFMAs of
+  // K(tile(i+2)) and V(tile(i+1)) into them, then run the score MFMAs of
   // tile(i+1) alongside the softmax of tile(i), then the PV MFMAs of tile(i).
   // Before the barrier each wave waits for its own copies of K(tile(i+1)) and
-  // V(tile(i)), issued NS-1 steps earlier; the copies of the last NS-2 steps
-  // may still be in flight.
+  // V(tile(i)), issued by the previous step.
   auto nextp = [](auto par) YR_INLINE { return std::integral_constant<int, (decltype(par)::value + 1) % NS>{}; };
   auto prevp = [](auto par) YR_INLINE { return std::integral_constant<int, (decltype(par)::value + NS - 1) % NS>{}; };
   auto stage = [&](auto par, int i) YR_INLINE {
-    if constexpr (NS == 2) {
-      wait_dma<0>();
-    } else {
-      // copies issued by step i-1: K(tile(i+2)) and V(tile(i+1)) when they exist
-      const int pending = (i >= 1 && i + 2 < count ? 1 : 0) + (i >= 1 && i + 1 < count ? 1 : 0);
-      if (pending == 2) wait_dma<2 * DPW>();
-      else if (pending == 1) wait_dma<DPW>();
-      else wait_dma<0>();
-    }
+    wait_dma<0>();
     __syncthreads();
     if (i + NS < count) copy_tile(kst(par), kseq, tile_of(i + NS), false);
     if (i + NS - 1 < count) copy_tile(vst(prevp(par)), vseq, tile_of(i + NS - 1), true);
@@ -460,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   if (active(tile_of(0))) scores(std::integral_constant<int, 0>{}, sa);
   // Steps are unrolled over the stage index (i % NS) and the score buffer
   // (i % 2), so every LDS array and register array is picked at compile time.
-  constexpr int BL = NS == 2 ? 2 : 6;
+  constexpr int BL = 2;
   auto sbuf = [&](auto ic) YR_INLINE -> f32x16(&)[2] {
     if constexpr (decltype(ic)::value % 2 == 0) return sa; else return sb;
   };
@@ -492,7 +481,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   for (; i < c0; i += BL) general_block(i);
   // the unmasked run in blocks of 4 steps (two stage / buffer cycles; +0.5-1%
   // over blocks of 2), its remainder in blocks of 2
-  constexpr int BLC = NS == 2 ? 4 : BL;
+  constexpr int BLC = 4;
   for (; i + BLC < c1; i += BLC) {
     static_for<0, BLC>([&](auto ic) YR_INLINE {
       constexpr int I = decltype(ic)::value;
