@@ -268,7 +268,7 @@ size_t attn_decode_workspace_bytes(int B, int max_cache_len, int Hq, int head_di
   if (B < 1 || max_cache_len < 1 || Hq < 1 || head_dim < 1) return kHeader;
   // chunking depends on Hkv only through the split count heuristic; size for
   // the finest chunking any Hkv <= Hq can select
-  const int chunk = decode_chunk(B, max_cache_len, 1);
+  const int chunk = decode_chunk(B, max_cache_len, 1, kDecodeMinChunk);
   const size_t ns = (size_t)decode_nsplit(max_cache_len, chunk);
   const size_t rows = (size_t)B * Hq * ns;
   return kHeader + align_up(rows * head_dim * 4, 256) + align_up(rows * 4, 256);
@@ -315,7 +315,13 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
   const size_t need = attn_decode_workspace_bytes(B, max_cache_len, Hq, head_dim);
   if (workspace_bytes < need) return bad(YR_ERR_WORKSPACE, "workspace too small");
 
-  int chunk = decode_chunk(B, max_cache_len, Hkv);
+  // the matrix-core kernel launches one workgroup per group of KV heads, the
+  // fp32 one per head: chunk so that either launches enough workgroups
+  const bool fp8 = cache_dtype == YR_FP8_E4M3, win = window > 0;
+  const int units = cache_dtype == YR_F32 ? Hkv : decode_wg_groups(Hkv, head_dim, fp8, win);
+  const int min_chunk =
+      cache_dtype == YR_F32 ? kDecodeMinChunk : decode_min_chunk_mfma(fp8, win);
+  int chunk = decode_chunk(B, max_cache_len, units, min_chunk);
   int nsplit = decode_nsplit(max_cache_len, chunk);
   // With a window the matrix-core sweep can split the visible rows alone
   // (normally window - 1 + sinks of them) instead of the whole cache, so that
@@ -324,7 +330,7 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
   int vis_split = 0;
   if (window > 0 && cache_dtype != YR_F32) {
     const int span = (int)std::min<long long>(max_cache_len, (long long)window + sinks);
-    const int cw = decode_chunk(B, span, Hkv);
+    const int cw = decode_chunk(B, span, units, min_chunk);
     const int nw = decode_nsplit(span, cw);
     if (nw < nsplit) {
       chunk = cw;

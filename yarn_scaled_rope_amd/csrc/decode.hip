@@ -29,8 +29,8 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 8;  // keys per lane group per iteration (loads in flight)
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int kMfmaWaves = 4;   // waves per workgroup, bf16 kernel
-constexpr int kMfmaStages = 1;  // LDS stages per wave, bf16 kernel (two workgroups fit a CU)
+constexpr int kMfmaStages = 2;  // LDS stages per wave, matrix-core kernel
+constexpr int kMfmaLdsBudget = 128 * 1024;  // ring bytes per workgroup
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -314,9 +314,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 }
 
 // ---- bf16 inputs: matrix-core split kernel ----------------------------------
-// Per 32-key block a wave computes S^T = K Q^T (keys x query heads of the
-// group, v_mfma_f32_32x32x16_bf16 with the group's heads as the 32 columns)
-// and O^T += V^T P^T.  K and V blocks go straight from HBM into a ring of LDS
+// A workgroup owns (sequence, key chunk, group of W KV heads); wave w sweeps
+// the whole chunk for KV head hg*W + w, so the W waves stream the same cache
+// rows side by side and together read each row's W heads (W*D elements,
+// contiguous) at about the same time: measured 7.1 TB/s for that access
+// pattern against 6.3 TB/s when each workgroup owns one head's 256-byte
+// slices of the rows.  Per 32-key block a wave computes S^T = K Q^T (keys x
+// query heads of its KV head, v_mfma_f32_32x32x16_bf16 with those heads as
+// the 32 columns) and O^T += V^T P^T, and at the end writes its heads'
+// partial (O, log2-sum-exp) itself.  K and V blocks go straight from HBM into a ring of LDS
 // stages private to the wave (buffer_load ... lds: no staging registers, no
 // workgroup barriers in the sweep); the wave waits on exact vmcnt counts, so
 // the next blocks stream in while the current one is computed.
@@ -367,19 +373,31 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
                fp8x2_to_bf16x2<true>(w1)};
 }
 
-template <int D, int W, int NB, int EB>
+template <int D, int W>
+struct MfmaComb {  // the waves' partial states of one KV head, combined at the end
+  float o[W][D][33];
+  float m[W][32];
+  float l[W][32];
+};
+template <int D, int W, int NB, int EB, bool SH>
 struct MfmaSmem {
   union {
     uint8_t ring[W][NB][2][kBlk * D * EB];  // [wave][stage][K|V][row bytes, swizzled chunks]
-    struct {
-      float o[W][D][33];
-      float m[W][32];
-      float l[W][32];
-    } comb;
+    std::conditional_t<SH, MfmaComb<D, W>, char> comb;
   } u;
-  uint16_t qt[32][D + 8];  // rotated query heads of the group (bf16), one per row
-  float cs[D / 2], sn[D / 2];
+  uint16_t qt[SH ? 32 : 1][D + 8];  // SH: the rotated query heads (bf16), one per row
+  float cs[D / 2], sn[D / 2];        // cos / sin of the query position
 };
+
+// Ring bytes of a workgroup of W waves (one KV head each).
+constexpr int mfma_ring_bytes(int W, int D, int EB) { return W * kMfmaStages * 2 * kBlk * D * EB; }
+// KV heads per workgroup of the head-per-wave form: the largest of 8, 4, 2,
+// 1 that divides Hkv and keeps the ring within the budget (head_dim 128: 4).
+constexpr int heads_per_wg(int Hkv, int D, int EB) {
+  return (Hkv % 8 == 0 && mfma_ring_bytes(8, D, EB) <= kMfmaLdsBudget) ? 8
+         : (Hkv % 4 == 0 && mfma_ring_bytes(4, D, EB) <= kMfmaLdsBudget) ? 4
+         : Hkv % 2 == 0 ? 2 : 1;
+}
 
 // s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
 template <int N>
@@ -405,6 +423,23 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F);
 // LDS byte address of a shared-memory pointer
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const YR_LDS void *)p;
+}
+
+// LDS accesses away from the ring, in asm: written as builtins, they would
+// make the compiler wait for every LDS DMA of the wave in flight.  The read
+// waits for its own result inside the block.
+__device__ __forceinline__ void lds_store_f32(uint32_t addr, float v) {
+  asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ f32x4 lds_load_f32x4(uint32_t addr) {
+  f32x4 r;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+// workgroup barrier after this wave's LDS accesses have completed (not its
+// global ones, unlike __syncthreads)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // The V^T operands of one k-step: for each 32-row block db, two transposing
@@ -471,8 +506,11 @@ __device__ __forceinline__ void tr8_reads(u32x2 (&r)[DBLK], const uint32_t (&a)[
   }
 }
 
-// WIN: sliding window / sinks (compiled out without it)
-template <int D, int W, int NB, bool FP8, bool WIN>
+// WIN: sliding window / sinks (compiled out without it).  SH: the W waves
+// share one KV head and take alternate blocks of the chunk, then combine
+// through LDS (the FP8 form: its blocks are half the bytes and twice the
+// conversion work, and measured faster this way, 6.2 against 5.9 TB/s).
+template <int D, int W, int NB, bool FP8, bool WIN, bool SH>
 __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     const uint16_t *__restrict__ q, const void *__restrict__ kc,
     const void *__restrict__ vc, const int *__restrict__ seqlens,
@@ -495,14 +533,27 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
   constexpr int NT = W * 64;
   static_assert((2 * NB - 1) * H < 64, "vmcnt range");
 
-  __shared__ __align__(16) MfmaSmem<D, W, NB, EB> sm;
+  __shared__ __align__(16) MfmaSmem<D, W, NB, EB, SH> sm;
+  constexpr int HW = SH ? 1 : W;  // KV heads of the workgroup
 
   if (flag != nullptr && blockIdx.x == 0) validate_decode_lens(seqlens, qpos, B, Lmax, flag);
 
-  const int split = blockIdx.x % nsplit;
-  const int rest = blockIdx.x / nsplit;
-  const int hk = rest % Hkv;
-  const int b = rest / Hkv;
+  // Head-per-wave: head group fastest, so that the workgroups that read the
+  // other heads of the same cache rows are launched next to this one.
+  // Shared: chunk fastest (measured faster for that form).
+  int hg, split, b;
+  if constexpr (SH) {
+    split = blockIdx.x % nsplit;
+    const int rest = blockIdx.x / nsplit;
+    hg = rest % Hkv;
+    b = rest / Hkv;
+  } else {
+    const int ngroups = Hkv / W;
+    hg = blockIdx.x % ngroups;
+    const int rest = blockIdx.x / ngroups;
+    split = rest % nsplit;
+    b = rest / nsplit;
+  }
   const int g = Hq / Hkv;
   int L = seqlens[b];
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
@@ -514,6 +565,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hk = SH ? hg : hg * W + wave;  // this wave's KV head
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int gc = min(g, 32);
@@ -546,10 +598,11 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
   const int nba = (na + kBlk - 1) / kBlk;
   const int nblk = nba + (nb + kBlk - 1) / kBlk;
   if (nblk == 0) {
-    // nothing visible here: an empty partial (weight 0 in the merge)
-    for (int idx = tid; idx < gc * D; idx += NT) {
-      const int gi = idx / D, d = idx % D;
-      const long long row = ((long long)b * Hq + hk * g + gi) * nsplit + split;
+    // nothing visible here: empty partials (weight 0 in the merge) for every
+    // query head of the workgroup's KV heads
+    for (int idx = tid; idx < HW * gc * D; idx += NT) {
+      const int w = idx / (gc * D), gi = (idx / D) % gc, d = idx % D;
+      const long long row = ((long long)b * Hq + (hg * HW + w) * g + gi) * nsplit + split;
       part_o[row * D + d] = 0.f;
       if (d == 0) part_lse[row] = -INFINITY;
     }
@@ -563,7 +616,9 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
   const long long rstride = (long long)Hkv * ROWB;  // bytes between keys
   const uint8_t *kbase = (const uint8_t *)kc + ((long long)b * Lmax * Hkv + hk) * ROWB;
   const uint8_t *vbase = (const uint8_t *)vc + ((long long)b * Lmax * Hkv + hk) * ROWB;
-  const int nmine = nblk > wave ? (nblk - wave + W - 1) / W : 0;  // blocks of this wave
+  // blocks of this wave: every block of the chunk, or (SH) every W-th
+  const int nmine = SH ? (nblk > wave ? (nblk - wave + W - 1) / W : 0) : nblk;
+  auto gblk = [&](int t) { return SH ? wave + t * W : t; };
   // FP8: the per-head scales fold into the logit scale and the output
   float sl = scale_log2, vsc = 1.f;
   if constexpr (FP8) {
@@ -585,11 +640,15 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     voff_v[p] = (uint32_t)(r * rstride + 16 * (dslot ^ vx));
   }
 
-  // t-th block of this wave -> stage; rows past the block's share read 0
+  // t-th block of this wave -> stage; rows past the block's share read 0,
+  // and so does the whole stage when the wave has no t-th block (the first
+  // stages are always issued, so that every path has the same loads in flight
+  // and the compiler's waits for the query loads stay partial)
   auto issue = [&](int t, int stage, int which) {
-    const int key0 = blk_start(wave + t * W);
-    const int rows = blk_rows(wave + t * W);
-    const uint32_t bytes = (uint32_t)((rows - 1) * rstride + ROWB);
+    const bool ok = t < nmine;
+    const int key0 = ok ? blk_start(gblk(t)) : 0;
+    const int rows = ok ? blk_rows(gblk(t)) : 0;
+    const uint32_t bytes = ok ? (uint32_t)((rows - 1) * rstride + ROWB) : 0u;
     const uint8_t *src = (which == 0 ? kbase : vbase) + key0 * rstride;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, bytes);
     uint8_t *dst = sm.u.ring[wave][stage][which];
@@ -601,21 +660,42 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     }
   };
 
+  // ---- query heads of the wave's KV head (one per MFMA column l32; columns
+  // past the group are zero), rotated at the new token's position and rounded
+  // to bf16.  k-step kk, lane half hh covers head dims qd(kk) .. +7:
+  // 16 kk + 8 hh, or with an FP8 cache, where one 16-byte read of a K row
+  // serves two k-steps, 16 (2 (kk / 2) + hh) + 8 (kk % 2).
+  auto qd = [&](int kk) { return FP8 ? 16 * (2 * (kk / 2) + hh) + 8 * (kk % 2) : 16 * kk + 8 * hh; };
+  static_assert(D / 2 <= NT, "one frequency per thread");
+  // Head-per-wave: each lane loads its query row ahead of the first blocks,
+  // so that the wait for it does not take in theirs, and the LDS round trip
+  // of cos / sin goes through asm for the same reason.
+  u32x4 qraw[KSTEPS];
+  double th = 0.0;
+  if constexpr (!SH) {
+    const uint16_t *qrow = q + ((long long)b * Hq + hk * g + min(l32, gc - 1)) * D;
 #pragma unroll
-  for (int s = 0; s < NB; ++s)
-    if (s < nmine) {
-      issue(s, s, 0);
-      issue(s, s, 1);
-    }
+    for (int kk = 0; kk < KSTEPS; ++kk) qraw[kk] = *reinterpret_cast<const u32x4 *>(qrow + qd(kk));
+    if (theta != nullptr) th = theta[tid & (D / 2 - 1)];
+  }
 
-  // ---- query heads of the group: rotate at the new token's position, round
-  // to bf16, one head per row of qt (rows past the group stay zero)
-  {
-    for (int i = tid; i < D / 2; i += NT) {
+#pragma unroll
+  for (int s = 0; s < NB; ++s) {
+    issue(s, s, 0);
+    issue(s, s, 1);
+  }
+
+  bf16x8 qf[KSTEPS];
+  if constexpr (SH) {
+    // Shared: the waves stage the one group's heads through LDS; the
+    // barriers here also wait for the first blocks, so the waves start the
+    // sweep together (measured faster for this form than letting each start
+    // as soon as its query is in, 6.0 against 5.7 TB/s with FP8)
+    if (tid < D / 2) {
       float c = 1.f, s = 0.f;
-      if (theta != nullptr) rope_cos_sin((double)qm, theta[i], &c, &s);
-      sm.cs[i] = c;
-      sm.sn[i] = s;
+      if (theta != nullptr) rope_cos_sin((double)qm, theta[tid], &c, &s);
+      sm.cs[tid] = c;
+      sm.sn[tid] = s;
     }
     __syncthreads();
     for (int idx = tid; idx < 32 * (D / 2); idx += NT) {
@@ -630,15 +710,31 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
       *reinterpret_cast<uint32_t *>(&sm.qt[col][2 * pr]) = pack_bf16x2(x0, x1);
     }
     __syncthreads();
-  }
-  // k-step kk, lane half hh covers head dims 16 kk + 8 hh .. +7; with an FP8
-  // cache one 16-byte read of a K row serves two k-steps, so there lane half
-  // hh covers 16 (2 (kk / 2) + hh) + 8 (kk % 2) .. +7 (Q follows the same order)
-  bf16x8 qf[KSTEPS];
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) {
-    const int d0 = FP8 ? 16 * (2 * (kk / 2) + hh) + 8 * (kk % 2) : 16 * kk + 8 * hh;
-    qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&sm.qt[l32][d0]));
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&sm.qt[l32][qd(kk)]));
+  } else {
+    const uint32_t cs_addr = lds_addr(sm.cs), sn_addr = lds_addr(sm.sn);
+    if (tid < D / 2) {
+      float c = 1.f, s = 0.f;
+      if (theta != nullptr) rope_cos_sin((double)qm, th, &c, &s);
+      lds_store_f32(cs_addr + 4 * tid, c);
+      lds_store_f32(sn_addr + 4 * tid, s);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const int d0 = qd(kk);  // pairs d0 / 2 .. +3: one aligned 16-byte read each
+      const f32x4 c4 = lds_load_f32x4(cs_addr + 2 * d0), s4 = lds_load_f32x4(sn_addr + 2 * d0);
+      u32x4 w = qraw[kk];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x0 = bf16_to_f32(w[e] & 0xffffu), x1 = bf16_to_f32(w[e] >> 16);
+        rotate_pair(x0, x1, c4[e], s4[e]);
+        w[e] = l32 < gc ? pack_bf16x2(x0, x1) : 0u;
+      }
+      qf[kk] = __builtin_bit_cast(bf16x8, w);
+    }
   }
 
   f32x16 o[DBLK];
@@ -683,7 +779,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
 
   auto block = [&](int t, auto stage_c) {
     constexpr int S = decltype(stage_c)::value;
-    const int rows = blk_rows(wave + t * W);
+    const int rows = blk_rows(gblk(t));
     const int ahead = min(NB - 1, nmine - 1 - t);  // later blocks already issued
     const bool refill = t + NB < nmine;
 
@@ -790,38 +886,56 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     if (NB > 3 && t + 3 < nmine) block(t + 3, std::integral_constant<int, (NB > 3 ? 3 : 0)>{});
   }
 
-  // ---- combine: the two lane halves of a column hold disjoint keys; then
-  // the waves, through LDS (the ring is free once every wave is here)
+  // ---- the two lane halves of a column hold disjoint keys of the same
+  // query head
   lsum = half_sum(lsum);
-  __syncthreads();
-  if (l32 < gc) {
+  if constexpr (!SH) {
+    // the wave saw the whole chunk for its KV head: it writes the partials
+    if (l32 < gc) {
+      const long long row = ((long long)b * Hq + hk * g + l32) * nsplit + split;
+      const float inv = vsc / lsum;
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db)
+      for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        sm.u.comb.o[wave][32 * db + 8 * (e >> 2) + 4 * hh + (e & 3)][l32] = o[db][e];
-    if (hh == 0) {
-      sm.u.comb.m[wave][l32] = mrun;
-      sm.u.comb.l[wave][l32] = lsum;
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4 *>(part_o + row * D + 32 * db + 8 * j + 4 * hh) =
+              make_float4(o[db][4 * j] * inv, o[db][4 * j + 1] * inv, o[db][4 * j + 2] * inv,
+                          o[db][4 * j + 3] * inv);
+      if (hh == 0) part_lse[row] = mrun + __log2f(lsum);
     }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < gc * D; idx += NT) {
-    const int gi = idx / D, d = idx % D;
-    float M = -INFINITY;
+  } else {
+    // the waves saw alternate blocks: combine them through LDS (the ring is
+    // free once every wave is here); a wave without blocks has m = -inf
+    __syncthreads();
+    if (l32 < gc) {
 #pragma unroll
-    for (int w = 0; w < W; ++w) M = fmaxf(M, sm.u.comb.m[w][gi]);
-    float num = 0.f, den = 0.f;
+      for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float mw = sm.u.comb.m[w][gi];
-      const float s = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      num += s * sm.u.comb.o[w][d][gi];
-      den += s * sm.u.comb.l[w][gi];
+        for (int e = 0; e < 16; ++e)
+          sm.u.comb.o[wave][32 * db + 8 * (e >> 2) + 4 * hh + (e & 3)][l32] = o[db][e];
+      if (hh == 0) {
+        sm.u.comb.m[wave][l32] = mrun;
+        sm.u.comb.l[wave][l32] = lsum;
+      }
     }
-    const long long row = ((long long)b * Hq + hk * g + gi) * nsplit + split;
-    part_o[row * D + d] = num / den * vsc;
-    if (d == 0) part_lse[row] = M + __log2f(den);
+    __syncthreads();
+    for (int idx = tid; idx < gc * D; idx += NT) {
+      const int gi = idx / D, d = idx % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < W; ++w) M = fmaxf(M, sm.u.comb.m[w][gi]);
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float mw = sm.u.comb.m[w][gi];
+        const float sc_ = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+        num += sc_ * sm.u.comb.o[w][d][gi];
+        den += sc_ * sm.u.comb.l[w][gi];
+      }
+      const long long row = ((long long)b * Hq + hk * g + gi) * nsplit + split;
+      part_o[row * D + d] = num / den * vsc;
+      if (d == 0) part_lse[row] = M + __log2f(den);
+    }
   }
 }
 
@@ -926,17 +1040,35 @@ hipError_t launch_split_g(const DecodeArgs &a, hipStream_t s) {
   return launch_split<T, D, 16>(a, s);
 }
 
-template <int D, bool FP8, bool WIN>
-hipError_t launch_mfma(const DecodeArgs &a, hipStream_t s) {
-  constexpr int W = kMfmaWaves, NB = kMfmaStages;
-  const long long blocks = (long long)a.B * a.Hkv * a.nsplit;
+template <int D, bool FP8, bool WIN, int W, bool SH = false>
+hipError_t launch_mfma_w(const DecodeArgs &a, hipStream_t s) {
+  constexpr int NB = SH ? 1 : kMfmaStages;
+  const long long blocks = (long long)a.B * (SH ? a.Hkv : a.Hkv / W) * a.nsplit;
   const float scale_log2 = (float)((double)a.softmax_scale * 1.4426950408889634074);
-  hipLaunchKernelGGL((decode_mfma_kernel<D, W, NB, FP8, WIN>), dim3((unsigned)blocks), dim3(W * 64), 0,
+  hipLaunchKernelGGL((decode_mfma_kernel<D, W, NB, FP8, WIN, SH>), dim3((unsigned)blocks), dim3(W * 64), 0,
                      s, (const uint16_t *)a.q, a.k_cache, a.v_cache, a.seqlens, a.q_pos, a.B,
                      a.max_cache_len, a.Hq, a.Hkv, a.theta, scale_log2, a.chunk, a.nsplit,
                      a.part_o, a.part_lse, a.dev_flag, a.window, a.sinks, a.k_scale, a.v_scale,
                      a.vis_split);
   return hipGetLastError();
+}
+
+template <int D, bool FP8, bool WIN>
+hipError_t launch_mfma(const DecodeArgs &a, hipStream_t s) {
+  constexpr int EB = FP8 ? 1 : 2;
+  if constexpr (decode_shared_form(FP8, WIN)) {
+    return launch_mfma_w<D, FP8, WIN, 4, true>(a, s);
+  } else {
+    switch (heads_per_wg(a.Hkv, D, EB)) {
+      case 8:
+        if constexpr (mfma_ring_bytes(8, D, EB) <= kMfmaLdsBudget)
+          return launch_mfma_w<D, FP8, WIN, 8>(a, s);
+        return hipErrorInvalidValue;
+      case 4: return launch_mfma_w<D, FP8, WIN, 4>(a, s);
+      case 2: return launch_mfma_w<D, FP8, WIN, 2>(a, s);
+      default: return launch_mfma_w<D, FP8, WIN, 1>(a, s);
+    }
+  }
 }
 
 template <int D>
@@ -955,13 +1087,17 @@ hipError_t launch_merge(const DecodeArgs &a, hipStream_t s) {
 
 }  // namespace
 
-int decode_chunk(int B, int max_cache_len, int Hkv) {
+int decode_wg_groups(int Hkv, int head_dim, bool fp8, bool win) {
+  return decode_shared_form(fp8, win) ? Hkv : Hkv / heads_per_wg(Hkv, head_dim, fp8 ? 1 : 2);
+}
+
+int decode_chunk(int B, int max_cache_len, int units, int min_chunk) {
   // Enough workgroups to fill 256 CUs several times over; chunks are powers
-  // of two, at most 2048 keys (1 MiB of K and V at 128 bf16 elements per key
-  // and 8 KV heads) so that a workgroup's start-up and combine stay small
-  // next to its sweep.
+  // of two, at most 2048 keys so that a workgroup's start-up and combine stay
+  // small next to its sweep, and at least min_chunk.
   int chunk = 2048;
-  while (chunk > 64 && (long long)B * Hkv * decode_nsplit(max_cache_len, chunk) < 2048) chunk >>= 1;
+  while (chunk > min_chunk && (long long)B * units * decode_nsplit(max_cache_len, chunk) < 2048)
+    chunk >>= 1;
   return chunk;
 }
 

@@ -92,9 +92,22 @@ hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 
 // Decode split geometry: keys per chunk and number of chunks for a cache
-// length bound.  Pure function of its arguments so that workspace sizing and
-// the launch agree.
-int decode_chunk(int B, int max_cache_len, int Hkv);
+// length bound, with `units` workgroups per (sequence, chunk).  Pure function
+// of its arguments so that workspace sizing and the launch agree.
+constexpr int kDecodeMinChunk = 64;       // fp32 kernel (a workgroup per KV head)
+constexpr int kDecodeMinChunkMfma = 256;  // head-per-wave decode: >= 8 blocks per wave
+int decode_chunk(int B, int max_cache_len, int units, int min_chunk);
+// The matrix-core decode has two forms.  Head-per-wave: each wave sweeps a
+// whole chunk for one KV head and a workgroup takes 8, 4, 2 or 1 KV heads
+// (the largest dividing Hkv whose LDS ring fits the budget).  Shared: four
+// waves take alternate blocks of one KV head's chunk and combine in LDS.
+constexpr bool decode_shared_form(bool fp8, bool win) { return fp8 || win; }
+// Workgroups per (sequence, chunk) of the matrix-core decode, and the least
+// chunk length worth a workgroup.
+int decode_wg_groups(int Hkv, int head_dim, bool fp8, bool win);
+inline int decode_min_chunk_mfma(bool fp8, bool win) {
+  return decode_shared_form(fp8, win) ? kDecodeMinChunk : kDecodeMinChunkMfma;
+}
 inline int decode_nsplit(int max_cache_len, int chunk) {
   return (max_cache_len + chunk - 1) / chunk;
 }
