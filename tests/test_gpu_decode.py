@@ -75,6 +75,36 @@ def test_decode_workload_full():
     assert e_out <= BF16_TOL and e_lse <= BF16_TOL
 
 
+@pytest.mark.parametrize("hq,hkv,D,use_qpos", [
+    (32, 8, 128, False),
+    (48, 12, 128, True),
+    (16, 4, 64, False),
+])
+def test_decode_balanced_split(hq, hkv, D, use_qpos):
+    """Caches of >= 512K keys in all take the balanced split over one
+    workgroup per CU (head-per-wave form, four KV heads per workgroup):
+    lengths of 1, 31, 32, 33 keys beside full and odd ones, so that pieces
+    start and end inside sequences and some sequences fit inside one piece."""
+    B, lmax = 10, 60000
+    cfg = _cfg("bf16", hq, hkv, D)
+    inp = wl.make_decode(cfg, seed=77 + hkv, batch=B, max_cache_len=lmax, min_cache_len=lmax)
+    lens = np.array([1, 31, 32, 33, lmax, lmax - 1, 1000, 20000, 7, 45001], dtype=np.int32)
+    for name in ("k_cache", "v_cache"):
+        for b in range(B):
+            inp[name][b, lens[b]:] = wl.BF16_NAN_BITS
+    inp["seqlens"] = lens
+    q_pos = None
+    if use_qpos:
+        q_pos = [int(x) for x in np.maximum(lens // 2, 0)]
+    say(f"decode balanced split hq={hq} hkv={hkv} D={D} seqlens={lens.tolist()} q_pos={q_pos}")
+    out, lse = _run(inp, cfg, out_dtype=ops.YR_F32, q_pos=q_pos)
+    ro, rl = _oracle(inp, cfg, q_pos=q_pos)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    e_out, e_lse = max_abs(out, ro), max_abs(lse, rl)
+    print(f"max-abs out {e_out:.3e} lse {e_lse:.3e}")
+    assert e_out <= BF16_TOL and e_lse <= BF16_TOL
+
+
 def test_decode_matches_prefill_last_row():
     """Decode at q_pos = L-1 over the keys rotated by rope_apply equals row
     L-1 of prefill over the same unrotated inputs."""

@@ -270,7 +270,11 @@ size_t attn_decode_workspace_bytes(int B, int max_cache_len, int Hq, int head_di
   // the finest chunking any Hkv <= Hq can select
   const int chunk = decode_chunk(B, max_cache_len, 1, kDecodeMinChunk);
   const size_t ns = (size_t)decode_nsplit(max_cache_len, chunk);
-  const size_t rows = (size_t)B * Hq * ns;
+  size_t rows = (size_t)B * Hq * ns;
+  // the balanced split writes at most (workgroups + segments) partials of
+  // Hq / (segments per sequence) query heads each: <= (max workgroups + B) * Hq
+  if (decode_stream_eligible(B, max_cache_len))
+    rows = std::max(rows, ((size_t)kDecodeStreamMaxWg + B) * Hq);
   return kHeader + align_up(rows * head_dim * 4, 256) + align_up(rows * 4, 256);
 }
 
@@ -339,7 +343,17 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
     }
   }
   if ((long long)B * Hkv * nsplit > 0x7fffffffLL) return bad(YR_ERR_INVALID, "grid too large");
-  const size_t rows = (size_t)B * Hq * nsplit;
+  size_t rows = (size_t)B * Hq * nsplit;
+  // head-per-wave bf16 sweep of a large cache, four KV heads per workgroup:
+  // split the key blocks evenly over one workgroup per CU instead
+  int stream_wg = 0, stream_hpw = 0;
+  if (cache_dtype == YR_BF16 && !win && !decode_shared_form(fp8, win) &&
+      Hkv / units == 4 && decode_stream_eligible(B, max_cache_len)) {
+    stream_wg = decode_stream_wgs();
+    if (stream_wg <= 0) return bad(YR_ERR_HIP, "cannot query the device's compute units");
+    stream_hpw = 4;
+    rows = ((size_t)stream_wg + (size_t)B * units) * (size_t)(Hq / units);
+  }
   char *ws = static_cast<char *>(workspace);
   DecodeArgs d{};
   d.q = q;
@@ -368,6 +382,8 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
   d.k_scale = k_scale;
   d.v_scale = v_scale;
   d.vis_split = vis_split;
+  d.stream_wg = stream_wg;
+  d.stream_hpw = stream_hpw;
   const hipError_t e = launch_decode(d, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, fn);
   return YR_OK;

@@ -510,7 +510,13 @@ __device__ __forceinline__ void tr8_reads(u32x2 (&r)[DBLK], const uint32_t (&a)[
 // share one KV head and take alternate blocks of the chunk, then combine
 // through LDS (the FP8 form: its blocks are half the bytes and twice the
 // conversion work, and measured faster this way, 6.2 against 5.9 TB/s).
-template <int D, int W, int NB, bool FP8, bool WIN, bool SH>
+// STREAM (head-per-wave form, no window): instead of one chunk per
+// workgroup, the flattened space of (sequence, head group, 32-key block) is
+// cut into gridDim.x equal ranges, one per workgroup (one per CU); a
+// workgroup sweeps the pieces of the segments its range meets and writes one
+// partial per piece, at index (workgroup + segment).  Every CU then streams
+// the same number of blocks, and no CU waits for a last round of chunks.
+template <int D, int W, int NB, bool FP8, bool WIN, bool SH, bool STREAM>
 __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     const uint16_t *__restrict__ q, const void *__restrict__ kc,
     const void *__restrict__ vc, const int *__restrict__ seqlens,
@@ -537,27 +543,60 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
   constexpr int HW = SH ? 1 : W;  // KV heads of the workgroup
 
   if (flag != nullptr && blockIdx.x == 0) validate_decode_lens(seqlens, qpos, B, Lmax, flag);
+  static_assert(!STREAM || (!SH && !WIN), "the balanced split is for the head-per-wave form");
 
-  // Head-per-wave: head group fastest, so that the workgroups that read the
-  // other heads of the same cache rows are launched next to this one.
-  // Shared: chunk fastest (measured faster for that form).
-  int hg, split, b;
-  if constexpr (SH) {
+  // STREAM: this workgroup's range [r, r1) of the flattened block space
+  auto nblocks_of = [&](int bb) {
+    const int Lb = seqlens[bb];
+    return ((Lb < 0 ? 0 : (Lb > Lmax ? Lmax : Lb)) + kBlk - 1) / kBlk;
+  };
+  const int ngr = Hkv / HW;
+  int r = 0, r1 = 0;
+  if constexpr (STREAM) {
+    long long tb = 0;
+    for (int bb = 0; bb < B; ++bb) tb += (long long)ngr * nblocks_of(bb);
+    const long long per = tb > 0 ? (tb + gridDim.x - 1) / gridDim.x : 1;
+    const long long rs = (long long)blockIdx.x * per;
+    if (rs >= tb) return;
+    r = (int)rs;
+    r1 = (int)min(tb, rs + per);
+  }
+  for (;;) {  // STREAM: one pass per piece; otherwise a single pass
+  int hg, split, b, c0, cnt = 0;
+  if constexpr (STREAM) {
+    // the segment (sequence b, head group hg) holding block r, and the piece
+    // of it in this range; split = index of this piece's partial
+    int base = 0, bb = 0, nbk = 0;
+    for (;; ++bb) {
+      nbk = nblocks_of(bb);
+      if (r < base + ngr * nbk) break;
+      base += ngr * nbk;
+    }
+    b = bb;
+    hg = (r - base) / nbk;
+    const int blk0 = (r - base) % nbk;
+    cnt = min(nbk - blk0, r1 - r);
+    c0 = blk0 * kBlk;
+    split = (int)blockIdx.x + b * ngr + hg;
+  } else if constexpr (SH) {
+    // Shared: chunk fastest (measured faster for that form)
     split = blockIdx.x % nsplit;
     const int rest = blockIdx.x / nsplit;
     hg = rest % Hkv;
     b = rest / Hkv;
+    c0 = split * chunk;
   } else {
-    const int ngroups = Hkv / W;
-    hg = blockIdx.x % ngroups;
-    const int rest = blockIdx.x / ngroups;
+    // Head-per-wave: head group fastest, so that the workgroups that read the
+    // other heads of the same cache rows are launched next to this one
+    hg = blockIdx.x % ngr;
+    const int rest = blockIdx.x / ngr;
     split = rest % nsplit;
     b = rest / nsplit;
+    c0 = split * chunk;
   }
   const int g = Hq / Hkv;
   int L = seqlens[b];
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-  int c0 = split * chunk;
   if (vis_split == 0 && c0 >= L) return;
   int qm = qpos != nullptr ? qpos[b] : L;  // the query's position
   qm = qm < 0 ? 0 : qm;
@@ -590,7 +629,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     b0 = lo + max(c0, se) - se;
     nb = max(0, v1 - max(c0, se));
   } else {
-    const int c1 = min(L, c0 + chunk);
+    const int c1 = STREAM ? min(L, c0 + cnt * kBlk) : min(L, c0 + chunk);
     na = max(0, min(c1, se) - c0);
     b0 = max(c0, lo);
     nb = max(0, c1 - b0);
@@ -891,8 +930,10 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
   lsum = half_sum(lsum);
   if constexpr (!SH) {
     // the wave saw the whole chunk for its KV head: it writes the partials
+    // (STREAM: partial `split` holds the W*g query heads of the group)
     if (l32 < gc) {
-      const long long row = ((long long)b * Hq + hk * g + l32) * nsplit + split;
+      const long long row = STREAM ? (long long)split * (W * g) + wave * g + l32
+                                   : ((long long)b * Hq + hk * g + l32) * nsplit + split;
       const float inv = vsc / lsum;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db)
@@ -937,13 +978,24 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
       if (d == 0) part_lse[row] = M + __log2f(den);
     }
   }
+  if constexpr (!STREAM) {
+    break;
+  } else {
+    r += cnt;
+    if (r >= r1) break;
+    lds_barrier();  // every wave is past its reads of cos / sin
+  }
+  }  // piece loop
 }
 
+// nwg > 0: the partials of a balanced split (decode_mfma_kernel<..., STREAM>)
+// over nwg workgroups of hpw KV heads each; the pieces of this query head's
+// segment are found from seqlens the same way the split found them.
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float *__restrict__ part_o, const float *__restrict__ part_lse,
     const int *__restrict__ seqlens, int Hq, int Lmax, int chunk, int nsplit, int vis_split,
-    void *__restrict__ out, float *__restrict__ lse) {
+    void *__restrict__ out, float *__restrict__ lse, int B, int Hkv, int nwg, int hpw) {
   constexpr int PER = D / 64;  // output elements per lane
   constexpr int MW = 4;        // waves; wave w takes partials w, w+4, ...
   constexpr int U = 4;         // partials per wave in flight
@@ -956,13 +1008,38 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   int L = seqlens[b];
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
   // partials written: every chunk of the visible rows, or the chunks of
-  // [0, L) (those starting past L exit without one)
-  const int nv = vis_split != 0 ? nsplit : (L + chunk - 1) / chunk;
-  const long long row0 = ((long long)b * Hq + h) * nsplit;
+  // [0, L) (those starting past L exit without one); partial p is row
+  // row0 + p * stride
+  int nv;
+  long long row0, stride = 1;
+  if (nwg > 0) {
+    const int g = Hq / Hkv, ngr = Hkv / hpw;
+    const int hk = h / g, hg = hk / hpw;
+    auto nblocks_of = [&](int bb) {
+      const int Lb = seqlens[bb];
+      return ((Lb < 0 ? 0 : (Lb > Lmax ? Lmax : Lb)) + kBlk - 1) / kBlk;
+    };
+    long long tb = 0, base = 0;
+    for (int bb = 0; bb < B; ++bb) {
+      const long long n = (long long)ngr * nblocks_of(bb);
+      if (bb < b) base += n;
+      tb += n;
+    }
+    const long long per = tb > 0 ? (tb + nwg - 1) / nwg : 1;
+    const int nbk = nblocks_of(b);
+    const long long s0 = base + (long long)hg * nbk;  // first block of the segment
+    const long long w0 = s0 / per;
+    nv = nbk > 0 ? (int)((s0 + nbk - 1) / per - w0 + 1) : 0;
+    stride = (long long)hpw * g;
+    row0 = (w0 + (long long)b * ngr + hg) * stride + (hk % hpw) * g + h % g;
+  } else {
+    nv = vis_split != 0 ? nsplit : (L + chunk - 1) / chunk;
+    row0 = ((long long)b * Hq + h) * nsplit;
+  }
 
   // common reference: the largest partial log2-sum-exp (every wave computes it)
   float M = -INFINITY;
-  for (int p = lane; p < nv; p += 64) M = fmaxf(M, part_lse[row0 + p]);
+  for (int p = lane; p < nv; p += 64) M = fmaxf(M, part_lse[row0 + p * stride]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   // no visible key in any chunk (a query placed past its window): empty result
@@ -977,9 +1054,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     float w[U], x[U][PER];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      w[u] = part_lse[row0 + p + u * MW];
+      const long long rw = row0 + (p + u * MW) * stride;
+      w[u] = part_lse[rw];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) x[u][i] = part_o[(row0 + p + u * MW) * D + lane + 64 * i];
+      for (int i = 0; i < PER; ++i) x[u][i] = part_o[rw * D + lane + 64 * i];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -990,10 +1068,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     }
   }
   for (; p < nv; p += MW) {
-    const float e = __builtin_amdgcn_exp2f(part_lse[row0 + p] - M);
+    const long long rw = row0 + p * stride;
+    const float e = __builtin_amdgcn_exp2f(part_lse[rw] - M);
     den += e;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) num[i] = fmaf(e, part_o[(row0 + p) * D + lane + 64 * i], num[i]);
+    for (int i = 0; i < PER; ++i) num[i] = fmaf(e, part_o[rw * D + lane + 64 * i], num[i]);
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i) sm_num[wave][lane + 64 * i] = num[i];
@@ -1040,12 +1119,13 @@ hipError_t launch_split_g(const DecodeArgs &a, hipStream_t s) {
   return launch_split<T, D, 16>(a, s);
 }
 
-template <int D, bool FP8, bool WIN, int W, bool SH = false>
+template <int D, bool FP8, bool WIN, int W, bool SH = false, bool STREAM = false>
 hipError_t launch_mfma_w(const DecodeArgs &a, hipStream_t s) {
   constexpr int NB = SH ? 1 : kMfmaStages;
-  const long long blocks = (long long)a.B * (SH ? a.Hkv : a.Hkv / W) * a.nsplit;
+  const long long blocks =
+      STREAM ? a.stream_wg : (long long)a.B * (SH ? a.Hkv : a.Hkv / W) * a.nsplit;
   const float scale_log2 = (float)((double)a.softmax_scale * 1.4426950408889634074);
-  hipLaunchKernelGGL((decode_mfma_kernel<D, W, NB, FP8, WIN, SH>), dim3((unsigned)blocks), dim3(W * 64), 0,
+  hipLaunchKernelGGL((decode_mfma_kernel<D, W, NB, FP8, WIN, SH, STREAM>), dim3((unsigned)blocks), dim3(W * 64), 0,
                      s, (const uint16_t *)a.q, a.k_cache, a.v_cache, a.seqlens, a.q_pos, a.B,
                      a.max_cache_len, a.Hq, a.Hkv, a.theta, scale_log2, a.chunk, a.nsplit,
                      a.part_o, a.part_lse, a.dev_flag, a.window, a.sinks, a.k_scale, a.v_scale,
@@ -1064,7 +1144,10 @@ hipError_t launch_mfma(const DecodeArgs &a, hipStream_t s) {
         if constexpr (mfma_ring_bytes(8, D, EB) <= kMfmaLdsBudget)
           return launch_mfma_w<D, FP8, WIN, 8>(a, s);
         return hipErrorInvalidValue;
-      case 4: return launch_mfma_w<D, FP8, WIN, 4>(a, s);
+      case 4:
+        if constexpr (!WIN)
+          if (a.stream_wg > 0) return launch_mfma_w<D, FP8, WIN, 4, false, true>(a, s);
+        return launch_mfma_w<D, FP8, WIN, 4>(a, s);
       case 2: return launch_mfma_w<D, FP8, WIN, 2>(a, s);
       default: return launch_mfma_w<D, FP8, WIN, 1>(a, s);
     }
@@ -1077,11 +1160,11 @@ hipError_t launch_merge(const DecodeArgs &a, hipStream_t s) {
   if (a.out_dtype == YR_F32)
     hipLaunchKernelGGL((decode_merge_kernel<D, true>), grid, block, 0, s, a.part_o, a.part_lse,
                        a.seqlens, a.Hq, a.max_cache_len, a.chunk, a.nsplit, a.vis_split, a.out,
-                       a.lse);
+                       a.lse, a.B, a.Hkv, a.stream_wg, a.stream_hpw);
   else
     hipLaunchKernelGGL((decode_merge_kernel<D, false>), grid, block, 0, s, a.part_o, a.part_lse,
                        a.seqlens, a.Hq, a.max_cache_len, a.chunk, a.nsplit, a.vis_split, a.out,
-                       a.lse);
+                       a.lse, a.B, a.Hkv, a.stream_wg, a.stream_hpw);
   return hipGetLastError();
 }
 
@@ -1089,6 +1172,21 @@ hipError_t launch_merge(const DecodeArgs &a, hipStream_t s) {
 
 int decode_wg_groups(int Hkv, int head_dim, bool fp8, bool win) {
   return decode_shared_form(fp8, win) ? Hkv : Hkv / heads_per_wg(Hkv, head_dim, fp8 ? 1 : 2);
+}
+
+int decode_stream_wgs() {
+  // one workgroup per CU (the head-per-wave ring takes most of a CU's LDS);
+  // the CU count is read once per device
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 0;
+  n = n < kDecodeStreamMaxWg ? n : kDecodeStreamMaxWg;
+  if (dev < 64) cached[dev] = n;
+  return n;
 }
 
 int decode_chunk(int B, int max_cache_len, int units, int min_chunk) {

@@ -84,6 +84,11 @@ struct DecodeArgs {
   const float *k_scale;  // YR_FP8_E4M3 caches: per-KV-head scales
   const float *v_scale;
   int vis_split;         // 1: chunks split the visible rows (window), not [0, L)
+  // > 0: balanced split of the head-per-wave form over stream_wg workgroups
+  // of stream_hpw KV heads (chunk / nsplit unused); partials [stream_wg +
+  // B * Hkv / stream_hpw][stream_hpw * Hq / Hkv][D]
+  int stream_wg;
+  int stream_hpw;
 };
 
 hipError_t launch_rope(const RopeArgs &a, hipStream_t s);
@@ -108,6 +113,16 @@ int decode_wg_groups(int Hkv, int head_dim, bool fp8, bool win);
 inline int decode_min_chunk_mfma(bool fp8, bool win) {
   return decode_shared_form(fp8, win) ? kDecodeMinChunk : kDecodeMinChunkMfma;
 }
+// Balanced split: used for the head-per-wave form without a window when the
+// caches hold at least kDecodeStreamMinKeys keys in all; at most
+// kDecodeStreamMaxWg workgroups (one per CU).
+constexpr long long kDecodeStreamMinKeys = 512 * 1024;
+constexpr int kDecodeStreamMaxWg = 1024;
+inline bool decode_stream_eligible(int B, int max_cache_len) {
+  return (long long)B * max_cache_len >= kDecodeStreamMinKeys;
+}
+// workgroups of the balanced split on the current device (its CU count)
+int decode_stream_wgs();
 inline int decode_nsplit(int max_cache_len, int chunk) {
   return (max_cache_len + chunk - 1) / chunk;
 }
