@@ -232,7 +232,7 @@ def bench_decode(args, torch, ops, wl):
            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                         "traffic": traffic_from_profiles("decode", cfg.name, digest),
-                        "kernel": "decode_mfma_kernel<128,4,2,false,false,false> + decode_merge_kernel<128,false> (one call)",
+                        "kernel": "decode_mfma_kernel<128,4,2,false,false,false,true> + decode_merge_kernel<128,false> (one call)",
                         "kernel_ms": round(call_ms, 4), "bytes_per_launch": int(nbytes)},
            "source_digest": digest}
     state = {"seqlens": inp["seqlens"], "sl": sl, "q": q, "kc": kc, "vc": vc, "theta": theta,

@@ -1,8 +1,8 @@
 """attn_decode_fp8 (E4M3 cache, per-KV-head scales) on the GPU against the
 oracle over the exactly decoded cache: small caches in full (head_dim 64 and
 128, 1 to 32 query heads per KV head, windows with sinks, NaN codes past every
-sequence), four cache-length-128K sequences of the decode workload's shape,
-and the cross-check with the bf16 decode over the same values (exact in
+sequence), four cache-length-128K sequences of the decode workload's shape, the
+balanced split over short and full caches, and the cross-check with the bf16 decode over the same values (exact in
 bf16)."""
 
 import numpy as np
@@ -81,6 +81,27 @@ def test_decode_fp8_long_caches():
     say(f"fp8 decode 4 long caches, seqlens={list(inp['seqlens'])}")
     out, lse = _run(inp, cfg, out_dtype=ops.YR_BF16)
     ro, rl = _oracle(inp, cfg)
+    e_out, e_lse = max_abs(out, ro), max_abs(lse, rl)
+    print(f"max-abs out {e_out:.3e} lse {e_lse:.3e}")
+    assert e_out <= BF16_TOL and e_lse <= BF16_TOL
+
+
+@pytest.mark.parametrize("hq,hkv,D", [(32, 8, 128), (16, 4, 64)])
+def test_decode_fp8_balanced_split(hq, hkv, D):
+    """Caches of >= 512K keys in all take the balanced split (head-per-wave
+    form, one workgroup per CU): very short, full and odd lengths."""
+    B, lmax = 10, 60000
+    cfg = _cfg(hq, hkv, D)
+    inp = wl.make_decode_fp8(cfg, seed=95 + D, batch=B, max_cache_len=lmax, min_cache_len=lmax)
+    lens = np.array([1, 31, 32, 33, lmax, lmax - 1, 1000, 20000, 7, 45001], dtype=np.int32)
+    for name in ("k_cache", "v_cache"):
+        for b in range(B):
+            inp[name][b, lens[b]:] = wl.E4M3_NAN_CODE
+    inp["seqlens"] = lens
+    say(f"fp8 decode balanced split hq={hq} hkv={hkv} D={D} seqlens={lens.tolist()}")
+    out, lse = _run(inp, cfg)
+    ro, rl = _oracle(inp, cfg)
+    assert np.all(np.isfinite(out))
     e_out, e_lse = max_abs(out, ro), max_abs(lse, rl)
     print(f"max-abs out {e_out:.3e} lse {e_lse:.3e}")
     assert e_out <= BF16_TOL and e_lse <= BF16_TOL

@@ -322,9 +322,14 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
   // the matrix-core kernel launches one workgroup per group of KV heads, the
   // fp32 one per head: chunk so that either launches enough workgroups
   const bool fp8 = cache_dtype == YR_FP8_E4M3, win = window > 0;
-  const int units = cache_dtype == YR_F32 ? Hkv : decode_wg_groups(Hkv, head_dim, fp8, win);
+  const bool balanced =
+      cache_dtype != YR_F32 && decode_stream_form(B, max_cache_len, Hkv, head_dim, fp8, win);
+  const bool shared = decode_shared_form(fp8, win, balanced);
+  const int units = cache_dtype == YR_F32 || shared
+                        ? Hkv
+                        : Hkv / decode_heads_per_wg(Hkv, head_dim, fp8);
   const int min_chunk =
-      cache_dtype == YR_F32 ? kDecodeMinChunk : decode_min_chunk_mfma(fp8, win);
+      cache_dtype == YR_F32 || shared ? kDecodeMinChunk : kDecodeMinChunkMfma;
   int chunk = decode_chunk(B, max_cache_len, units, min_chunk);
   int nsplit = decode_nsplit(max_cache_len, chunk);
   // With a window the matrix-core sweep can split the visible rows alone
@@ -344,14 +349,13 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
   }
   if ((long long)B * Hkv * nsplit > 0x7fffffffLL) return bad(YR_ERR_INVALID, "grid too large");
   size_t rows = (size_t)B * Hq * nsplit;
-  // head-per-wave bf16 sweep of a large cache, four KV heads per workgroup:
-  // split the key blocks evenly over one workgroup per CU instead
+  // head-per-wave sweep of a large cache, four or eight KV heads per
+  // workgroup: split the key blocks evenly over one workgroup per CU instead
   int stream_wg = 0, stream_hpw = 0;
-  if (cache_dtype == YR_BF16 && !win && !decode_shared_form(fp8, win) &&
-      Hkv / units == 4 && decode_stream_eligible(B, max_cache_len)) {
+  if (balanced) {
     stream_wg = decode_stream_wgs();
     if (stream_wg <= 0) return bad(YR_ERR_HIP, "cannot query the device's compute units");
-    stream_hpw = 4;
+    stream_hpw = Hkv / units;
     rows = ((size_t)stream_wg + (size_t)B * units) * (size_t)(Hq / units);
   }
   char *ws = static_cast<char *>(workspace);
@@ -384,6 +388,7 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
   d.vis_split = vis_split;
   d.stream_wg = stream_wg;
   d.stream_hpw = stream_hpw;
+  d.shared_form = shared ? 1 : 0;
   const hipError_t e = launch_decode(d, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, fn);
   return YR_OK;

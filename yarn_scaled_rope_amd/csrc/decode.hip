@@ -1136,13 +1136,16 @@ hipError_t launch_mfma_w(const DecodeArgs &a, hipStream_t s) {
 template <int D, bool FP8, bool WIN>
 hipError_t launch_mfma(const DecodeArgs &a, hipStream_t s) {
   constexpr int EB = FP8 ? 1 : 2;
-  if constexpr (decode_shared_form(FP8, WIN)) {
+  if (a.shared_form) {
     return launch_mfma_w<D, FP8, WIN, 4, true>(a, s);
   } else {
     switch (heads_per_wg(a.Hkv, D, EB)) {
       case 8:
-        if constexpr (mfma_ring_bytes(8, D, EB) <= kMfmaLdsBudget)
+        if constexpr (mfma_ring_bytes(8, D, EB) <= kMfmaLdsBudget) {
+          if constexpr (!WIN)
+            if (a.stream_wg > 0) return launch_mfma_w<D, FP8, WIN, 8, false, true>(a, s);
           return launch_mfma_w<D, FP8, WIN, 8>(a, s);
+        }
         return hipErrorInvalidValue;
       case 4:
         if constexpr (!WIN)
@@ -1170,8 +1173,8 @@ hipError_t launch_merge(const DecodeArgs &a, hipStream_t s) {
 
 }  // namespace
 
-int decode_wg_groups(int Hkv, int head_dim, bool fp8, bool win) {
-  return decode_shared_form(fp8, win) ? Hkv : Hkv / heads_per_wg(Hkv, head_dim, fp8 ? 1 : 2);
+int decode_heads_per_wg(int Hkv, int head_dim, bool fp8) {
+  return heads_per_wg(Hkv, head_dim, fp8 ? 1 : 2);
 }
 
 int decode_stream_wgs() {

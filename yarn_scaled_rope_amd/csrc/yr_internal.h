@@ -89,6 +89,7 @@ struct DecodeArgs {
   // B * Hkv / stream_hpw][stream_hpw * Hq / Hkv][D]
   int stream_wg;
   int stream_hpw;
+  int shared_form;       // matrix-core decode: 1 = shared form, 0 = head per wave
 };
 
 hipError_t launch_rope(const RopeArgs &a, hipStream_t s);
@@ -106,20 +107,28 @@ int decode_chunk(int B, int max_cache_len, int units, int min_chunk);
 // whole chunk for one KV head and a workgroup takes 8, 4, 2 or 1 KV heads
 // (the largest dividing Hkv whose LDS ring fits the budget).  Shared: four
 // waves take alternate blocks of one KV head's chunk and combine in LDS.
-constexpr bool decode_shared_form(bool fp8, bool win) { return fp8 || win; }
-// Workgroups per (sequence, chunk) of the matrix-core decode, and the least
-// chunk length worth a workgroup.
-int decode_wg_groups(int Hkv, int head_dim, bool fp8, bool win);
-inline int decode_min_chunk_mfma(bool fp8, bool win) {
-  return decode_shared_form(fp8, win) ? kDecodeMinChunk : kDecodeMinChunkMfma;
-}
-// Balanced split: used for the head-per-wave form without a window when the
-// caches hold at least kDecodeStreamMinKeys keys in all; at most
-// kDecodeStreamMaxWg workgroups (one per CU).
+// KV heads per workgroup of the head-per-wave form:
+int decode_heads_per_wg(int Hkv, int head_dim, bool fp8);
+// Balanced split of the head-per-wave form (no window, 4 or 8 KV heads per
+// workgroup) when the caches hold at least kDecodeStreamMinKeys keys in all:
+// the key blocks are cut evenly over one workgroup per CU (at most
+// kDecodeStreamMaxWg).
 constexpr long long kDecodeStreamMinKeys = 512 * 1024;
 constexpr int kDecodeStreamMaxWg = 1024;
 inline bool decode_stream_eligible(int B, int max_cache_len) {
   return (long long)B * max_cache_len >= kDecodeStreamMinKeys;
+}
+inline bool decode_stream_form(int B, int max_cache_len, int Hkv, int head_dim, bool fp8,
+                               bool win) {
+  const int hpw = decode_heads_per_wg(Hkv, head_dim, fp8);
+  return !win && (hpw == 4 || hpw == 8) && decode_stream_eligible(B, max_cache_len);
+}
+// Which form: a window takes the shared form (its chunks are short); an FP8
+// cache takes it too unless the balanced split applies (measured: shared
+// 6.0 TB/s, head-per-wave in chunks 5.3-5.9, balanced split 6.3); bf16 takes
+// the head-per-wave form.
+inline bool decode_shared_form(bool fp8, bool win, bool stream) {
+  return win || (fp8 && !stream);
 }
 // workgroups of the balanced split on the current device (its CU count)
 int decode_stream_wgs();
