@@ -105,6 +105,59 @@ def test_decode_balanced_split(hq, hkv, D, use_qpos):
     assert e_out <= BF16_TOL and e_lse <= BF16_TOL
 
 
+@pytest.mark.parametrize("window,sinks,lmax", [(4096, 4, 60000), (100, 0, 60000), (1, 3, 60000),
+                                               (60000, 4, 70000), (70000, 2, 60000)])
+def test_decode_balanced_split_window(window, sinks, lmax):
+    """Windows and sinks on large caches: short windows take the shared form
+    in chunks; windows whose visible rows reach 512K keys in all take the
+    balanced split, where a sequence contributes its visible rows only, sinks
+    first; query positions at, inside and past the cache."""
+    B, hq, hkv, D = 10, 32, 8, 128
+    cfg = _cfg("bf16", hq, hkv, D)
+    inp = wl.make_decode(cfg, seed=79, batch=B, max_cache_len=lmax, min_cache_len=lmax)
+    lens = np.array([1, 31, 32, 33, lmax, lmax - 1, 1000, 20000, 7, 45001], dtype=np.int32)
+    for name in ("k_cache", "v_cache"):
+        for b in range(B):
+            inp[name][b, lens[b]:] = wl.BF16_NAN_BITS
+    inp["seqlens"] = lens
+    q_pos = [int(L) if b % 3 == 0 else int(L) // 2 if b % 3 == 1 else int(L) + 50
+             for b, L in enumerate(lens)]
+    say(f"decode balanced split window={window} sinks={sinks} seqlens={lens.tolist()} "
+        f"q_pos={q_pos}")
+    th_dev, scale = lib_theta(D, cfg.base, cfg.factor, cfg.original_max_position)
+    out, lse = ops.attn_decode(to_dev(inp["q"], "bf16"), to_dev(inp["k_cache"], "bf16"),
+                               to_dev(inp["v_cache"], "bf16"),
+                               torch.from_numpy(lens).cuda(), th_dev, scale,
+                               q_pos=torch.tensor(q_pos, dtype=torch.int32, device="cuda"),
+                               out_dtype=ops.YR_F32, window=window, sinks=sinks)
+    torch.cuda.synchronize()
+    got, gl = to_f64(out), lse.cpu().numpy().astype(np.float64)
+    # queries that see no row (past the window, no sinks before it): 0 / -inf
+    seen = np.array([window == 0 or bool(np.any((np.arange(L) > q - window) | (np.arange(L) < sinks)))
+                     for L, q in zip(lens.tolist(), q_pos)])
+    assert np.all(got[~seen] == 0.0) and np.all(np.isneginf(gl[~seen]))
+    idx = np.flatnonzero(seen)
+    th, sc = oracle_theta(D, cfg.base, cfg.factor, cfg.original_max_position)
+    ro, rl = oatt.decode(wl.as_f64(inp["q"], "bf16")[idx], _Rows(LazyF64(inp["k_cache"], "bf16"), idx),
+                         _Rows(LazyF64(inp["v_cache"], "bf16"), idx), lens[idx], th, sc,
+                         q_pos=[q_pos[i] for i in idx], window=window, sinks=sinks)
+    e_out, e_lse = max_abs(got[idx], ro), max_abs(gl[idx], rl)
+    print(f"{len(idx)} of {B} see rows: max-abs out {e_out:.3e} lse {e_lse:.3e}")
+    assert e_out <= BF16_TOL and e_lse <= BF16_TOL
+
+
+class _Rows:
+    """The caches of the sequences in idx only (the oracle slices [b, :L, h, :])."""
+
+    def __init__(self, cache, idx):
+        self.cache, self.idx = cache, idx
+        self.shape = (len(idx),) + tuple(cache.shape[1:])
+
+    def __getitem__(self, key):
+        b, rows, h, d = key
+        return self.cache[int(self.idx[b]), rows, h, d]
+
+
 def test_decode_matches_prefill_last_row():
     """Decode at q_pos = L-1 over the keys rotated by rope_apply equals row
     L-1 of prefill over the same unrotated inputs."""

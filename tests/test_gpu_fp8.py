@@ -86,8 +86,9 @@ def test_decode_fp8_long_caches():
     assert e_out <= BF16_TOL and e_lse <= BF16_TOL
 
 
-@pytest.mark.parametrize("hq,hkv,D", [(32, 8, 128), (16, 4, 64)])
-def test_decode_fp8_balanced_split(hq, hkv, D):
+@pytest.mark.parametrize("hq,hkv,D,window,sinks", [(32, 8, 128, 0, 0), (16, 4, 64, 0, 0),
+                                                  (32, 8, 128, 3000, 4)])
+def test_decode_fp8_balanced_split(hq, hkv, D, window, sinks):
     """Caches of >= 512K keys in all take the balanced split (head-per-wave
     form, one workgroup per CU): very short, full and odd lengths."""
     B, lmax = 10, 60000
@@ -98,9 +99,10 @@ def test_decode_fp8_balanced_split(hq, hkv, D):
         for b in range(B):
             inp[name][b, lens[b]:] = wl.E4M3_NAN_CODE
     inp["seqlens"] = lens
-    say(f"fp8 decode balanced split hq={hq} hkv={hkv} D={D} seqlens={lens.tolist()}")
-    out, lse = _run(inp, cfg)
-    ro, rl = _oracle(inp, cfg)
+    say(f"fp8 decode balanced split hq={hq} hkv={hkv} D={D} W={window} S={sinks} "
+        f"seqlens={lens.tolist()}")
+    out, lse = _run(inp, cfg, window, sinks)
+    ro, rl = _oracle(inp, cfg, window, sinks)
     assert np.all(np.isfinite(out))
     e_out, e_lse = max_abs(out, ro), max_abs(lse, rl)
     print(f"max-abs out {e_out:.3e} lse {e_lse:.3e}")

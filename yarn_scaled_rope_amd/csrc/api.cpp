@@ -323,7 +323,7 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
   // fp32 one per head: chunk so that either launches enough workgroups
   const bool fp8 = cache_dtype == YR_FP8_E4M3, win = window > 0;
   const bool balanced =
-      cache_dtype != YR_F32 && decode_stream_form(B, max_cache_len, Hkv, head_dim, fp8, win);
+      cache_dtype != YR_F32 && decode_stream_form(B, max_cache_len, Hkv, head_dim, fp8, window, sinks);
   const bool shared = decode_shared_form(fp8, win, balanced);
   const int units = cache_dtype == YR_F32 || shared
                         ? Hkv

@@ -510,7 +510,21 @@ __device__ __forceinline__ void tr8_reads(u32x2 (&r)[DBLK], const uint32_t (&a)[
 // share one KV head and take alternate blocks of the chunk, then combine
 // through LDS (the FP8 form: its blocks are half the bytes and twice the
 // conversion work, and measured faster this way, 6.2 against 5.9 TB/s).
-// STREAM (head-per-wave form, no window): instead of one chunk per
+// Cache rows of sequence bb that its query sees: all of [0, L), or with a
+// window the sinks [0, se) and the window [lo, L) (the query at q_pos or L).
+__device__ __forceinline__ int decode_visible_rows(int bb, const int *seqlens, const int *qpos,
+                                                   int Lmax, int window, int sinks) {
+  int L = seqlens[bb];
+  L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+  if (window <= 0) return L;
+  int qm = qpos != nullptr ? qpos[bb] : L;
+  qm = qm < 0 ? 0 : qm;
+  const int lo = max(0, qm - window + 1);
+  const int se = min(sinks, lo);
+  return se + max(0, L - lo);
+}
+
+// STREAM (head-per-wave form): instead of one chunk per
 // workgroup, the flattened space of (sequence, head group, 32-key block) is
 // cut into gridDim.x equal ranges, one per workgroup (one per CU); a
 // workgroup sweeps the pieces of the segments its range meets and writes one
@@ -543,12 +557,13 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
   constexpr int HW = SH ? 1 : W;  // KV heads of the workgroup
 
   if (flag != nullptr && blockIdx.x == 0) validate_decode_lens(seqlens, qpos, B, Lmax, flag);
-  static_assert(!STREAM || (!SH && !WIN), "the balanced split is for the head-per-wave form");
+  static_assert(!STREAM || !SH, "the balanced split is for the head-per-wave form");
 
-  // STREAM: this workgroup's range [r, r1) of the flattened block space
+  // STREAM: this workgroup's range [r, r1) of the flattened block space;
+  // a sequence contributes the 32-key blocks of its visible rows (all of
+  // [0, L), or with a window the sinks and then the window, counted in order)
   auto nblocks_of = [&](int bb) {
-    const int Lb = seqlens[bb];
-    return ((Lb < 0 ? 0 : (Lb > Lmax ? Lmax : Lb)) + kBlk - 1) / kBlk;
+    return (decode_visible_rows(bb, seqlens, qpos, Lmax, window, sinks) + kBlk - 1) / kBlk;
   };
   const int ngr = Hkv / HW;
   int r = 0, r1 = 0;
@@ -597,7 +612,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
   const int g = Hq / Hkv;
   int L = seqlens[b];
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-  if (vis_split == 0 && c0 >= L) return;
+  if (!STREAM && vis_split == 0 && c0 >= L) return;
   int qm = qpos != nullptr ? qpos[b] : L;  // the query's position
   qm = qm < 0 ? 0 : qm;
 
@@ -622,9 +637,10 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     se = min(sinks, lo);
   }
   int na, b0, nb;
-  if (vis_split != 0) {
+  if (vis_split != 0 || (STREAM && WIN)) {
     const int nvis = se + max(0, L - lo);
-    const int v1 = split == nsplit - 1 ? nvis : min(nvis, c0 + chunk);
+    const int v1 = STREAM ? min(nvis, c0 + cnt * kBlk)
+                          : (split == nsplit - 1 ? nvis : min(nvis, c0 + chunk));
     na = max(0, min(v1, se) - c0);
     b0 = lo + max(c0, se) - se;
     nb = max(0, v1 - max(c0, se));
@@ -995,7 +1011,8 @@ template <int D, bool OUT_F32>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float *__restrict__ part_o, const float *__restrict__ part_lse,
     const int *__restrict__ seqlens, int Hq, int Lmax, int chunk, int nsplit, int vis_split,
-    void *__restrict__ out, float *__restrict__ lse, int B, int Hkv, int nwg, int hpw) {
+    void *__restrict__ out, float *__restrict__ lse, int B, int Hkv, int nwg, int hpw,
+    const int *__restrict__ qpos, int window, int sinks) {
   constexpr int PER = D / 64;  // output elements per lane
   constexpr int MW = 4;        // waves; wave w takes partials w, w+4, ...
   constexpr int U = 4;         // partials per wave in flight
@@ -1016,8 +1033,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     const int g = Hq / Hkv, ngr = Hkv / hpw;
     const int hk = h / g, hg = hk / hpw;
     auto nblocks_of = [&](int bb) {
-      const int Lb = seqlens[bb];
-      return ((Lb < 0 ? 0 : (Lb > Lmax ? Lmax : Lb)) + kBlk - 1) / kBlk;
+      return (decode_visible_rows(bb, seqlens, qpos, Lmax, window, sinks) + kBlk - 1) / kBlk;
     };
     long long tb = 0, base = 0;
     for (int bb = 0; bb < B; ++bb) {
@@ -1142,14 +1158,12 @@ hipError_t launch_mfma(const DecodeArgs &a, hipStream_t s) {
     switch (heads_per_wg(a.Hkv, D, EB)) {
       case 8:
         if constexpr (mfma_ring_bytes(8, D, EB) <= kMfmaLdsBudget) {
-          if constexpr (!WIN)
-            if (a.stream_wg > 0) return launch_mfma_w<D, FP8, WIN, 8, false, true>(a, s);
+          if (a.stream_wg > 0) return launch_mfma_w<D, FP8, WIN, 8, false, true>(a, s);
           return launch_mfma_w<D, FP8, WIN, 8>(a, s);
         }
         return hipErrorInvalidValue;
       case 4:
-        if constexpr (!WIN)
-          if (a.stream_wg > 0) return launch_mfma_w<D, FP8, WIN, 4, false, true>(a, s);
+        if (a.stream_wg > 0) return launch_mfma_w<D, FP8, WIN, 4, false, true>(a, s);
         return launch_mfma_w<D, FP8, WIN, 4>(a, s);
       case 2: return launch_mfma_w<D, FP8, WIN, 2>(a, s);
       default: return launch_mfma_w<D, FP8, WIN, 1>(a, s);
@@ -1163,11 +1177,11 @@ hipError_t launch_merge(const DecodeArgs &a, hipStream_t s) {
   if (a.out_dtype == YR_F32)
     hipLaunchKernelGGL((decode_merge_kernel<D, true>), grid, block, 0, s, a.part_o, a.part_lse,
                        a.seqlens, a.Hq, a.max_cache_len, a.chunk, a.nsplit, a.vis_split, a.out,
-                       a.lse, a.B, a.Hkv, a.stream_wg, a.stream_hpw);
+                       a.lse, a.B, a.Hkv, a.stream_wg, a.stream_hpw, a.q_pos, a.window, a.sinks);
   else
     hipLaunchKernelGGL((decode_merge_kernel<D, false>), grid, block, 0, s, a.part_o, a.part_lse,
                        a.seqlens, a.Hq, a.max_cache_len, a.chunk, a.nsplit, a.vis_split, a.out,
-                       a.lse, a.B, a.Hkv, a.stream_wg, a.stream_hpw);
+                       a.lse, a.B, a.Hkv, a.stream_wg, a.stream_hpw, a.q_pos, a.window, a.sinks);
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
 
@@ -118,17 +119,24 @@ constexpr int kDecodeStreamMaxWg = 1024;
 inline bool decode_stream_eligible(int B, int max_cache_len) {
   return (long long)B * max_cache_len >= kDecodeStreamMinKeys;
 }
+// With a window the visible rows decide (window + sinks per sequence at most):
+// a short window leaves too few blocks per CU for one workgroup per CU to
+// keep enough copies in flight (W 4096 on 16 sequences measured 0.0576 ms
+// against 0.0551 ms in shared-form chunks).
 inline bool decode_stream_form(int B, int max_cache_len, int Hkv, int head_dim, bool fp8,
-                               bool win) {
+                               int window, int sinks) {
   const int hpw = decode_heads_per_wg(Hkv, head_dim, fp8);
-  return !win && (hpw == 4 || hpw == 8) && decode_stream_eligible(B, max_cache_len);
+  const long long span = window > 0 ? std::min<long long>(max_cache_len, (long long)window + sinks)
+                                    : max_cache_len;
+  return (hpw == 4 || hpw == 8) && decode_stream_eligible(B, max_cache_len) &&
+         (long long)B * span >= kDecodeStreamMinKeys;
 }
-// Which form: a window takes the shared form (its chunks are short); an FP8
-// cache takes it too unless the balanced split applies (measured: shared
-// 6.0 TB/s, head-per-wave in chunks 5.3-5.9, balanced split 6.3); bf16 takes
-// the head-per-wave form.
+// Which form without the balanced split: a window takes the shared form (its
+// chunks are short), an FP8 cache too (measured: shared 6.0 TB/s,
+// head-per-wave in chunks 5.3-5.9, balanced split 6.3); bf16 takes the
+// head-per-wave form.
 inline bool decode_shared_form(bool fp8, bool win, bool stream) {
-  return win || (fp8 && !stream);
+  return (win || fp8) && !stream;
 }
 // workgroups of the balanced split on the current device (its CU count)
 int decode_stream_wgs();
