@@ -262,15 +262,20 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       u32x4 w = {0u, 0u, 0u, 0u};
       if (qvalid) {
         w = *reinterpret_cast<const u32x4 *>(qp + kk * 16);
-        if (ROTATE_Q) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < 4; ++e) {
+          if (ROTATE_Q) {
             float x0 = bf16_to_f32(w[e] & 0xffffu), x1 = bf16_to_f32(w[e] >> 16);
             float c, s;
             rope_cos_sin((double)(P + tq), theta[kk * 8 + hh * 4 + e], &c, &s);
             rotate_pair(x0, x1, c, s);
-            w[e] = pack_bf16x2(x0, x1);
+            w[e] = pack_bf16x2(x0, x1);  // the rotated query in bf16, as a caller would pass it
           }
+          // the logit scale (log2 units) folded into the query, so that the
+          // scores come out of the matrix cores ready for exp2
+          const float y0 = bf16_to_f32(w[e] & 0xffffu) * scale_log2;
+          const float y1 = bf16_to_f32(w[e] >> 16) * scale_log2;
+          w[e] = pack_bf16x2(y0, y1);
         }
       }
       qf[kk] = as_bf16x8(w);
@@ -282,6 +287,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
   float m_run = -INFINITY;
   float l_part = 0.f;
+  // -m_run (0 while m_run = -inf) in every slot: the accumulator the score
+  // MFMAs start from, so that they return s * scale - m directly
+  f32x16 negm = f32x16{};
 
   // LDS operand addresses (elements).  K: row kb*32 + l32, chunk 2kk + hh.
   // V^T (transposing reads): lane t of a 16-lane group reads 4 elements of key
@@ -315,19 +323,20 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const uint16_t *ks = kst(par);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
         const bf16x8 a = as_bf16x8(
             *reinterpret_cast<const u32x4 *>(ks + (kb * 32 + l32) * D + 8 * ((2 * kk + hh) ^ kx)));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], kk == 0 ? negm : s[kb], 0, 0, 0);
       }
     }
   };
 
   // softmax front half of tile j: mask (diagonal/tail tiles only), row max,
   // lazy rescale of the running state; returns -m for the exp2 argument
-  auto softmax_front = [&](int j, f32x16 (&s)[2], bool may_mask) YR_INLINE -> float {
+  // nx: the scores of the next tile, already issued against the old -m_run,
+  // which move to the new reference with this tile's
+  auto softmax_front = [&](int j, f32x16 (&s)[2], f32x16 (&nx)[2], bool may_mask) YR_INLINE -> float {
     const int key0 = j * kBC;
     const bool wmask = window > 0 && key0 <= P + tw0 + 31 - window && key0 + kBC > sinks;
     if (may_mask && ((key0 + kBC - 1 > P + tw0) || (key0 + kBC > nk) || wmask)) {
@@ -349,19 +358,33 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
     }
-    mx = half_max(mx) * scale_log2;   // row max on raw scores (scale > 0)
-    const bool grow = mx > m_run + 8.0f;                 // lazy running max
+    // the tile's row max less m_run (the scores carry -m_run already)
+    mx = half_max(mx);
+    const bool first = m_run == -INFINITY;
+    const bool grow = first ? mx > -INFINITY : mx > 8.0f;  // lazy running max
     if (__any(grow)) {
-      const float m_new = grow ? mx : m_run;
+      const float m_new = grow ? (first ? mx : m_run + mx) : m_run;
       // 0 when m_run = -inf; 1 for a row that has seen no visible key yet
       // (with a window a row can meet tiles it does not see at all)
       const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      // move this tile's scores to the new reference
+      const float shift = (first ? 0.f : m_run) - (m_new == -INFINITY ? 0.f : m_new);
       m_run = m_new;
       l_part *= alpha;
 #pragma unroll
       for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          s[kb][rr] += shift;
+          nx[kb][rr] += shift;
+        }
+      const float nm = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) negm[rr] = nm;
     }
-    return (m_run == -INFINITY) ? 0.f : -m_run;
+    return 0.f;
   };
 
   // softmax back half: P = exp2(s*scale - m) in bf16, row sum.  The 8
@@ -372,8 +395,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       u32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][(ks & 1) * 8 + 2 * e], scale_log2, neg_m));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][(ks & 1) * 8 + 2 * e + 1], scale_log2, neg_m));
+        const float p0 = __builtin_amdgcn_exp2f(s[ks >> 1][(ks & 1) * 8 + 2 * e]);
+        const float p1 = __builtin_amdgcn_exp2f(s[ks >> 1][(ks & 1) * 8 + 2 * e + 1]);
         l_part += p0 + p1;
         w[e] = pack_bf16x2(p0, p1);
       }
@@ -421,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     stage(par, i);
     if (i + 1 < count && active(tile_of(i + 1))) scores(nextp(par), nxt);
     if (active(tile_of(i))) {
-      const float neg_m = softmax_front(tile_of(i), cur, true);
+      const float neg_m = softmax_front(tile_of(i), cur, nxt, true);
       bf16x8 pf[4];
       softmax_back(cur, neg_m, pf);
       pv(par, pf);
@@ -436,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   auto step_clear = [&](auto par, int i, f32x16 (&cur)[2], f32x16 (&nxt)[2]) YR_INLINE {
     stage(par, i);
     scores(nextp(par), nxt);
-    const float neg_m = softmax_front(tile_of(i), cur, false);
+    const float neg_m = softmax_front(tile_of(i), cur, nxt, false);
     bf16x8 pf[4];
     softmax_back(cur, neg_m, pf);
     pv(par, pf);
