@@ -228,9 +228,11 @@ size_t attn_decode_workspace_bytes(int B, int max_cache_len, int Hq, int head_di
  * research hub, "Key math").  The query of sequence b is rotated at q_pos[b]
  * (or at seqlens[b] when q_pos is NULL) and attends, unmasked, to cache rows
  * 0 .. seqlens[b]-1, whose keys are taken as already rotated.  The cache is
- * swept in fixed-size key chunks in parallel; each chunk yields a partial
- * (out, LSE) and the partials are merged by log-sum-exp ("Long-context
- * models", "Context parallelism distributes exact attention").
+ * swept in parallel pieces -- fixed-size key chunks, or for caches of 512K
+ * keys or more in all, equal ranges of 32-key blocks, one per compute unit;
+ * each piece yields a partial (out, LSE) and the partials are merged by
+ * log-sum-exp ("Long-context models", "Context parallelism distributes exact
+ * attention").
  * With window = W > 0 only the cache rows the query's window and sinks make
  * visible are read (rows > m - W, and rows < sinks, m = its position): the
  * rest of the cache costs no bandwidth.  The new token's own row is not in

@@ -244,6 +244,11 @@ def test_workspace_sizes(lib):
     assert n > 16 * 32 * 128 * 4 and n % 256 == 0
     # larger caches never need less
     assert ops.attn_decode_workspace_bytes(16, 262144, 32, 128) >= n
+    # caches of >= 512K keys in all may take the balanced split: room for
+    # (1024 workgroups + B) * Hq partial rows of head_dim + 1 floats
+    for B, L, hq, d in ((1, 524288, 32, 128), (16, 32768, 8, 64), (3, 200000, 64, 128)):
+        assert ops.attn_decode_workspace_bytes(B, L, hq, d) >= 256 + (1024 + B) * hq * (d + 1) * 4
+    assert ops.attn_decode_workspace_bytes(1, 1000, 32, 128) < 1 << 20
 
 
 def test_missing_library_raises(monkeypatch, tmp_path):
