@@ -54,6 +54,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 512;
 constexpr int kBQ = kThreads / 2;  // query rows per workgroup (32 per wave)
 constexpr int kBC = 64;            // keys per tile
+constexpr int KB = kBC / 32;       // 32-key blocks of a tile (score accumulators)
+constexpr int KS = kBC / 16;       // 16-key k-steps of a tile (P fragments)
 constexpr int kXcds = 8;
 constexpr int kMaxRankedSeqs = 64;  // chunked prefill orders up to this many sequences
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -319,10 +321,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 
   // S^T = K Q^T for one tile (two 32-key blocks); accumulator slot rr of block
   // kb (lane half hh) holds key 32 kb + 8 (rr >> 2) + 4 hh + (rr & 3)
-  auto scores = [&](auto par, f32x16 (&s)[2]) YR_INLINE {
+  auto scores = [&](auto par, f32x16 (&s)[KB]) YR_INLINE {
     const uint16_t *ks = kst(par);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
         const bf16x8 a = as_bf16x8(
@@ -336,13 +338,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   // lazy rescale of the running state; returns -m for the exp2 argument
   // nx: the scores of the next tile, already issued against the old -m_run,
   // which move to the new reference with this tile's
-  auto softmax_front = [&](int j, f32x16 (&s)[2], f32x16 (&nx)[2], bool may_mask) YR_INLINE -> float {
+  auto softmax_front = [&](int j, f32x16 (&s)[KB], f32x16 (&nx)[KB], bool may_mask) YR_INLINE -> float {
     const int key0 = j * kBC;
     const bool wmask = window > 0 && key0 <= P + tw0 + 31 - window && key0 + kBC > sinks;
     if (may_mask && ((key0 + kBC - 1 > P + tw0) || (key0 + kBC > nk) || wmask)) {
       const int pos = P + tq;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           const int key = key0 + kb * 32 + (rr >> 2) * 8 + hh * 4 + (rr & 3);
@@ -354,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
     }
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           s[kb][rr] += shift;
@@ -389,9 +391,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 
   // softmax back half: P = exp2(s*scale - m) in bf16, row sum.  The 8
   // accumulator slots 8 (ks & 1) .. +7 of block ks >> 1 form k-step ks.
-  auto softmax_back = [&](f32x16 (&s)[2], float neg_m, bf16x8 (&pf)[4]) YR_INLINE {
+  auto softmax_back = [&](f32x16 (&s)[KB], float neg_m, bf16x8 (&pf)[KS]) YR_INLINE {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       u32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -407,10 +409,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   // O^T += V^T P^T (k-step major: the MFMAs of k-step ks need only pf[ks]).
   // Element e of the operands is key 16 ks + 4 hh + 8 (e >> 2) + (e & 3), the
   // order in which the score accumulator holds P.
-  auto pv = [&](auto par, bf16x8 (&pf)[4]) YR_INLINE {
+  auto pv = [&](auto par, bf16x8 (&pf)[KS]) YR_INLINE {
     const uint16_t *vs = vst(par);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
         const uint16_t *ap = vs + vbase[db] + 16 * ks * D;
@@ -440,12 +442,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   };
   // General step (diagonal, window-edge and tail tiles, the last step): every
   // check.
-  auto step = [&](auto par, int i, f32x16 (&cur)[2], f32x16 (&nxt)[2]) YR_INLINE {
+  auto step = [&](auto par, int i, f32x16 (&cur)[KB], f32x16 (&nxt)[KB]) YR_INLINE {
     stage(par, i);
     if (i + 1 < count && active(tile_of(i + 1))) scores(nextp(par), nxt);
     if (active(tile_of(i))) {
       const float neg_m = softmax_front(tile_of(i), cur, nxt, true);
-      bf16x8 pf[4];
+      bf16x8 pf[KS];
       softmax_back(cur, neg_m, pf);
       pv(par, pf);
     }
@@ -456,11 +458,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   // first, right after the barrier, and the row max, exp / convert work of
   // tile i and its PV MFMAs follow (measured 1-1.5% faster than issuing the
   // scores after the row max).
-  auto step_clear = [&](auto par, int i, f32x16 (&cur)[2], f32x16 (&nxt)[2]) YR_INLINE {
+  auto step_clear = [&](auto par, int i, f32x16 (&cur)[KB], f32x16 (&nxt)[KB]) YR_INLINE {
     stage(par, i);
     scores(nextp(par), nxt);
     const float neg_m = softmax_front(tile_of(i), cur, nxt, false);
-    bf16x8 pf[4];
+    bf16x8 pf[KS];
     softmax_back(cur, neg_m, pf);
     pv(par, pf);
   };
@@ -468,15 +470,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   // prologue: every prologue copy landed; S(tile(0))
   wait_dma<0>();
   __syncthreads();
-  f32x16 sa[2], sb[2];
+  f32x16 sa[KB], sb[KB];
   if (active(tile_of(0))) scores(std::integral_constant<int, 0>{}, sa);
   // Steps are unrolled over the stage index (i % NS) and the score buffer
   // (i % 2), so every LDS array and register array is picked at compile time.
   constexpr int BL = 2;
-  auto sbuf = [&](auto ic) YR_INLINE -> f32x16(&)[2] {
+  auto sbuf = [&](auto ic) YR_INLINE -> f32x16(&)[KB] {
     if constexpr (decltype(ic)::value % 2 == 0) return sa; else return sb;
   };
-  auto obuf = [&](auto ic) YR_INLINE -> f32x16(&)[2] {
+  auto obuf = [&](auto ic) YR_INLINE -> f32x16(&)[KB] {
     if constexpr (decltype(ic)::value % 2 == 0) return sb; else return sa;
   };
   // The tiles that need no mask for any row form one run of the list: from
