@@ -79,10 +79,12 @@ def test_decode_workload_full():
     (32, 8, 128, False),
     (48, 12, 128, True),
     (16, 4, 64, False),
+    (32, 8, 64, True),   # eight KV heads per workgroup
 ])
 def test_decode_balanced_split(hq, hkv, D, use_qpos):
     """Caches of >= 512K keys in all take the balanced split over one
-    workgroup per CU (head-per-wave form, four KV heads per workgroup):
+    workgroup per CU (head-per-wave form, four or eight KV heads per
+    workgroup):
     lengths of 1, 31, 32, 33 keys beside full and odd ones, so that pieces
     start and end inside sequences and some sequences fit inside one piece."""
     B, lmax = 10, 60000

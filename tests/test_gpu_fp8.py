@@ -87,7 +87,8 @@ def test_decode_fp8_long_caches():
 
 
 @pytest.mark.parametrize("hq,hkv,D,window,sinks", [(32, 8, 128, 0, 0), (16, 4, 64, 0, 0),
-                                                  (32, 8, 128, 3000, 4)])
+                                                  (32, 8, 64, 0, 0), (32, 8, 128, 3000, 4),
+                                                  (32, 8, 128, 60000, 4)])
 def test_decode_fp8_balanced_split(hq, hkv, D, window, sinks):
     """Caches of >= 512K keys in all take the balanced split (head-per-wave
     form, one workgroup per CU): very short, full and odd lengths."""
