@@ -313,13 +313,16 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   }
 }
 
-// ---- bf16 inputs: matrix-core split kernel ----------------------------------
-// A workgroup owns (sequence, key chunk, group of W KV heads); wave w sweeps
-// the whole chunk for KV head hg*W + w, so the W waves stream the same cache
-// rows side by side and together read each row's W heads (W*D elements,
-// contiguous) at about the same time: measured 7.1 TB/s for that access
-// pattern against 6.3 TB/s when each workgroup owns one head's 256-byte
-// slices of the rows.  Per 32-key block a wave computes S^T = K Q^T (keys x
+// ---- bf16 / FP8 caches: matrix-core split kernel -----------------------------
+// Head-per-wave form: a workgroup owns (sequence, key range, group of W KV
+// heads), the range being a key chunk or one workgroup's share of a balanced
+// split (STREAM below); wave w sweeps the whole range for KV head hg*W + w,
+// so the W waves stream the same cache rows side by side and together read
+// each row's W heads (W*D elements, contiguous) at about the same time:
+// measured 7.1 TB/s for that access pattern against 6.3 TB/s when each
+// workgroup owns one head's 256-byte slices of the rows.  Shared form (SH):
+// the waves of a workgroup take alternate blocks of one KV head's chunk and
+// combine through LDS.  Per 32-key block a wave computes S^T = K Q^T (keys x
 // query heads of its KV head, v_mfma_f32_32x32x16_bf16 with those heads as
 // the 32 columns) and O^T += V^T P^T, and at the end writes its heads'
 // partial (O, log2-sum-exp) itself.  K and V blocks go straight from HBM into a ring of LDS
@@ -392,7 +395,8 @@ struct MfmaSmem {
 // Ring bytes of a workgroup of W waves (one KV head each).
 constexpr int mfma_ring_bytes(int W, int D, int EB) { return W * kMfmaStages * 2 * kBlk * D * EB; }
 // KV heads per workgroup of the head-per-wave form: the largest of 8, 4, 2,
-// 1 that divides Hkv and keeps the ring within the budget (head_dim 128: 4).
+// 1 that divides Hkv and keeps the ring within the budget (head_dim 128: 4
+// with a bf16 cache, 8 with FP8).
 constexpr int heads_per_wg(int Hkv, int D, int EB) {
   return (Hkv % 8 == 0 && mfma_ring_bytes(8, D, EB) <= kMfmaLdsBudget) ? 8
          : (Hkv % 4 == 0 && mfma_ring_bytes(4, D, EB) <= kMfmaLdsBudget) ? 4
