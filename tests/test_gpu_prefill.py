@@ -190,7 +190,11 @@ def test_prerotated_inputs_equal_fused_rotation():
     ops.rope_apply(kr, pos, th_dev)
     b, bl = ops.attn_prefill_fwd(qr, kr, v, cu, 400, None, scale)
     torch.cuda.synchronize()
-    assert torch.equal(a, b) and torch.equal(al, bl)
+    # the fused path rounds the rotated, scaled query to bf16 once; a
+    # pre-rotated query was rounded once already (by rope_apply), then scaled
+    # and rounded again: equal up to that one bf16 rounding of q
+    assert max_abs(to_f64(a), to_f64(b)) <= BF16_TOL
+    assert max_abs(al.cpu().numpy(), bl.cpu().numpy()) <= BF16_TOL
 
 
 def test_k_rotated_flag_equals_library_key_pass():

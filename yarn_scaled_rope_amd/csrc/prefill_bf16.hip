@@ -266,18 +266,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         w = *reinterpret_cast<const u32x4 *>(qp + kk * 16);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+          // the logit scale (log2 units) folded into the query before its one
+          // rounding to bf16, so that the scores come out of the matrix cores
+          // ready for exp2
+          float x0 = bf16_to_f32(w[e] & 0xffffu), x1 = bf16_to_f32(w[e] >> 16);
           if (ROTATE_Q) {
-            float x0 = bf16_to_f32(w[e] & 0xffffu), x1 = bf16_to_f32(w[e] >> 16);
             float c, s;
             rope_cos_sin((double)(P + tq), theta[kk * 8 + hh * 4 + e], &c, &s);
             rotate_pair(x0, x1, c, s);
-            w[e] = pack_bf16x2(x0, x1);  // the rotated query in bf16, as a caller would pass it
           }
-          // the logit scale (log2 units) folded into the query, so that the
-          // scores come out of the matrix cores ready for exp2
-          const float y0 = bf16_to_f32(w[e] & 0xffffu) * scale_log2;
-          const float y1 = bf16_to_f32(w[e] >> 16) * scale_log2;
-          w[e] = pack_bf16x2(y0, y1);
+          w[e] = pack_bf16x2(x0 * scale_log2, x1 * scale_log2);
         }
       }
       qf[kk] = as_bf16x8(w);
