@@ -9,6 +9,8 @@
 // as one contiguous segment.  Positions come either from an explicit
 // array (rope_apply) or from the row's offset inside its sequence of a packed
 // batch (the key pass of prefill, which also writes out of place).
+#include <type_traits>
+
 #include "device_common.h"
 #include "yr_internal.h"
 
@@ -88,16 +90,18 @@ __global__ __launch_bounds__(256) void rope_kernel(const T *src, T *dst,  // may
 
 // The same rotation with 16-byte accesses (buffers 16-byte aligned): a lane
 // owns PPL consecutive pairs of one token (4 in bf16, 2 in fp32), so a wave
-// moves 1 KB per access, and the heads are taken 8 at a time, all 8 loaded
-// before any is stored, so that in-place rotation keeps 8 loads in flight.
-template <typename T, bool FROM_CU>
+// moves 1 KB per access, and the heads are taken up to 32 at a time, all
+// loaded before any is stored, so that in-place rotation keeps that many
+// loads in flight.  HB (heads per batch) is 32 for 32 heads or more (6.1
+// against 5.6 TB/s at 32 heads), else 8: the 32-head batch's registers halve
+// the waves a SIMD holds, which costs more than it gives below 32 heads.
+template <typename T, bool FROM_CU, int HB>
 __global__ __launch_bounds__(256) void rope_vec_kernel(const T *src, T *dst,  // may alias
                                                       long long ntok, int H, int D,
                                                       const int *__restrict__ pos_or_cu, int B,
                                                       int max_seqlen,
                                                       const double *__restrict__ theta, int *flag) {
   constexpr int PPL = 16 / (2 * (int)sizeof(T));  // pairs per lane
-  constexpr int HB = 8;                           // heads per batch
   if (FROM_CU && flag != nullptr && blockIdx.x == 0)
     validate_cu_seqlens(pos_or_cu, B, ntok, max_seqlen, flag);
   const int lpr = (D >> 1) / PPL;  // lanes per (token, head) row
@@ -140,18 +144,24 @@ __global__ __launch_bounds__(256) void rope_vec_kernel(const T *src, T *dst,  //
       }
       return make_uint4(w[0], w[1], w[2], w[3]);
     };
+    // heads in batches of HB, then 8, 4, 2, 1: all loads of a batch before
+    // its stores
     int h0 = 0;
-    for (; h0 + HB <= H; h0 += HB) {
-      uint4 v[HB];
+    auto batch = [&](auto nc) {
+      constexpr int N = decltype(nc)::value;
+      for (; h0 + N <= H; h0 += N) {
+        uint4 v[N];
 #pragma unroll
-      for (int u = 0; u < HB; ++u) v[u] = *reinterpret_cast<const uint4 *>(src + row + (long long)(h0 + u) * D);
+        for (int u = 0; u < N; ++u) v[u] = *reinterpret_cast<const uint4 *>(src + row + (long long)(h0 + u) * D);
 #pragma unroll
-      for (int u = 0; u < HB; ++u) *reinterpret_cast<uint4 *>(dst + row + (long long)(h0 + u) * D) = rot(v[u]);
-    }
-    for (; h0 < H; ++h0) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(src + row + (long long)h0 * D);
-      *reinterpret_cast<uint4 *>(dst + row + (long long)h0 * D) = rot(v);
-    }
+        for (int u = 0; u < N; ++u) *reinterpret_cast<uint4 *>(dst + row + (long long)(h0 + u) * D) = rot(v[u]);
+      }
+    };
+    batch(std::integral_constant<int, HB>{});
+    batch(std::integral_constant<int, 8>{});
+    batch(std::integral_constant<int, 4>{});
+    batch(std::integral_constant<int, 2>{});
+    batch(std::integral_constant<int, 1>{});
   }
 }
 
@@ -164,8 +174,12 @@ void launch_rope_t(const RopeArgs &a, const int *pc, hipStream_t s) {
   if (blocks < 1) blocks = 1;
   if (blocks > 65536) blocks = 65536;  // grid-stride beyond this
   const dim3 grid((unsigned)blocks), block(256);
-  if (vec)
-    hipLaunchKernelGGL((rope_vec_kernel<T, FROM_CU>), grid, block, 0, s, (const T *)a.src,
+  if (vec && a.H >= 32)
+    hipLaunchKernelGGL((rope_vec_kernel<T, FROM_CU, 32>), grid, block, 0, s, (const T *)a.src,
+                       (T *)a.dst, a.T, a.H, a.head_dim, pc, a.B, a.max_seqlen, a.theta,
+                       a.dev_flag);
+  else if (vec)
+    hipLaunchKernelGGL((rope_vec_kernel<T, FROM_CU, 8>), grid, block, 0, s, (const T *)a.src,
                        (T *)a.dst, a.T, a.H, a.head_dim, pc, a.B, a.max_seqlen, a.theta,
                        a.dev_flag);
   else
