@@ -339,7 +339,7 @@ int decode_impl(const char *fn, const void *q, const void *k_cache, const void *
   int vis_split = 0;
   if (window > 0 && cache_dtype != YR_F32) {
     const int span = (int)std::min<long long>(max_cache_len, (long long)window + sinks);
-    const int cw = decode_chunk(B, span, units, min_chunk);
+    const int cw = decode_chunk(B, span, units, min_chunk, 1024);
     const int nw = decode_nsplit(span, cw);
     if (nw < nsplit) {
       chunk = cw;

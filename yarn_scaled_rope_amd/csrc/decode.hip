@@ -1210,12 +1210,12 @@ int decode_stream_wgs() {
   return n;
 }
 
-int decode_chunk(int B, int max_cache_len, int units, int min_chunk) {
-  // Enough workgroups to fill 256 CUs several times over; chunks are powers
-  // of two, at most 2048 keys so that a workgroup's start-up and combine stay
-  // small next to its sweep, and at least min_chunk.
+int decode_chunk(int B, int max_cache_len, int units, int min_chunk, int target) {
+  // At least `target` workgroups (several per CU); chunks are powers of two,
+  // at most 2048 keys so that a workgroup's start-up and combine stay small
+  // next to its sweep, and at least min_chunk.
   int chunk = 2048;
-  while (chunk > min_chunk && (long long)B * units * decode_nsplit(max_cache_len, chunk) < 2048)
+  while (chunk > min_chunk && (long long)B * units * decode_nsplit(max_cache_len, chunk) < target)
     chunk >>= 1;
   return chunk;
 }
