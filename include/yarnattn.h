@@ -229,7 +229,8 @@ size_t attn_decode_workspace_bytes(int B, int max_cache_len, int Hq, int head_di
  * (or at seqlens[b] when q_pos is NULL) and attends, unmasked, to cache rows
  * 0 .. seqlens[b]-1, whose keys are taken as already rotated.  The cache is
  * swept in parallel pieces -- fixed-size key chunks, or for caches of 512K
- * keys or more in all, equal ranges of 32-key blocks, one per compute unit;
+ * keys or more in all (at most 128 sequences), equal ranges of 32-key
+ * blocks, one per compute unit;
  * each piece yields a partial (out, LSE) and the partials are merged by
  * log-sum-exp ("Long-context models", "Context parallelism distributes exact
  * attention").

@@ -117,10 +117,14 @@ int decode_heads_per_wg(int Hkv, int head_dim, bool fp8);
 // workgroup) when the caches hold at least kDecodeStreamMinKeys keys in all:
 // the key blocks are cut evenly over one workgroup per CU (at most
 // kDecodeStreamMaxWg).
+// Every workgroup and every merge workgroup walks the B sequence lengths to
+// find its pieces, so the split is kept to batches of at most
+// kDecodeStreamMaxB sequences.
 constexpr long long kDecodeStreamMinKeys = 512 * 1024;
 constexpr int kDecodeStreamMaxWg = 1024;
+constexpr int kDecodeStreamMaxB = 128;
 inline bool decode_stream_eligible(int B, int max_cache_len) {
-  return (long long)B * max_cache_len >= kDecodeStreamMinKeys;
+  return B <= kDecodeStreamMaxB && (long long)B * max_cache_len >= kDecodeStreamMinKeys;
 }
 // With a window the visible rows decide (window + sinks per sequence at most):
 // a short window leaves too few blocks per CU for one workgroup per CU to
