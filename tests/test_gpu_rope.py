@@ -17,6 +17,10 @@ pytestmark = pytest.mark.gpu
     ("f32", 333, 2, 128, 500000.0, 8.0, 16384),
     ("bf16", 777, 8, 128, 500000.0, 8.0, 16384),
     ("bf16", 65, 5, 64, 10000.0, 4.0, 4096),
+    # 32 heads or more go in batches of 32, the rest in 8, 4, 2, 1
+    ("bf16", 257, 32, 128, 500000.0, 8.0, 16384),
+    ("bf16", 100, 47, 64, 10000.0, 4.0, 4096),
+    ("f32", 50, 33, 128, 500000.0, 8.0, 16384),
 ])
 def test_rope_apply_matches_oracle(dtype, T, H, D, base, s, L):
     rng = np.random.Generator(np.random.PCG64(100 + T))
