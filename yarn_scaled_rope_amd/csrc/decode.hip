@@ -1057,6 +1057,22 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     row0 = ((long long)b * Hq + h) * nsplit;
   }
 
+  // The wave's first U partials are loaded before the reference below is
+  // known, so that both loads are in flight together.
+  float w0[U], x0[U][PER];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int pu = wave + u * MW;
+    w0[u] = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) x0[u][i] = 0.f;
+    if (pu < nv) {
+      const long long rw = row0 + pu * stride;
+      w0[u] = part_lse[rw];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) x0[u][i] = part_o[rw * D + lane + 64 * i];
+    }
+  }
   // common reference: the largest partial log2-sum-exp (every wave computes it)
   float M = -INFINITY;
   for (int p = lane; p < nv; p += 64) M = fmaxf(M, part_lse[row0 + p * stride]);
@@ -1069,7 +1085,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   float num[PER], den = 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) num[i] = 0.f;
-  int p = wave;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    // partials past nv (w0 = -inf) and empty ones weigh 0
+    const float e = w0[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(w0[u] - M);
+    den += e;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) num[i] = fmaf(e, x0[u][i], num[i]);
+  }
+  int p = wave + U * MW;
   for (; p + (U - 1) * MW < nv; p += U * MW) {
     float w[U], x[U][PER];
 #pragma unroll
