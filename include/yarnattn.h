@@ -100,6 +100,26 @@ int yarn_rope_freqs(int head_dim, double base, double factor,
                     double *attn_factor);
 
 /*
+ * yarn_rope_dynamic_ntk_freqs -- host-only: the Dynamic NTK table for a
+ * sequence of seq_len tokens ("Arch 03 -- Long Context", NTK-aware slide:
+ * at inference the factor is set to the current sequence length over the
+ * training length).  s = max(1, seq_len / original_max_position) (real
+ * division), then the YR_ROPE_NTK table for that s (plain RoPE over the base
+ * base * s^(d/(d-2))).  At or below the training length s = 1 and the table
+ * is the plain one bit for bit.  The logit temperature stays 1 (only YaRN
+ * rescales logits).  A caller re-derives the table when the sequence grows.
+ *
+ *   head_dim               even, 2..1024;  base > 1
+ *   seq_len                >= 0, the current sequence length
+ *   original_max_position  L_train >= 1
+ *   inv_freq_f32, inv_freq_f64   host tables of head_dim/2 entries or NULL
+ *   factor                 host double or NULL: receives s
+ */
+int yarn_rope_dynamic_ntk_freqs(int head_dim, double base, long long seq_len,
+                                long long original_max_position, float *inv_freq_f32,
+                                double *inv_freq_f64, double *factor);
+
+/*
  * rope_apply -- rotate x in place: pair (2i, 2i+1) of row t turns by
  * positions[t] * theta_i with R = [[cos, -sin], [sin, cos]] ("Arch 03 --
  * Long Context", RoPE slide; "Long-context models", "Position enters

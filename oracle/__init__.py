@@ -24,12 +24,16 @@ Sources (web pages about long-context attention, cited by title and section):
     "Context parallelism distributes exact attention".
 
 Parity status: every function here is pinned by the CPU tests in ``tests/``
-(closed forms, invariants, brute force on tiny inputs, printed values) except
-the end-to-end YaRN value itself: the pages print no worked YaRN frequency or
-attention value, so the YaRN path is pinned only through its reductions
-(s = 1 gives plain RoPE, the pure regions give exactly theta and theta/s, the
-region boundaries agree with their closed form) -- "parity unpinned beyond
-these invariants" for the ramp interior.
+(closed forms, invariants, brute force on tiny inputs, printed values).  The
+pages print no worked YaRN frequency or attention value, so the YaRN table is
+pinned by what the mathematics fixes: s = 1 gives plain RoPE, the pure
+regions give exactly theta and theta/s, the region boundaries agree with their
+closed form, and the ramp interior is pinned at constructed original lengths
+that put a pair at a known turn count (half way from alpha to beta: the mean
+of theta/s and theta; a quarter and three quarters of the way: the values
+that fixes) and by its linearity in the original length.  Dynamic NTK is
+pinned by its rule (no scaling below the training length) and by the NTK-aware
+slide's worked base at eight times the training length.
 """
 
 from . import freqs, rope, attention, bruteforce  # noqa: F401

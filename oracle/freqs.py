@@ -98,6 +98,19 @@ def ntk_theta(head_dim: int, base: float, factor: float) -> np.ndarray:
     return rope_theta(head_dim, ntk_base(head_dim, base, factor))
 
 
+def dynamic_ntk_factor(seq_len: int, original_max_position: float) -> float:
+    """Dynamic NTK: the factor follows the current sequence, s = length /
+    training length, and no scaling applies below the training length
+    (s = max(1, length / L)) ("Arch 03 -- Long Context", NTK-aware slide)."""
+    return max(1.0, float(seq_len) / float(original_max_position))
+
+
+def dynamic_ntk_theta(head_dim: int, base: float, seq_len: int,
+                      original_max_position: float) -> np.ndarray:
+    """NTK-aware frequencies for the factor Dynamic NTK picks at seq_len."""
+    return ntk_theta(head_dim, base, dynamic_ntk_factor(seq_len, original_max_position))
+
+
 def attention_temperature(factor: float) -> float:
     """YaRN logit temperature t = 0.1 * ln(s) + 1 (natural log)
     ("Arch 03 -- Long Context", YaRN slide; "LLM context window mechanics",

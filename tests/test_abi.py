@@ -267,3 +267,39 @@ def test_binding_constants_match_header():
     for name in ("YR_OK", "YR_F32", "YR_BF16", "YR_PREFILL_K_ROTATED", "YR_DEVERR_CU_SEQLENS",
                  "YR_DEVERR_SEQLENS", "YR_DEVERR_QPOS", "YR_DEVERR_CTX_LENS"):
         assert name in macros and hasattr(ops, name), name
+
+
+@pytest.mark.parametrize("n,L,d,base", [(0, 4096, 128, 10000.0), (4096, 4096, 128, 10000.0),
+                                        (32768, 4096, 128, 10000.0), (6000, 4096, 64, 500000.0),
+                                        (131072, 16384, 128, 500000.0)])
+def test_dynamic_ntk_bit_exact_vs_oracle(lib, n, L, d, base):
+    f32, f64, s = ops.yarn_rope_dynamic_ntk_freqs(d, base, n, L)
+    assert s == ofreqs.dynamic_ntk_factor(n, L)
+    ref = ofreqs.dynamic_ntk_theta(d, base, n, L)
+    assert np.array_equal(f32, ofreqs.to_fp32(ref))
+    assert np.max(np.abs(f64 - ref) / np.spacing(ref)) <= 4
+    if n <= L:
+        assert np.array_equal(f64, ofreqs.rope_theta(d, base))
+
+
+def test_dynamic_ntk_rejects(lib):
+    for args in ((128, 10000.0, -1, 4096), (128, 10000.0, 10, 0), (127, 10000.0, 10, 4096)):
+        with pytest.raises(ops.YarnAttnError):
+            ops.yarn_rope_dynamic_ntk_freqs(*args)
+
+
+@pytest.mark.parametrize("s", [2.0, 4.0, 8.0])
+def test_library_yarn_ramp_midpoint(lib, s):
+    """The library's table at a constructed point of the ramp: d = 4 and
+    base = (L / (16.5 * 2 pi))^2 put pair 1 at r = L theta_1 / 2 pi = 16.5 turns
+    over L = 16384, half way from alpha = 1 to beta = 32, so theta'_1 is the
+    mean of theta_1 / s and theta_1 ("Arch 03 -- Long Context", YaRN slide)."""
+    import math
+    L = 16384
+    base = (L / (16.5 * 2.0 * math.pi)) ** 2
+    f32, f64, t = ops.yarn_rope_freqs(4, base, s, L)
+    th1 = 16.5 * 2.0 * math.pi / L
+    want = (th1 + th1 / s) / 2.0
+    assert abs(f64[1] - want) <= 4 * np.spacing(want)
+    assert f64[0] == 1.0     # pair 0 turns L / 2 pi > beta times: unscaled
+    assert t == pytest.approx(0.1 * math.log(s) + 1.0, rel=1e-15)

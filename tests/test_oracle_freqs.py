@@ -154,3 +154,100 @@ def test_ntk_worked_example():
 def test_fp32_table_far_from_rounding_midpoints(d, base, s, L, method):
     th = freqs.theta_for(method, d, base, s, L)
     assert np.min(freqs.fp32_midpoint_distance(th)) > 2.0 ** -40
+
+
+# ---- the interior of the YaRN ramp ------------------------------------------
+# The pages print no worked YaRN frequency, so the ramp interior is pinned by
+# constructions whose answer the mathematics fixes: an original length L that
+# puts a pair's turn count r = L / lambda at a known point of [alpha, beta]
+# ("Arch 03 -- Long Context", YaRN slide: linear ramp between the PI-scaled
+# and the unscaled frequency; steps table: alpha = 1, beta = 32).
+
+def _ulps(a, b):
+    return abs(a - b) / np.spacing(abs(b))
+
+
+@pytest.mark.parametrize("s", [2.0, 4.0, 8.0])
+def test_yarn_ramp_midpoint_is_the_mean_of_pi_and_unscaled(s):
+    """r = (alpha + beta) / 2 = 16.5 turns: gamma = 1/2, so theta' is the
+    arithmetic mean of theta / s and theta.  Base 16, d 8 gives theta =
+    1, 1/2, 1/4, 1/8 exactly; L = 16.5 * 2 pi / theta_i puts pair i there."""
+    th = [1.0, 0.5, 0.25, 0.125]
+    for i, t in enumerate(th):
+        L = 16.5 * 2.0 * math.pi / t
+        got = freqs.yarn_theta(8, 16.0, s, L)[i]
+        want = (t + t / s) / 2.0
+        assert _ulps(got, want) <= 2, (i, got, want)
+    # s = 4, pair 0: (1 + 1/4) / 2 = 0.625 written out
+    assert _ulps(freqs.yarn_theta(8, 16.0, 4.0, 33.0 * math.pi)[0], 0.625) <= 2
+
+
+def test_yarn_ramp_quarter_and_three_quarter_points():
+    """r = alpha + (beta - alpha)/4 = 8.75 gives gamma = 1/4: theta' =
+    theta/s + (theta - theta/s)/4, i.e. 0.4375 for theta = 1, s = 4;
+    r = alpha + 3 (beta - alpha)/4 = 24.25 gives gamma = 3/4: 0.8125."""
+    assert _ulps(freqs.yarn_theta(8, 16.0, 4.0, 8.75 * 2.0 * math.pi)[0], 0.4375) <= 2
+    assert _ulps(freqs.yarn_theta(8, 16.0, 4.0, 24.25 * 2.0 * math.pi)[0], 0.8125) <= 2
+    # pair 2 (theta = 1/4) at the quarter point, s = 8: 1/32 + (1/4 - 1/32)/4
+    got = freqs.yarn_theta(8, 16.0, 8.0, 8.75 * 2.0 * math.pi / 0.25)[2]
+    assert _ulps(got, 0.0859375) <= 2
+
+
+def test_yarn_ramp_is_linear_in_the_original_length():
+    """Inside the ramp r is proportional to L, so theta'(L) is an affine
+    function of L: the value at the midpoint of two lengths is the mean of the
+    two values, and equal steps in L give equal steps in theta'.  A blend that
+    is linear in log(theta) (geometric between theta/s and theta) fails this."""
+    d, base, s = 128, 10000.0, 4.0
+    lam = 2.0 * math.pi / freqs.rope_theta(d, base)
+    i = 30
+    # lengths that keep pair i strictly inside (alpha, beta)
+    lo, hi = 2.0 * lam[i], 30.0 * lam[i]
+    Ls = np.linspace(lo, hi, 9)
+    vals = np.array([freqs.yarn_theta(d, base, s, L)[i] for L in Ls])
+    steps = np.diff(vals)
+    assert np.all(steps > 0)
+    assert np.allclose(steps, steps[0], rtol=1e-9, atol=0)
+    mid = freqs.yarn_theta(d, base, s, (lo + hi) / 2.0)[i]
+    assert mid == pytest.approx((vals[0] + vals[-1]) / 2.0, rel=1e-14)
+    # and the line runs from theta/s at r = alpha to theta at r = beta
+    th = freqs.rope_theta(d, base)[i]
+    slope = steps[0] / (Ls[1] - Ls[0])
+    assert vals[0] + slope * (1.0 * lam[i] - lo) == pytest.approx(th / s, rel=1e-12)
+    assert vals[0] + slope * (32.0 * lam[i] - lo) == pytest.approx(th, rel=1e-12)
+
+
+# ---- Dynamic NTK --------------------------------------------------------------
+def test_dynamic_ntk_factor_rule():
+    # "s equal to the current sequence length / L_train"; no scaling below it
+    assert freqs.dynamic_ntk_factor(0, 4096) == 1.0
+    assert freqs.dynamic_ntk_factor(4096, 4096) == 1.0
+    assert freqs.dynamic_ntk_factor(2000, 4096) == 1.0
+    assert freqs.dynamic_ntk_factor(8192, 4096) == 2.0
+    assert freqs.dynamic_ntk_factor(32768, 4096) == 8.0
+    assert freqs.dynamic_ntk_factor(6144, 4096) == 1.5
+
+
+def test_dynamic_ntk_below_training_length_is_plain_rope():
+    for n in (1, 100, 4096):
+        assert np.array_equal(freqs.dynamic_ntk_theta(128, 10000.0, n, 4096),
+                              freqs.rope_theta(128, 10000.0))
+
+
+def test_dynamic_ntk_at_eight_times_the_training_length_is_the_printed_base():
+    # the NTK-aware slide's worked case: s = 8, d = 128, base 10000 -> ~82,000
+    th = freqs.dynamic_ntk_theta(128, 10000.0, 8 * 4096, 4096)
+    b = freqs.ntk_base(128, 10000.0, 8.0)
+    assert abs(b - 82000.0) / 82000.0 < 0.01
+    # theta_i = b^(-2i/d): i = 32 gives b^(-1/2)
+    assert th[32] == pytest.approx(b ** -0.5, rel=1e-14)
+    assert th[0] == 1.0
+
+
+def test_dynamic_ntk_frequencies_fall_as_the_sequence_grows():
+    prev = freqs.dynamic_ntk_theta(64, 10000.0, 1024, 1024)
+    for n in (1500, 2048, 5000, 65536):
+        cur = freqs.dynamic_ntk_theta(64, 10000.0, n, 1024)
+        assert cur[0] == 1.0
+        assert np.all(cur[1:] < prev[1:])
+        prev = cur

@@ -76,3 +76,25 @@ extern "C" int yarn_rope_freqs(int head_dim, double base, double factor,
     *attn_factor = (method == YR_ROPE_YARN) ? 0.1 * std::log(factor) + 1.0 : 1.0;
   return YR_OK;
 }
+
+// Dynamic NTK ("Arch 03 -- Long Context", NTK-aware slide): at inference time
+// the factor follows the sequence, s = current length / training length, and
+// the NTK-aware table is built for that s.  Below the training length no
+// scaling applies (s = 1, the plain table bit for bit).
+extern "C" int yarn_rope_dynamic_ntk_freqs(int head_dim, double base, long long seq_len,
+                                           long long original_max_position,
+                                           float *inv_freq_f32, double *inv_freq_f64,
+                                           double *factor) {
+  if (seq_len < 0)
+    return yr::fail(YR_ERR_INVALID, "yarn_rope_dynamic_ntk_freqs: seq_len must be >= 0");
+  if (original_max_position < 1)
+    return yr::fail(YR_ERR_INVALID,
+                    "yarn_rope_dynamic_ntk_freqs: original_max_position must be >= 1");
+  const double r = (double)seq_len / (double)original_max_position;
+  const double s = r > 1.0 ? r : 1.0;
+  const int st = yarn_rope_freqs(head_dim, base, s, original_max_position, 1.0, 32.0,
+                                 YR_ROPE_NTK, inv_freq_f32, inv_freq_f64, nullptr);
+  if (st != YR_OK) return st;
+  if (factor) *factor = s;
+  return YR_OK;
+}

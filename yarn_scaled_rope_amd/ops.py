@@ -56,6 +56,7 @@ def _declare(lib):
                            ctypes.c_float, ctypes.c_size_t)
     sig = {
         "yarn_rope_freqs": (i, [i, d, d, ll, d, d, i, vp, vp, vp]),
+        "yarn_rope_dynamic_ntk_freqs": (i, [i, d, ll, ll, vp, vp, vp]),
         "rope_apply": (i, [vp, i, ll, i, i, vp, vp, vp]),
         "rope_apply_packed": (i, [vp, vp, i, vp, i, i, ll, i, i, vp, vp, vp]),
         "attn_prefill_workspace_bytes": (sz, [ll, i, i, i]),
@@ -144,6 +145,21 @@ def yarn_rope_freqs(head_dim: int, base: float, factor: float = 1.0,
                                METHODS[method], f32.ctypes.data_as(ctypes.c_void_p),
                                f64.ctypes.data_as(ctypes.c_void_p), ctypes.byref(t)))
     return f32, f64, t.value
+
+
+def yarn_rope_dynamic_ntk_freqs(head_dim: int, base: float, seq_len: int,
+                                original_max_position: int):
+    """Host call: Dynamic NTK table for a sequence of seq_len tokens.  Returns
+    (fp32 table, fp64 table, factor s)."""
+    lib = load_library()
+    f32 = np.zeros(head_dim // 2, dtype=np.float32)
+    f64 = np.zeros(head_dim // 2, dtype=np.float64)
+    s = ctypes.c_double(0.0)
+    _check(lib.yarn_rope_dynamic_ntk_freqs(int(head_dim), float(base), int(seq_len),
+                                           int(original_max_position),
+                                           f32.ctypes.data_as(ctypes.c_void_p),
+                                           f64.ctypes.data_as(ctypes.c_void_p), ctypes.byref(s)))
+    return f32, f64, s.value
 
 
 # ------------------------------------------------------------------ rope
