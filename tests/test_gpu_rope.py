@@ -21,6 +21,17 @@ pytestmark = pytest.mark.gpu
     ("bf16", 257, 32, 128, 500000.0, 8.0, 16384),
     ("bf16", 100, 47, 64, 10000.0, 4.0, 4096),
     ("f32", 50, 33, 128, 500000.0, 8.0, 16384),
+    # head dims whose rows are not whole 16-byte chunks take the pair-per-
+    # thread kernel even in aligned buffers (every pair rotated)
+    ("bf16", 70, 3, 2, 10000.0, 4.0, 64),
+    ("bf16", 70, 3, 6, 10000.0, 4.0, 64),
+    ("bf16", 70, 5, 12, 500000.0, 8.0, 16384),
+    ("bf16", 40, 33, 4, 10000.0, 4.0, 64),
+    ("f32", 70, 3, 6, 10000.0, 4.0, 64),
+    ("f32", 40, 2, 2, 500000.0, 8.0, 16384),
+    # rows of whole chunks at odd sizes keep the 16-byte kernel
+    ("bf16", 70, 3, 24, 10000.0, 4.0, 64),
+    ("f32", 70, 3, 12, 10000.0, 4.0, 64),
 ])
 def test_rope_apply_matches_oracle(dtype, T, H, D, base, s, L):
     rng = np.random.Generator(np.random.PCG64(100 + T))

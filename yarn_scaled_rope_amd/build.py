@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libyarnattn.so")
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
-          "-Wall", "-Wno-unused-function"]
+          "-Wall", "-Wno-unused-function", "-fvisibility=hidden"]
 # device code: no packed-fp32 instructions (hipcc's host pass warns that it
 # does not know the feature; that warning is harmless)
 DEVICE_ONLY = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

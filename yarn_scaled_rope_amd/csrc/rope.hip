@@ -167,7 +167,12 @@ __global__ __launch_bounds__(256) void rope_vec_kernel(const T *src, T *dst,  //
 
 template <typename T, bool FROM_CU>
 void launch_rope_t(const RopeArgs &a, const int *pc, hipStream_t s) {
-  const bool vec = ((reinterpret_cast<uintptr_t>(a.src) | reinterpret_cast<uintptr_t>(a.dst)) & 15) == 0;
+  // 16-byte accesses need 16-byte aligned buffers and rows that are a whole
+  // number of 16-byte chunks (every lane then owns PPL pairs of one row and
+  // every row starts aligned); other head dims take the pair-per-thread form
+  const bool vec =
+      ((reinterpret_cast<uintptr_t>(a.src) | reinterpret_cast<uintptr_t>(a.dst)) & 15) == 0 &&
+      ((size_t)a.head_dim * sizeof(T)) % 16 == 0;
   const int per = vec ? (a.head_dim / 2) / (16 / (2 * (int)sizeof(T))) : a.head_dim / 2;
   const long long total = a.T * (long long)per;
   long long blocks = (total + 255) / 256;

@@ -34,6 +34,7 @@ YR_ROPE_YARN = 3
 METHODS = {"plain": YR_ROPE_PLAIN, "pi": YR_ROPE_PI, "ntk": YR_ROPE_NTK, "yarn": YR_ROPE_YARN}
 
 YR_PREFILL_K_ROTATED = 1
+YR_PREFILL_PERMUTED_ORDER = 2
 
 YR_DEVERR_CU_SEQLENS = 1
 YR_DEVERR_SEQLENS = 2
@@ -122,13 +123,42 @@ def _torch_dtype(code: int):
     return torch.float32 if code == YR_F32 else torch.bfloat16
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, device=True):
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None, numel=None):
+    """Host-side checks of one tensor argument (no device access): contiguous,
+    of the given dtype, shape and / or element count."""
+    if not isinstance(t, torch.Tensor):
+        raise YarnAttnError(YR_ERR_INVALID, f"{name} must be a tensor")
     if not t.is_contiguous():
         raise YarnAttnError(YR_ERR_INVALID, f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
-        raise YarnAttnError(YR_ERR_INVALID, f"{name} must be {dtype}")
-    if device and not t.is_cuda:
-        raise YarnAttnError(YR_ERR_INVALID, f"{name} must be a device tensor")
+        raise YarnAttnError(YR_ERR_INVALID, f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise YarnAttnError(YR_ERR_INVALID, f"{name} must have shape {tuple(shape)}, "
+                                            f"got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise YarnAttnError(YR_ERR_INVALID, f"{name} must have {numel} elements, got {t.numel()}")
+
+
+def _ndim(t: torch.Tensor, name: str, n: int):
+    if not isinstance(t, torch.Tensor) or t.dim() != n:
+        raise YarnAttnError(YR_ERR_INVALID, f"{name} must be a {n}-d tensor")
+
+
+def _on_device(**tensors):
+    """Every given tensor lives in device memory (checked after the shapes, so
+    that argument errors are reported the same with or without a GPU)."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise YarnAttnError(YR_ERR_INVALID, f"{name} must be a device tensor")
+
+
+def _table(inv_freq_f64, D: int):
+    if inv_freq_f64 is not None:
+        _need(inv_freq_f64, "inv_freq_f64", torch.float64, numel=D // 2)
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
 
 
 # ------------------------------------------------------------------ freqs
@@ -165,10 +195,15 @@ def yarn_rope_dynamic_ntk_freqs(head_dim: int, base: float, seq_len: int,
 # ------------------------------------------------------------------ rope
 def rope_apply(x: torch.Tensor, positions: torch.Tensor, inv_freq_f64: torch.Tensor, stream=None):
     """Rotate x [T, H, D] in place at positions[T] (int32)."""
+    _ndim(x, "x", 3)
     _need(x, "x")
-    _need(positions, "positions", torch.int32)
-    _need(inv_freq_f64, "inv_freq_f64", torch.float64)
     T, H, D = x.shape
+    _need(positions, "positions", torch.int32, numel=T)
+    if inv_freq_f64 is None:
+        raise YarnAttnError(YR_ERR_NULL, "inv_freq_f64 is required")
+    _table(inv_freq_f64, D)
+    _dtype_code(x)
+    _on_device(x=x, positions=positions, inv_freq_f64=inv_freq_f64)
     lib = load_library()
     _check(lib.rope_apply(_ptr(x), _dtype_code(x), T, H, D, _ptr(positions), _ptr(inv_freq_f64),
                           _stream(stream)))
@@ -180,17 +215,27 @@ def rope_apply_packed(src: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: i
                       dev_error: Optional[torch.Tensor] = None, stream=None):
     """Rotate the rows of a packed batch [T, H, D] at their in-sequence
     positions into dst (a new tensor by default; may be src)."""
+    _ndim(src, "src", 3)
     _need(src, "src")
+    T, H, D = src.shape
+    _dtype_code(src)
+    _ndim(cu_seqlens, "cu_seqlens", 1)
     _need(cu_seqlens, "cu_seqlens", torch.int32)
-    _need(inv_freq_f64, "inv_freq_f64", torch.float64)
-    if dst is None:
-        dst = torch.empty_like(src)
-    _need(dst, "dst", src.dtype)
-    if dst.shape != src.shape:
-        raise YarnAttnError(YR_ERR_INVALID, "dst must match src")
+    if cu_seqlens.numel() < 2:
+        raise YarnAttnError(YR_ERR_INVALID, "cu_seqlens needs B+1 >= 2 entries")
+    if inv_freq_f64 is None:
+        raise YarnAttnError(YR_ERR_NULL, "inv_freq_f64 is required")
+    _table(inv_freq_f64, D)
+    if dst is not None:
+        _need(dst, "dst", src.dtype, shape=src.shape)
     if dev_error is not None:
         _need(dev_error, "dev_error", torch.int32)
-    T, H, D = src.shape
+        if dev_error.numel() < 1:
+            raise YarnAttnError(YR_ERR_INVALID, "dev_error needs one element")
+    _on_device(src=src, cu_seqlens=cu_seqlens, inv_freq_f64=inv_freq_f64, dst=dst,
+               dev_error=dev_error)
+    if dst is None:
+        dst = torch.empty_like(src)
     lib = load_library()
     _check(lib.rope_apply_packed(_ptr(src), _ptr(dst), _dtype_code(src), _ptr(cu_seqlens),
                                  cu_seqlens.numel() - 1, int(max_seqlen), T, H, D,
@@ -205,29 +250,42 @@ def attn_prefill_workspace_bytes(T: int, hkv: int, head_dim: int, in_dtype: int)
 
 def attn_prefill_fwd(q, k, v, cu_seqlens, max_seqlen: int, inv_freq_f64, softmax_scale: float,
                      out=None, out_dtype=None, lse=None, workspace=None, want_lse=True,
-                     k_rotated=False, window: int = 0, sinks: int = 0, stream=None):
+                     k_rotated=False, window: int = 0, sinks: int = 0, stream=None,
+                     permuted_order=False):
     """Causal prefill.  q [T, Hq, D], k/v [T, Hkv, D] unrotated (or rotated,
     with inv_freq_f64=None; or only k rotated, with k_rotated=True);
     cu_seqlens int32 [B+1]; optional sliding window / sinks.  Returns
     (out, lse)."""
+    _ndim(q, "q", 3)
+    _ndim(k, "k", 3)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n)
-    _need(cu_seqlens, "cu_seqlens", torch.int32)
-    if inv_freq_f64 is not None:
-        _need(inv_freq_f64, "inv_freq_f64", torch.float64)
     T, hq, D = q.shape
     hkv = k.shape[1]
     if k.shape != (T, hkv, D) or v.shape != (T, hkv, D) or k.dtype != q.dtype or v.dtype != q.dtype:
         raise YarnAttnError(YR_ERR_INVALID, "k and v must be [T, Hkv, D] of q's dtype")
     in_code = _dtype_code(q)
+    _ndim(cu_seqlens, "cu_seqlens", 1)
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens.numel() < 2:
+        raise YarnAttnError(YR_ERR_INVALID, "cu_seqlens needs B+1 >= 2 entries")
+    _table(inv_freq_f64, D)
     out_code = (YR_F32 if in_code == YR_F32 else YR_BF16) if out_dtype is None else out_dtype
+    if out_code not in (YR_F32, YR_BF16):
+        raise YarnAttnError(YR_ERR_UNSUPPORTED, f"out_dtype {out_code}")
+    if out is not None:
+        _need(out, "out", _torch_dtype(out_code), shape=(T, hq, D))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, shape=(hq, T))
+    key_pass = inv_freq_f64 is not None and not k_rotated
+    if workspace is not None:
+        _need(workspace, "workspace")
+    _on_device(q=q, k=k, v=v, cu_seqlens=cu_seqlens, inv_freq_f64=inv_freq_f64, out=out, lse=lse,
+               workspace=workspace)
     if out is None:
         out = torch.empty((T, hq, D), dtype=_torch_dtype(out_code), device=q.device)
-    else:
-        _need(out, "out", _torch_dtype(out_code))
     if lse is None and want_lse:
         lse = torch.empty((hq, T), dtype=torch.float32, device=q.device)
-    key_pass = inv_freq_f64 is not None and not k_rotated
     need = attn_prefill_workspace_bytes(T, hkv, D, in_code) if key_pass else 256
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -235,11 +293,10 @@ def attn_prefill_fwd(q, k, v, cu_seqlens, max_seqlen: int, inv_freq_f64, softmax
     lib = load_library()
     _check(lib.attn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), in_code, _ptr(cu_seqlens), B,
                                 int(max_seqlen), T, hq, hkv, D, _ptr(inv_freq_f64),
-                                YR_PREFILL_K_ROTATED if k_rotated else 0,
+                                (YR_PREFILL_K_ROTATED if k_rotated else 0) |
+                                (YR_PREFILL_PERMUTED_ORDER if permuted_order else 0),
                                 float(softmax_scale), int(window), int(sinks), _ptr(out), out_code,
-                                _ptr(lse),
-                                _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                _stream(stream)))
+                                _ptr(lse), _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return out, lse
 
 
@@ -251,25 +308,33 @@ def attn_prefill_chunk(q, k_cache, v_cache, cu_seqlens_q, ctx_lens, max_seqlen_q
     against caches [B, Lmax, Hkv, D] that already hold ctx_lens[b] earlier
     tokens followed by the chunk's rotated keys and values.  Returns
     (out, lse)."""
+    _ndim(q, "q", 3)
+    _ndim(k_cache, "k_cache", 4)
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _need(t, n)
-    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32)
-    _need(ctx_lens, "ctx_lens", torch.int32)
-    if inv_freq_f64 is not None:
-        _need(inv_freq_f64, "inv_freq_f64", torch.float64)
     Tq, hq, D = q.shape
     B, lmax, hkv, _ = k_cache.shape
     if k_cache.shape != (B, lmax, hkv, D) or v_cache.shape != k_cache.shape or \
             k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise YarnAttnError(YR_ERR_INVALID, "caches must be [B, Lmax, Hkv, D] of q's dtype")
-    if cu_seqlens_q.numel() != B + 1 or ctx_lens.numel() != B:
-        raise YarnAttnError(YR_ERR_INVALID, "cu_seqlens_q must have B+1 and ctx_lens B entries")
     in_code = _dtype_code(q)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, numel=B + 1)
+    _need(ctx_lens, "ctx_lens", torch.int32, numel=B)
+    _table(inv_freq_f64, D)
     out_code = (YR_F32 if in_code == YR_F32 else YR_BF16) if out_dtype is None else out_dtype
+    if out_code not in (YR_F32, YR_BF16):
+        raise YarnAttnError(YR_ERR_UNSUPPORTED, f"out_dtype {out_code}")
+    if out is not None:
+        _need(out, "out", _torch_dtype(out_code), shape=(Tq, hq, D))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, shape=(hq, Tq))
+    if workspace is not None:
+        _need(workspace, "workspace")
+    _on_device(q=q, k_cache=k_cache, v_cache=v_cache, cu_seqlens_q=cu_seqlens_q,
+               ctx_lens=ctx_lens, inv_freq_f64=inv_freq_f64, out=out, lse=lse,
+               workspace=workspace)
     if out is None:
         out = torch.empty((Tq, hq, D), dtype=_torch_dtype(out_code), device=q.device)
-    else:
-        _need(out, "out", _torch_dtype(out_code))
     if lse is None and want_lse:
         lse = torch.empty((hq, Tq), dtype=torch.float32, device=q.device)
     if workspace is None:
@@ -279,8 +344,7 @@ def attn_prefill_chunk(q, k_cache, v_cache, cu_seqlens_q, ctx_lens, max_seqlen_q
                                   _ptr(cu_seqlens_q), _ptr(ctx_lens), B, int(max_seqlen_q), Tq,
                                   lmax, hq, hkv, D, _ptr(inv_freq_f64), float(softmax_scale),
                                   int(window), int(sinks), _ptr(out), out_code, _ptr(lse),
-                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                  _stream(stream)))
+                                  _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return out, lse
 
 
@@ -289,25 +353,47 @@ def attn_decode_workspace_bytes(B: int, max_cache_len: int, hq: int, head_dim: i
     return int(load_library().attn_decode_workspace_bytes(B, max_cache_len, hq, head_dim))
 
 
-def attn_decode(q, k_cache, v_cache, seqlens, inv_freq_f64, softmax_scale: float, q_pos=None,
-                out=None, out_dtype=None, lse=None, workspace=None, want_lse=True,
-                window: int = 0, sinks: int = 0, stream=None):
-    """One query per sequence over a contiguous cache.  q [B, Hq, D];
-    caches [B, Lmax, Hkv, D]; seqlens int32 [B]; optional sliding window /
-    sinks.  Returns (out, lse)."""
+def _decode_checks(q, k_cache, v_cache, seqlens, q_pos, inv_freq_f64, out, out_code, lse,
+                   workspace, cache_dtype):
+    """Shapes and dtypes of a decode call (host side, before any launch)."""
+    _ndim(q, "q", 3)
+    _ndim(k_cache, "k_cache", 4)
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _need(t, n)
-    _need(seqlens, "seqlens", torch.int32)
-    if q_pos is not None:
-        _need(q_pos, "q_pos", torch.int32)
-    if inv_freq_f64 is not None:
-        _need(inv_freq_f64, "inv_freq_f64", torch.float64)
     B, hq, D = q.shape
     _, lmax, hkv, _ = k_cache.shape
     if k_cache.shape != (B, lmax, hkv, D) or v_cache.shape != k_cache.shape:
         raise YarnAttnError(YR_ERR_INVALID, "caches must be [B, Lmax, Hkv, D]")
+    if k_cache.dtype != cache_dtype or v_cache.dtype != cache_dtype:
+        raise YarnAttnError(YR_ERR_INVALID, f"caches must be {cache_dtype}")
+    _need(seqlens, "seqlens", torch.int32, numel=B)
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int32, numel=B)
+    _table(inv_freq_f64, D)
+    if out_code not in (YR_F32, YR_BF16):
+        raise YarnAttnError(YR_ERR_UNSUPPORTED, f"out_dtype {out_code}")
+    if out is not None:
+        _need(out, "out", _torch_dtype(out_code), shape=(B, hq, D))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, shape=(B, hq))
+    if workspace is not None:
+        _need(workspace, "workspace")
+    _on_device(q=q, k_cache=k_cache, v_cache=v_cache, seqlens=seqlens, q_pos=q_pos,
+               inv_freq_f64=inv_freq_f64, out=out, lse=lse, workspace=workspace)
+    return B, hq, D, lmax, hkv
+
+
+def attn_decode(q, k_cache, v_cache, seqlens, inv_freq_f64, softmax_scale: float, q_pos=None,
+                out=None, out_dtype=None, lse=None, workspace=None, want_lse=True,
+                window: int = 0, sinks: int = 0, stream=None):
+    """One query per sequence over a contiguous cache.  q [B, Hq, D];
+    caches [B, Lmax, Hkv, D] of q's dtype; seqlens int32 [B]; optional
+    sliding window / sinks.  Returns (out, lse)."""
+    _ndim(q, "q", 3)
     in_code = _dtype_code(q)
     out_code = (YR_F32 if in_code == YR_F32 else YR_BF16) if out_dtype is None else out_dtype
+    B, hq, D, lmax, hkv = _decode_checks(q, k_cache, v_cache, seqlens, q_pos, inv_freq_f64, out,
+                                         out_code, lse, workspace, q.dtype)
     if out is None:
         out = torch.empty((B, hq, D), dtype=_torch_dtype(out_code), device=q.device)
     if lse is None and want_lse:
@@ -319,8 +405,7 @@ def attn_decode(q, k_cache, v_cache, seqlens, inv_freq_f64, softmax_scale: float
     _check(lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), in_code, _ptr(seqlens),
                            _ptr(q_pos), B, lmax, hq, hkv, D, _ptr(inv_freq_f64),
                            float(softmax_scale), int(window), int(sinks), _ptr(out), out_code,
-                           _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                           _stream(stream)))
+                           _ptr(lse), _ptr(workspace), _nbytes(workspace), _stream(stream)))
     return out, lse
 
 
@@ -330,23 +415,15 @@ def attn_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, seqlens, inv_freq_f64
     """attn_decode over an FP8 (E4M3) cache: q bf16 [B, Hq, D]; caches uint8
     [B, Lmax, Hkv, D] of E4M3 codes standing for code * k_scale[h] /
     code * v_scale[h] (float32 [Hkv]).  Returns (out, lse)."""
+    _ndim(q, "q", 3)
     _need(q, "q", torch.bfloat16)
-    _need(k_cache, "k_cache", torch.uint8)
-    _need(v_cache, "v_cache", torch.uint8)
-    _need(k_scale, "k_scale", torch.float32)
-    _need(v_scale, "v_scale", torch.float32)
-    _need(seqlens, "seqlens", torch.int32)
-    if q_pos is not None:
-        _need(q_pos, "q_pos", torch.int32)
-    if inv_freq_f64 is not None:
-        _need(inv_freq_f64, "inv_freq_f64", torch.float64)
-    B, hq, D = q.shape
-    _, lmax, hkv, _ = k_cache.shape
-    if k_cache.shape != (B, lmax, hkv, D) or v_cache.shape != k_cache.shape:
-        raise YarnAttnError(YR_ERR_INVALID, "caches must be [B, Lmax, Hkv, D]")
-    if k_scale.numel() != hkv or v_scale.numel() != hkv:
-        raise YarnAttnError(YR_ERR_INVALID, "k_scale and v_scale need Hkv entries")
+    _ndim(k_cache, "k_cache", 4)
+    _need(k_scale, "k_scale", torch.float32, numel=k_cache.shape[2])
+    _need(v_scale, "v_scale", torch.float32, numel=k_cache.shape[2])
     out_code = YR_BF16 if out_dtype is None else out_dtype
+    B, hq, D, lmax, hkv = _decode_checks(q, k_cache, v_cache, seqlens, q_pos, inv_freq_f64, out,
+                                         out_code, lse, workspace, torch.uint8)
+    _on_device(k_scale=k_scale, v_scale=v_scale)
     if out is None:
         out = torch.empty((B, hq, D), dtype=_torch_dtype(out_code), device=q.device)
     if lse is None and want_lse:
@@ -359,7 +436,7 @@ def attn_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, seqlens, inv_freq_f64
                                _ptr(v_scale), _ptr(seqlens), _ptr(q_pos), B, lmax, hq, hkv, D,
                                _ptr(inv_freq_f64), float(softmax_scale), int(window), int(sinks),
                                _ptr(out), out_code, _ptr(lse), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream(stream)))
+                               _nbytes(workspace), _stream(stream)))
     return out, lse
 
 
