@@ -3,35 +3,43 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-One step is one pass of the prefill hot path over the Llama-2-7B-shaped 16K
-prefill (batch 1, 32/32 heads, head_dim 128, bf16, YaRN s=4 over 4096, base
-1e4): the frequency table (host, fp64; computed once per model and timed
-separately), the key rotation pass (rope_apply_packed) and the attention
-kernel (queries rotated on load, causal online softmax on bf16 MFMA, out +
-LSE).  W untimed steps, then exactly K steps between two device
+One step is one pass of the prefill hot path over the largest single-GPU
+workload, the Llama-3-70B-shaped ragged batch (4 sequences of 131072, 65537,
+32000 and 4097 tokens, 64 query / 8 KV heads, head_dim 128, bf16, YaRN s=8
+over 16384, base 5e5): the key rotation pass (rope_apply_packed) and the
+attention kernel (queries rotated on load, causal online softmax on bf16 MFMA,
+out + LSE).  The frequency table (host, fp64, once per model) is timed
+separately.  W untimed steps, then exactly K steps between two device
 synchronisations; the JSON line's `value` is the algorithmic causal FLOPs of
 one step over the wall time of one step.
 
-The same run then times the decode hot path (split-K sweep + LSE merge) over
-the 16-sequence 32K-128K cache workload and reports it as `decode`; under
-`next` it times chunked prefill (4 chunks of 4096 new tokens after 28K-124K
-cached ones), a 4096-token sliding window with 4 sink tokens on the prefill
-and decode inputs, and decode over an FP8 (E4M3) copy of the decode cache; and it times the fp64 CPU checker on bounded
-samples of the prefill and decode workloads as `cpu_baseline`.
+The same run times, under `secondary`, the 128K Llama-3-8B GQA prefill and
+the 16K Llama-2-7B prefill with the same step; the decode hot path (split-K
+sweep + LSE merge) over the 16-sequence 32K-128K cache workload as `decode`;
+under `next`, chunked prefill (4 chunks of 4096 new tokens after 28K-124K
+cached ones), a 4096-token sliding window with 4 sink tokens on the 16K
+prefill and the decode inputs, and decode over an FP8 (E4M3) copy of the
+decode cache; and the fp64 CPU checker on bounded samples of the same inputs
+as `cpu_baseline` (per row).
 
-Roofline: the attention kernel's own duration comes from HIP events on the
-launch stream around its launch inside every timed step.  `traffic` is filled
-from a counter summary under profiles/ when one exists for the current
-kernel source (FETCH_SIZE + WRITE_SIZE per dispatch, scaled by the same
-counters on a plain copy of known size); otherwise it is null.
+Roofline: each kernel's own duration comes from HIP events on the launch
+stream around its launch inside every timed step.  `traffic` is filled from a
+counter summary under profiles/ when one exists for the current kernel source
+(FETCH_SIZE + WRITE_SIZE per dispatch, scaled by the same counters on a plain
+copy of known size); otherwise it is null.
 
 Other modes:
-    --workload NAME           time another prefill workload (parity configs)
+    --workload NAME           time another prefill workload as the main line
+    --secondary a,b           prefill workloads of the secondary rows
+                              ("none" for none)
     --copy-probe              also run a 1 GiB device copy (counter calibration)
-    --no-next                 skip the lines of the chunked-prefill and
-                              sliding-window paths (under "next")
-    --summarize DIR --out F   turn rocprofv3 output (kernel stats or counter
-                              CSVs under DIR) into a short text summary
+    --no-next                 skip the lines of the next rows
+    --summarize DIR --out F   turn rocprofv3 output (kernel stats and / or
+                              counter CSVs under DIR, or several DIRs joined
+                              by commas) into a short text summary, with the
+                              matrix-core utilisation, MFMA FLOPs and shader
+                              clock of each dispatch when the counters for
+                              them are there
     --counters-json FETCH_DIR WRITE_DIR [--command "c1 ;; c2"]
                               HBM bytes per launch of the prefill and decode
                               kernels from FETCH_SIZE / WRITE_SIZE runs of
@@ -96,8 +104,10 @@ def traffic_from_profiles(kind: str, workload: str, digest: str):
 
 
 # ------------------------------------------------------------------ prefill
-def bench_prefill(args, torch, ops, wl):
-    cfg = wl.PREFILL_CONFIGS[args.workload]
+def bench_prefill(args, torch, ops, wl, name=None, steps=None, warmup=None):
+    cfg = wl.PREFILL_CONFIGS[name or args.workload]
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     if cfg.dtype != "bf16":
         raise SystemExit("bench times the bf16 path; the fp32 workload is a parity case")
     D, hq, hkv = cfg.head_dim, cfg.hq, cfg.hkv
@@ -138,23 +148,23 @@ def bench_prefill(args, torch, ops, wl):
         if ev is not None:
             ev[2].record(stream)
 
-    log(f"prefill warmup x{args.warmup}")
-    for _ in range(args.warmup):
+    log(f"prefill {cfg.name} warmup x{warmup}")
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     if int(dev_err.item()) != 0 or ops.read_device_error(ws) != 0:
         raise SystemExit("device range check failed")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    log(f"prefill timed x{args.steps}")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    log(f"prefill {cfg.name} timed x{steps}")
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    rope_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
-    ms_per_step = wall / args.steps * 1e3
+    rope_ms = sum(e[0].elapsed_time(e[1]) for e in events) / steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in events) / steps
+    ms_per_step = wall / steps * 1e3
     flops = wl.prefill_causal_flops(cfg.seq_lens, hq, D)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (attn_ms * 1e-3) / 1e12
@@ -517,37 +527,52 @@ def oracle_threads() -> int:
         return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(cfg_name, state, wl, target_s: float):
-    """The fp64 oracle, as it stands, on the first heads of the same prefill
-    inputs (all rows of each head), until about target_s seconds of work."""
+class _HostBf16:
+    """fp64 view of a device bf16 tensor, copied to the host once and widened
+    slice by slice (the oracle only slices its inputs)."""
+
+    def __init__(self, t, wl, torch):
+        import numpy as np
+        self.bits = t.view(torch.int16).cpu().numpy().view(np.uint16)
+        self.shape = self.bits.shape
+        self.wl = wl
+
+    def __getitem__(self, idx):
+        return self.wl.as_f64(self.bits[idx], "bf16")
+
+
+def cpu_baseline_rows(cfg_name, state, wl, torch, target_s: float, seed: int = 11):
+    """The fp64 oracle, as it stands, on seeded random query rows of the same
+    prefill inputs (each row over its full causal prefix, all query heads of
+    KV head 0), in batches of 64 rows until about target_s seconds of work.
+    FLOPs counted: 4 * D * (position + 1) per (row, head)."""
+    import numpy as np
     from oracle import attention as oatt
     from oracle import freqs as ofreqs
-    threads = oracle_threads()
     cfg = wl.PREFILL_CONFIGS[cfg_name]
-    inp = state["inp"]
     th = ofreqs.yarn_theta(cfg.head_dim, cfg.base, cfg.factor, cfg.original_max_position)
     sc = ofreqs.softmax_scale(cfg.head_dim, ofreqs.attention_temperature(cfg.factor))
+    q, k, v = (_HostBf16(state[x], wl, torch) for x in ("q", "k", "v"))
+    cu = state["inp"]["cu_seqlens"]
+    T = int(cu[-1])
     g = cfg.hq // cfg.hkv
-    import torch
-    q_host = state["q"].view(torch.int16).cpu().numpy()
-    k_host = state["k"].view(torch.int16).cpu().numpy()
-    v_host = state["v"].view(torch.int16).cpu().numpy()
-    done_heads, flops, elapsed = 0, 0, 0.0
-    while done_heads < cfg.hq and elapsed < target_s:
-        h = done_heads
-        hk = h // g
-        q = wl.as_f64(q_host[:, h:h + 1].view("uint16"), "bf16")
-        k = wl.as_f64(k_host[:, hk:hk + 1].view("uint16"), "bf16")
-        v = wl.as_f64(v_host[:, hk:hk + 1].view("uint16"), "bf16")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    starts = np.asarray(cu[:-1], dtype=np.int64)
+    nrows, flops, elapsed = 0, 0, 0.0
+    while elapsed < target_s and nrows < T:
+        toks = rng.integers(0, T, size=64)
+        rows = [(int(t), h) for t in toks for h in range(g)]
+        pos = toks - starts[np.searchsorted(starts, toks, side="right") - 1]
         t0 = time.perf_counter()
-        oatt.prefill(q, k, v, inp["cu_seqlens"], th, sc)
+        oatt.prefill_rows(q, k, v, cu, th, sc, rows)
         elapsed += time.perf_counter() - t0
-        flops += wl.prefill_causal_flops(cfg.seq_lens, 1, cfg.head_dim)
-        done_heads += 1
-    return {"value": round(flops / elapsed / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(elapsed, 2),
-            "sample": f"fp64 dense causal prefill of the first {done_heads} of {cfg.hq} query "
-                      f"heads, all {cfg.total_tokens} rows each, same inputs"}
+        flops += int(4 * cfg.head_dim * g * int(np.sum(pos + 1)))
+        nrows += len(toks)
+    return {"value": round(flops / elapsed / 1e12, 5), "unit": "TFLOP/s",
+            "cores": int(oracle_threads()), "kind": "oracle", "seconds": round(elapsed, 2),
+            "sample": f"fp64 causal prefill of {nrows} seeded random query rows of the same "
+                      f"{cfg.name} inputs (rows of every sequence, each over its full causal "
+                      f"prefix), all {g} query heads of KV head 0"}
 
 
 def cpu_baseline_decode(state, wl, torch, seconds: float = 10.0, nseq: int = 4):
@@ -588,33 +613,89 @@ def cpu_baseline_decode(state, wl, torch, seconds: float = 10.0, nseq: int = 4):
 
 
 # ------------------------------------------------------------------ rocprof summaries
-def summarize(dirname: str, out_path: str, command: str):
-    """Condense rocprofv3 CSV output under dirname into a short text file."""
+N_SIMD = 1024   # 256 CUs x 4 SIMDs
+N_XCD = 8       # GRBM_GUI_ACTIVE counts once per XCD
+
+
+def summarize(dirnames: str, out_path: str, command: str):
+    """Condense rocprofv3 CSV output under one or more directories (comma
+    separated) into a short text file: kernel statistics, the mean of every
+    counter per dispatch, and per kernel the derived figures the counters
+    allow -- matrix-core busy fraction SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x
+    GRBM_GUI_ACTIVE / XCDs), MFMA FLOPs SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
+    per dispatch, and with a kernel trace of the same command the shader
+    clock GRBM_GUI_ACTIVE / XCDs / duration and the MFMA rate."""
     import csv
-    lines = [f"# rocprofv3 summary", f"# command: {command}", ""]
-    stats = glob.glob(os.path.join(dirname, "**", "*kernel_stats.csv"), recursive=True)
-    for p in stats:
-        rows = list(csv.DictReader(open(p)))
-        lines.append(f"## kernel stats ({os.path.relpath(p, dirname)})")
-        lines.append("name | calls | total_ns | avg_ns | min_ns | max_ns | pct")
-        for r in rows:
-            name = r.get("Name", "")[:110]
-            lines.append(f"{name} | {r.get('Calls')} | {r.get('TotalDurationNs')} | "
-                         f"{r.get('AverageNs')} | {r.get('MinNs')} | {r.get('MaxNs')} | "
-                         f"{r.get('Percentage')}")
-        lines.append("")
-    ctrs = glob.glob(os.path.join(dirname, "**", "*counter_collection.csv"), recursive=True)
-    for p in ctrs:
-        rows = list(csv.DictReader(open(p)))
-        agg = {}
-        for r in rows:
-            key = (r.get("Kernel_Name", "")[:110], r.get("Counter_Name", ""))
-            agg.setdefault(key, []).append(float(r.get("Counter_Value", 0) or 0))
-        lines.append(f"## counters ({os.path.relpath(p, dirname)}): mean per dispatch")
-        lines.append("kernel | counter | dispatches | mean | min | max")
-        for (kname, cname), vals in sorted(agg.items()):
-            lines.append(f"{kname} | {cname} | {len(vals)} | {sum(vals) / len(vals):.6g} | "
-                         f"{min(vals):.6g} | {max(vals):.6g}")
+    dirs = [d for d in dirnames.split(",") if d]
+    lines = ["# rocprofv3 summary", f"# command: {command}", ""]
+    durations = {}
+    for dirname in dirs:
+        for p in glob.glob(os.path.join(dirname, "**", "*kernel_stats.csv"), recursive=True):
+            rows = list(csv.DictReader(open(p)))
+            lines.append(f"## kernel stats ({os.path.relpath(p, dirname)})")
+            lines.append("name | calls | total_ns | avg_ns | min_ns | max_ns | pct")
+            for r in rows:
+                name = r.get("Name", "")[:110]
+                durations[name] = float(r.get("AverageNs") or 0)
+                lines.append(f"{name} | {r.get('Calls')} | {r.get('TotalDurationNs')} | "
+                             f"{r.get('AverageNs')} | {r.get('MinNs')} | {r.get('MaxNs')} | "
+                             f"{r.get('Percentage')}")
+            lines.append("")
+    derived = []
+    for dirname in dirs:
+        for p in glob.glob(os.path.join(dirname, "**", "*counter_collection.csv"), recursive=True):
+            rows = list(csv.DictReader(open(p)))
+            # sum the per-instance values of a counter within a dispatch first
+            per = {}
+            for r in rows:
+                key = (r.get("Kernel_Name", "")[:110], r.get("Counter_Name", ""),
+                       r.get("Dispatch_Id", ""))
+                per[key] = per.get(key, 0.0) + float(r.get("Counter_Value", 0) or 0)
+            agg = {}
+            for (kname, cname, _), val in per.items():
+                agg.setdefault((kname, cname), []).append(val)
+            lines.append(f"## counters ({os.path.relpath(p, dirname)}): mean per dispatch")
+            lines.append("kernel | counter | dispatches | mean | min | max")
+            for (kname, cname), vals in sorted(agg.items()):
+                lines.append(f"{kname} | {cname} | {len(vals)} | {sum(vals) / len(vals):.6g} | "
+                             f"{min(vals):.6g} | {max(vals):.6g}")
+            lines.append("")
+            kernels = sorted({k for k, _ in agg})
+            for kname in kernels:
+                m = {c: sum(v) / len(v) for (k, c), v in agg.items() if k == kname}
+                busy, gui = m.get("SQ_VALU_MFMA_BUSY_CYCLES"), m.get("GRBM_GUI_ACTIVE")
+                mops = m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+                if not busy or not gui:
+                    continue
+                cyc = gui / N_XCD
+                d = {"kernel": kname, "kernel_cycles": cyc,
+                     "mfma_busy_frac": busy / (N_SIMD * cyc)}
+                if mops:
+                    d["mfma_flops_per_dispatch"] = mops * 512
+                dur = durations.get(kname)
+                if dur:
+                    d["duration_ms"] = dur / 1e6
+                    d["shader_clock_ghz"] = cyc / dur
+                    if mops:
+                        d["mfma_tflops"] = mops * 512 / (dur * 1e-9) / 1e12
+                        d["frac_of_peak"] = d["mfma_tflops"] / PEAK_BF16_TFLOPS
+                derived.append(d)
+    if derived:
+        lines.append("## matrix-core utilisation (derived, mean per dispatch)")
+        lines.append(f"# busy frac = SQ_VALU_MFMA_BUSY_CYCLES / ({N_SIMD} SIMDs x GRBM_GUI_ACTIVE/"
+                     f"{N_XCD}); FLOPs = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; clock = "
+                     f"GRBM_GUI_ACTIVE/{N_XCD} / kernel-trace duration; peak "
+                     f"{PEAK_BF16_TFLOPS} TFLOP/s")
+        lines.append("kernel | mfma busy | kernel cycles | MFMA FLOP/dispatch | duration ms | "
+                     "clock GHz | MFMA TFLOP/s | frac of peak")
+
+        def f(d, k, fmt):
+            return format(d[k], fmt) if k in d else "-"
+        for d in derived:
+            lines.append(f"{d['kernel']} | {d['mfma_busy_frac']:.3f} | {d['kernel_cycles']:.4g} | "
+                         f"{f(d, 'mfma_flops_per_dispatch', '.4g')} | {f(d, 'duration_ms', '.4f')} | "
+                         f"{f(d, 'shader_clock_ghz', '.3f')} | {f(d, 'mfma_tflops', '.1f')} | "
+                         f"{f(d, 'frac_of_peak', '.4f')}")
         lines.append("")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -691,7 +772,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=None)
-    ap.add_argument("--workload", default="llama2_7b_prefill_16k")
+    ap.add_argument("--workload", default="llama3_70b_ragged_prefill")
+    ap.add_argument("--secondary", default="llama3_8b_gqa_prefill_128k,llama2_7b_prefill_16k")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true")
@@ -735,6 +817,35 @@ def main():
             "data": "synthetic", "config": conf, "roofline": roof,
             "frac_mfma_peak_wall": round(value / PEAK_BF16_TFLOPS, 4)}
     line.update(extra)
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle on sampled rows of the main workload")
+        line["cpu_baseline"] = cpu_baseline_rows(args.workload, pstate, wl, torch,
+                                                 args.cpu_seconds)
+    del pstate
+    torch.cuda.empty_cache()
+    # secondary prefill rows (same step, fewer steps for the long ones); the
+    # 16K state is kept for the windowed-prefill row
+    swa_state = None
+    names = [] if args.secondary == "none" else [n for n in args.secondary.split(",") if n]
+    if names:
+        line["secondary"] = {}
+    for name in names:
+        cfg = wl.PREFILL_CONFIGS[name]
+        big = max(cfg.seq_lens) > 32768
+        st = max(3, args.steps // 4) if big else args.steps
+        v2, ms2, roof2, extra2, conf2, state2 = bench_prefill(args, torch, ops, wl, name=name,
+                                                              steps=st)
+        row = {"metric": "causal prefill TFLOP/s", "value": round(v2, 2), "unit": "TFLOP/s",
+               "steps": st, "ms_per_step": round(ms2, 4),
+               "frac_mfma_peak_wall": round(v2 / PEAK_BF16_TFLOPS, 4), "config": conf2,
+               "roofline": roof2}
+        row.update(extra2)
+        line["secondary"][name] = row
+        if name == wl.LLAMA2_7B_16K.name:
+            swa_state = state2
+        else:
+            del state2
+        torch.cuda.empty_cache()
     if args.copy_probe:
         a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
         b = torch.empty_like(a)
@@ -747,12 +858,12 @@ def main():
         dres, dstate = bench_decode(args, torch, ops, wl)
         line["decode"] = dres
     if not args.no_next:
-        line["next"] = bench_next(args, torch, ops, wl, pstate, dstate)
-    if not args.no_cpu_baseline:
-        log("timing the fp64 CPU oracle on a bounded sample")
-        line["cpu_baseline"] = cpu_baseline(args.workload, pstate, wl, args.cpu_seconds)
-        if not args.no_decode:
-            line["decode"]["cpu_baseline"] = cpu_baseline_decode(dstate, wl, torch)
+        if swa_state is None:
+            *_, swa_state = bench_prefill(args, torch, ops, wl, name=wl.LLAMA2_7B_16K.name,
+                                          steps=1, warmup=1)
+        line["next"] = bench_next(args, torch, ops, wl, swa_state, dstate)
+    if not args.no_cpu_baseline and not args.no_decode:
+        line["decode"]["cpu_baseline"] = cpu_baseline_decode(dstate, wl, torch)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -23,8 +23,8 @@
  *  - Layouts are dense row-major with the last dimension contiguous.
  *    Element types: YR_F32 (float) or YR_BF16 (bfloat16 bit patterns).
  *  - Thread safety: the library keeps no global state besides the per-thread
- *    error message; concurrent calls are safe when their outputs and
- *    workspaces do not overlap.
+ *    error message and per-device constants it looks up once; concurrent
+ *    calls are safe when their outputs and workspaces do not overlap.
  *
  * Sources are cited by page title and section ("Arch 03 -- Long Context"
  * slide deck; "Long-context models", blog.ecitis.org; "LLM context window
@@ -38,6 +38,12 @@
 
 #ifdef __cplusplus
 extern "C" {
+#endif
+
+/* The entry points below are the library's only exported symbols (it is
+   built with hidden visibility by default). */
+#if defined(__GNUC__)
+#pragma GCC visibility push(default)
 #endif
 
 /* ---- status codes ------------------------------------------------------ */
@@ -156,6 +162,11 @@ int rope_apply_packed(const void *src, void *dst, int dtype, const int *cu_seqle
                                   rope_apply_packed or a rotated cache): no key
                                   pass; queries are still rotated on load when
                                   inv_freq_f64 != NULL */
+#define YR_PREFILL_PERMUTED_ORDER 2 /* bf16 path: the workgroups take their work
+                                  items (q-tile, sequence, head) in a permuted
+                                  order instead of longest first.  Results are
+                                  bit-identical (each item is computed alone);
+                                  it exists to test that, and is slower. */
 
 /* Workspace bytes attn_prefill_fwd needs for these sizes (with flags = 0). */
 size_t attn_prefill_workspace_bytes(long long T, int Hkv, int head_dim, int in_dtype);
@@ -188,7 +199,8 @@ size_t attn_prefill_workspace_bytes(long long T, int Hkv, int head_dim, int in_d
  *                  (zero-length sequences are allowed and produce nothing)
  *   inv_freq_f64   device double[head_dim/2], or NULL when q and k are already
  *                  rotated
- *   flags          0, or YR_PREFILL_K_ROTATED
+ *   flags          0 or a combination of YR_PREFILL_K_ROTATED and
+ *                  YR_PREFILL_PERMUTED_ORDER
  *   window, sinks  >= 0 (see above)
  *   out            device [T, Hq, head_dim] of out_dtype (YR_F32 or YR_BF16;
  *                  YR_F32 inputs require YR_F32 out)
@@ -322,6 +334,10 @@ const char *yr_status_string(int status);
 const char *yr_last_error(void);
 /* Library version as major*10000 + minor*100 + patch. */
 int yr_version(void);
+
+#if defined(__GNUC__)
+#pragma GCC visibility pop
+#endif
 
 #ifdef __cplusplus
 }

@@ -124,7 +124,7 @@ def prefill_call(lib, **kw):
     (dict(ws=ctypes.c_void_p((1 << 20) + 16)), ops.YR_ERR_WORKSPACE),
     (dict(ws_bytes=100), ops.YR_ERR_WORKSPACE),
     (dict(T=1 << 20, ws_bytes=(1 << 20) * 2 * 128 * 2), ops.YR_ERR_WORKSPACE),
-    (dict(flags=2), ops.YR_ERR_INVALID),
+    (dict(flags=4), ops.YR_ERR_INVALID),
     (dict(flags=ops.YR_PREFILL_K_ROTATED, ws_bytes=255), ops.YR_ERR_WORKSPACE),
     (dict(window=-1), ops.YR_ERR_INVALID),
     (dict(sinks=-4), ops.YR_ERR_INVALID),

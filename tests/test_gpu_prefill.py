@@ -96,12 +96,19 @@ def test_bf16_ragged_full(lens, hq, hkv, D, out_dtype):
     assert e_out <= BF16_TOL and e_lse <= BF16_TOL
 
 
-def _sampled(cfg, n_random):
+def _sampled(cfg, n_random, tile_edges_group=None):
+    """Full-size run, checked on sampled rows: the fixed edge rows and
+    n_random seeded rows per (sequence, KV group), and for one KV group the
+    first and last row of every 256-row q-tile of every sequence (the rows a
+    workgroup starts and ends on, across the whole length)."""
     inp = wl.make_prefill(cfg)
     say(f"prefill {cfg.name} full size, sampled rows")
     out, lse = _run(inp, cfg.hq, cfg.hkv, cfg.head_dim, cfg.base, cfg.factor,
                     cfg.original_max_position)
     rows = wl.sample_rows(cfg.seq_lens, cfg.hq, cfg.hkv, n_random=n_random)
+    if tile_edges_group is not None:
+        rows = sorted(set(rows) | set(wl.tile_edge_rows(cfg.seq_lens, cfg.hq, cfg.hkv,
+                                                        tile_edges_group, 256)))
     th, scale = oracle_theta(cfg.head_dim, cfg.base, cfg.factor, cfg.original_max_position)
     dt = inp["dtype"]
     ro, rl = oatt.prefill_rows(LazyF64(inp["q"], dt), LazyF64(inp["k"], dt),
@@ -110,21 +117,25 @@ def _sampled(cfg, n_random):
     got_o = np.stack([out[t, h] for t, h in rows])
     got_l = np.array([lse[h, t] for t, h in rows])
     e_out, e_lse = max_abs(got_o, ro), max_abs(got_l, rl)
-    print(f"{cfg.name}: {len(rows)} rows, max-abs out {e_out:.3e} lse {e_lse:.3e}")
+    print(f"{cfg.name}: {len(rows)} (row, head) pairs checked, max-abs out {e_out:.3e} "
+          f"lse {e_lse:.3e}")
     assert np.all(np.isfinite(out))
     assert e_out <= BF16_TOL and e_lse <= BF16_TOL
 
 
 def test_llama2_7b_16k_sampled():
-    _sampled(wl.LLAMA2_7B_16K, n_random=16)
+    _sampled(wl.LLAMA2_7B_16K, n_random=256, tile_edges_group=0)
 
 
+@pytest.mark.timeout(300)
 def test_llama3_8b_128k_sampled():
-    _sampled(wl.LLAMA3_8B_128K, n_random=8)
+    _sampled(wl.LLAMA3_8B_128K, n_random=256, tile_edges_group=3)
 
 
+@pytest.mark.timeout(400)
 def test_llama3_70b_ragged_sampled():
-    _sampled(wl.LLAMA3_70B_RAGGED, n_random=4)
+    # the inputs (3.8 GB of queries) take ~45 s to draw and the oracle ~50 s
+    _sampled(wl.LLAMA3_70B_RAGGED, n_random=64, tile_edges_group=5)
 
 
 def test_gqa_equals_repeated_heads_on_gpu():
@@ -146,6 +157,30 @@ def test_deterministic():
     a = _run(inp, 8, 2, 128, cfg.base, cfg.factor, cfg.original_max_position)
     b = _run(inp, 8, 2, 128, cfg.base, cfg.factor, cfg.original_max_position)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("lens,hq,hkv", [((1000, 999, 1, 77, 513), 64, 8), ((700, 300, 1300), 12, 3)])
+def test_deterministic_under_permuted_order(lens, hq, hkv):
+    """Workgroups taking their (q-tile, sequence, head) items in a permuted
+    order (reversed and rotated instead of longest first) give the same bits:
+    no result depends on which workgroup computes an item or on what runs
+    beside it."""
+    cfg = wl.PrefillConfig("t", 74, lens, hq, hkv, 128, "bf16", 500000.0, 8.0, 16384)
+    inp = wl.make_prefill(cfg)
+    th_dev, scale = lib_theta(128, cfg.base, cfg.factor, cfg.original_max_position)
+    cu = torch.from_numpy(inp["cu_seqlens"]).cuda()
+    q, k, v = to_dev(inp["q"], "bf16"), to_dev(inp["k"], "bf16"), to_dev(inp["v"], "bf16")
+    say(f"prefill permuted order lens={lens} hq={hq} hkv={hkv}")
+    a, al = ops.attn_prefill_fwd(q, k, v, cu, max(lens), th_dev, scale)
+    b, bl = ops.attn_prefill_fwd(q, k, v, cu, max(lens), th_dev, scale, permuted_order=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(al, bl)
+    th, sc = oracle_theta(128, cfg.base, cfg.factor, cfg.original_max_position)
+    rows = wl.sample_rows(lens, hq, hkv, n_random=8)
+    ro, rl = oatt.prefill_rows(wl.as_f64(inp["q"], "bf16"), wl.as_f64(inp["k"], "bf16"),
+                               wl.as_f64(inp["v"], "bf16"), inp["cu_seqlens"], th, sc, rows)
+    got = to_f64(b)
+    assert max_abs(np.stack([got[t, h] for t, h in rows]), ro) <= BF16_TOL
 
 
 def test_bad_cu_seqlens_sets_device_flag():
@@ -176,13 +211,20 @@ def test_bad_cu_seqlens_sets_device_flag():
     assert ops.read_device_error(ws) == ops.YR_DEVERR_CU_SEQLENS
 
 
-def test_prerotated_inputs_equal_fused_rotation():
+def test_prerotated_inputs_match_their_oracle():
+    """Queries and keys rotated beforehand (rope_apply, bf16 results) and
+    passed with inv_freq_f64 = NULL: the kernel only scales and rounds the
+    query, so the oracle for exactly those input bits (theta = None) is the
+    reference; the fused path on the unrotated inputs is checked against the
+    oracle that rotates them.  (The two paths round the rotated query to bf16
+    at different points, so they are compared each with its own reference.)"""
     cfg = wl.PrefillConfig("t", 72, (400, 50), 4, 2, 128, "bf16", 500000.0, 8.0, 64)
     inp = wl.make_prefill(cfg)
     th_dev, scale = lib_theta(128, cfg.base, cfg.factor, cfg.original_max_position)
+    th, sc = oracle_theta(128, cfg.base, cfg.factor, cfg.original_max_position)
     cu = torch.from_numpy(inp["cu_seqlens"]).cuda()
     q, k, v = to_dev(inp["q"], "bf16"), to_dev(inp["k"], "bf16"), to_dev(inp["v"], "bf16")
-    say("prefill fused vs pre-rotated")
+    say("prefill fused vs pre-rotated, each against its oracle")
     a, al = ops.attn_prefill_fwd(q, k, v, cu, 400, th_dev, scale)
     pos = torch.cat([torch.arange(400), torch.arange(50)]).to(torch.int32).cuda()
     qr, kr = q.clone(), k.clone()
@@ -190,11 +232,16 @@ def test_prerotated_inputs_equal_fused_rotation():
     ops.rope_apply(kr, pos, th_dev)
     b, bl = ops.attn_prefill_fwd(qr, kr, v, cu, 400, None, scale)
     torch.cuda.synchronize()
-    # the fused path rounds the rotated, scaled query to bf16 once; a
-    # pre-rotated query was rounded once already (by rope_apply), then scaled
-    # and rounded again: equal up to that one bf16 rounding of q
-    assert max_abs(to_f64(a), to_f64(b)) <= BF16_TOL
-    assert max_abs(al.cpu().numpy(), bl.cpu().numpy()) <= BF16_TOL
+    ro, rl = oatt.prefill(wl.as_f64(inp["q"], "bf16"), wl.as_f64(inp["k"], "bf16"),
+                          wl.as_f64(inp["v"], "bf16"), inp["cu_seqlens"], th, sc)
+    assert max_abs(to_f64(a), ro) <= BF16_TOL and max_abs(al.cpu().numpy(), rl) <= BF16_TOL
+    qr_bits = qr.view(torch.int16).cpu().numpy().view(np.uint16)
+    kr_bits = kr.view(torch.int16).cpu().numpy().view(np.uint16)
+    po, pl = oatt.prefill(wl.as_f64(qr_bits, "bf16"), wl.as_f64(kr_bits, "bf16"),
+                          wl.as_f64(inp["v"], "bf16"), inp["cu_seqlens"], None, sc)
+    e_out, e_lse = max_abs(to_f64(b), po), max_abs(bl.cpu().numpy(), pl)
+    print(f"pre-rotated path vs oracle: out {e_out:.3e} lse {e_lse:.3e}")
+    assert e_out <= BF16_TOL and e_lse <= BF16_TOL
 
 
 def test_k_rotated_flag_equals_library_key_pass():

@@ -36,6 +36,146 @@ int fail_hip(hipError_t err, const char *where) {
   return YR_ERR_HIP;
 }
 
+namespace {
+
+// attn_decode and attn_decode_fp8: validation, the choice of sweep form and
+// split, the workspace layout and the launch.  cache_dtype is the storage
+// type of the caches (q is YR_F32 with an fp32 cache, else YR_BF16).  The
+// workspace is checked against attn_decode_workspace_bytes, the bound for any
+// split of these sizes.
+struct DecodeCall {
+  const char *fn;
+  const void *q, *k_cache, *v_cache;
+  int cache_dtype;
+  const float *k_scale, *v_scale;
+  const int *seqlens, *q_pos;
+  int B, max_cache_len, Hq, Hkv, head_dim;
+  const double *inv_freq_f64;
+  float softmax_scale;
+  int window, sinks;
+  void *out;
+  int out_dtype;
+  float *lse;
+  void *workspace;
+  size_t workspace_bytes;
+  void *stream;
+};
+
+int decode_impl(const DecodeCall &c) {
+  char msg[200];
+  auto bad = [&](int st, const char *what) {
+    std::snprintf(msg, sizeof msg, "%s: %s", c.fn, what);
+    return fail(st, msg);
+  };
+  const int cache_dtype = c.cache_dtype, B = c.B, Hq = c.Hq, Hkv = c.Hkv;
+  const int head_dim = c.head_dim, max_cache_len = c.max_cache_len;
+  const int window = c.window, sinks = c.sinks;
+  if (cache_dtype != YR_F32 && cache_dtype != YR_BF16 && cache_dtype != YR_FP8_E4M3)
+    return bad(YR_ERR_UNSUPPORTED, "in_dtype must be YR_F32 or YR_BF16");
+  if (c.out_dtype != YR_F32 && c.out_dtype != YR_BF16)
+    return bad(YR_ERR_UNSUPPORTED, "out_dtype must be YR_F32 or YR_BF16");
+  if (!dims_ok(head_dim)) return bad(YR_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return bad(YR_ERR_INVALID, "need Hq >= 1, Hkv >= 1, Hq % Hkv == 0");
+  if (Hq / Hkv > (cache_dtype == YR_F32 ? 16 : 32))
+    return bad(YR_ERR_UNSUPPORTED, "at most 32 (bf16, fp8) or 16 (fp32) query heads per KV head");
+  if (B < 1 || max_cache_len < 1) return bad(YR_ERR_INVALID, "need B >= 1, max_cache_len >= 1");
+  if ((long long)B * max_cache_len > (1LL << 34)) return bad(YR_ERR_INVALID, "cache too large");
+  if (!std::isfinite(c.softmax_scale) || !(c.softmax_scale > 0.f))
+    return bad(YR_ERR_INVALID, "softmax_scale must be finite and > 0");
+  if (window < 0 || sinks < 0) return bad(YR_ERR_INVALID, "window and sinks must be >= 0");
+  if (window == 1 && sinks == 0)
+    return bad(YR_ERR_INVALID, "a one-token window without sinks sees no cache row");
+  if (!c.q || !c.k_cache || !c.v_cache || !c.seqlens || !c.out)
+    return bad(YR_ERR_NULL, "q, caches, seqlens and out are required");
+  if (cache_dtype == YR_FP8_E4M3 && (!c.k_scale || !c.v_scale))
+    return bad(YR_ERR_NULL, "k_scale and v_scale are required");
+  if (!c.workspace) return bad(YR_ERR_NULL, "workspace is required");
+  if ((reinterpret_cast<uintptr_t>(c.workspace) & 255) != 0)
+    return bad(YR_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const size_t need = attn_decode_workspace_bytes(B, max_cache_len, Hq, head_dim);
+  if (c.workspace_bytes < need) return bad(YR_ERR_WORKSPACE, "workspace too small");
+  hipStream_t stream = (hipStream_t)c.stream;
+
+  // the matrix-core kernel launches one workgroup per group of KV heads, the
+  // fp32 one per head: chunk so that either launches enough workgroups
+  const bool fp8 = cache_dtype == YR_FP8_E4M3, win = window > 0;
+  const bool balanced =
+      cache_dtype != YR_F32 && decode_stream_form(B, max_cache_len, Hkv, head_dim, fp8, window, sinks);
+  const bool shared = decode_shared_form(fp8, win, balanced);
+  const int units = cache_dtype == YR_F32 || shared
+                        ? Hkv
+                        : Hkv / decode_heads_per_wg(Hkv, head_dim, fp8);
+  const int min_chunk =
+      cache_dtype == YR_F32 || shared ? kDecodeMinChunk : kDecodeMinChunkMfma;
+  int chunk = decode_chunk(B, max_cache_len, units, min_chunk);
+  int nsplit = decode_nsplit(max_cache_len, chunk);
+  // With a window the matrix-core sweep can split the visible rows alone
+  // (normally window - 1 + sinks of them) instead of the whole cache, so that
+  // no workgroup starts on rows nobody reads; the workspace is sized for the
+  // finer split of the whole cache, so this applies when it needs fewer chunks.
+  int vis_split = 0;
+  if (window > 0 && cache_dtype != YR_F32) {
+    const int span = (int)std::min<long long>(max_cache_len, (long long)window + sinks);
+    const int cw = decode_chunk(B, span, units, min_chunk, 1024);
+    const int nw = decode_nsplit(span, cw);
+    if (nw < nsplit) {
+      chunk = cw;
+      nsplit = nw;
+      vis_split = 1;
+    }
+  }
+  if ((long long)B * Hkv * nsplit > 0x7fffffffLL) return bad(YR_ERR_INVALID, "grid too large");
+  size_t rows = (size_t)B * Hq * nsplit;
+  // head-per-wave sweep of a large cache, four or eight KV heads per
+  // workgroup: split the key blocks evenly over one workgroup per CU instead
+  int stream_wg = 0, stream_hpw = 0;
+  if (balanced) {
+    stream_wg = decode_stream_wgs(stream);
+    if (stream_wg <= 0) return bad(YR_ERR_HIP, "cannot query the device's compute units");
+    stream_hpw = Hkv / units;
+    rows = ((size_t)stream_wg + (size_t)B * units) * (size_t)(Hq / units);
+  }
+  const size_t o_bytes = align_up(rows * head_dim * 4, 256);
+  char *ws = static_cast<char *>(c.workspace);
+  int *flag = flag_of(c.workspace);
+  DecodeArgs d{};
+  d.q = c.q;
+  d.k_cache = c.k_cache;
+  d.v_cache = c.v_cache;
+  d.in_dtype = cache_dtype;
+  d.seqlens = c.seqlens;
+  d.q_pos = c.q_pos;
+  d.B = B;
+  d.max_cache_len = max_cache_len;
+  d.Hq = Hq;
+  d.Hkv = Hkv;
+  d.head_dim = head_dim;
+  d.theta = c.inv_freq_f64;
+  d.softmax_scale = c.softmax_scale;
+  d.out = c.out;
+  d.out_dtype = c.out_dtype;
+  d.lse = c.lse;
+  d.part_o = reinterpret_cast<float *>(ws + kHeader);
+  d.part_lse = reinterpret_cast<float *>(ws + kHeader + o_bytes);
+  d.chunk = chunk;
+  d.nsplit = nsplit;
+  d.dev_flag = flag;
+  d.window = window;
+  d.sinks = sinks;
+  d.k_scale = c.k_scale;
+  d.v_scale = c.v_scale;
+  d.vis_split = vis_split;
+  d.stream_wg = stream_wg;
+  d.stream_hpw = stream_hpw;
+  d.shared_form = shared ? 1 : 0;
+  const hipError_t e = launch_decode(d, stream);
+  if (e != hipSuccess) return fail_hip(e, c.fn);
+  return YR_OK;
+}
+
+}  // namespace
+
 }  // namespace yr
 
 using namespace yr;
@@ -122,7 +262,8 @@ int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
                      int head_dim, const double *inv_freq_f64, int flags, float softmax_scale,
                      int window, int sinks, void *out, int out_dtype, float *lse, void *workspace,
                      size_t workspace_bytes, void *stream) {
-  if (flags & ~YR_PREFILL_K_ROTATED) return fail(YR_ERR_INVALID, "attn_prefill_fwd: unknown flags");
+  if (flags & ~(YR_PREFILL_K_ROTATED | YR_PREFILL_PERMUTED_ORDER))
+    return fail(YR_ERR_INVALID, "attn_prefill_fwd: unknown flags");
   if (in_dtype != YR_F32 && in_dtype != YR_BF16)
     return fail(YR_ERR_UNSUPPORTED, "attn_prefill_fwd: in_dtype must be YR_F32 or YR_BF16");
   if (out_dtype != YR_F32 && out_dtype != YR_BF16)
@@ -174,6 +315,7 @@ int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
   p.ctx_lens = nullptr;
   p.window = window;
   p.sinks = sinks;
+  p.permuted_order = (flags & YR_PREFILL_PERMUTED_ORDER) ? 1 : 0;
 
   if (key_pass && T > 0) {
     // rotate every key once into the workspace; the attention kernel rotates
@@ -278,123 +420,6 @@ size_t attn_decode_workspace_bytes(int B, int max_cache_len, int Hq, int head_di
   return kHeader + align_up(rows * head_dim * 4, 256) + align_up(rows * 4, 256);
 }
 
-namespace {
-
-// attn_decode and attn_decode_fp8: validation, workspace layout and launch.
-// cache_dtype is the storage type of the caches (q is YR_F32 with an fp32
-// cache, else YR_BF16).
-int decode_impl(const char *fn, const void *q, const void *k_cache, const void *v_cache,
-                int cache_dtype, const float *k_scale, const float *v_scale, const int *seqlens,
-                const int *q_pos, int B, int max_cache_len, int Hq, int Hkv, int head_dim,
-                const double *inv_freq_f64, float softmax_scale, int window, int sinks,
-                void *out, int out_dtype, float *lse, void *workspace, size_t workspace_bytes,
-                void *stream) {
-  char msg[160];
-  auto bad = [&](int st, const char *what) {
-    std::snprintf(msg, sizeof msg, "%s: %s", fn, what);
-    return fail(st, msg);
-  };
-  if (cache_dtype != YR_F32 && cache_dtype != YR_BF16 && cache_dtype != YR_FP8_E4M3)
-    return bad(YR_ERR_UNSUPPORTED, "in_dtype must be YR_F32 or YR_BF16");
-  if (out_dtype != YR_F32 && out_dtype != YR_BF16)
-    return bad(YR_ERR_UNSUPPORTED, "out_dtype must be YR_F32 or YR_BF16");
-  if (!dims_ok(head_dim)) return bad(YR_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
-  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
-    return bad(YR_ERR_INVALID, "need Hq >= 1, Hkv >= 1, Hq % Hkv == 0");
-  if (Hq / Hkv > (cache_dtype == YR_F32 ? 16 : 32))
-    return bad(YR_ERR_UNSUPPORTED, "at most 32 (bf16, fp8) or 16 (fp32) query heads per KV head");
-  if (B < 1 || max_cache_len < 1) return bad(YR_ERR_INVALID, "need B >= 1, max_cache_len >= 1");
-  if ((long long)B * max_cache_len > (1LL << 34)) return bad(YR_ERR_INVALID, "cache too large");
-  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
-    return bad(YR_ERR_INVALID, "softmax_scale must be finite and > 0");
-  if (window < 0 || sinks < 0) return bad(YR_ERR_INVALID, "window and sinks must be >= 0");
-  if (window == 1 && sinks == 0)
-    return bad(YR_ERR_INVALID, "a one-token window without sinks sees no cache row");
-  if (!q || !k_cache || !v_cache || !seqlens || !out || !workspace)
-    return bad(YR_ERR_NULL, "q, caches, seqlens, out and workspace are required");
-  if (cache_dtype == YR_FP8_E4M3 && (!k_scale || !v_scale))
-    return bad(YR_ERR_NULL, "k_scale and v_scale are required");
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
-    return bad(YR_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  const size_t need = attn_decode_workspace_bytes(B, max_cache_len, Hq, head_dim);
-  if (workspace_bytes < need) return bad(YR_ERR_WORKSPACE, "workspace too small");
-
-  // the matrix-core kernel launches one workgroup per group of KV heads, the
-  // fp32 one per head: chunk so that either launches enough workgroups
-  const bool fp8 = cache_dtype == YR_FP8_E4M3, win = window > 0;
-  const bool balanced =
-      cache_dtype != YR_F32 && decode_stream_form(B, max_cache_len, Hkv, head_dim, fp8, window, sinks);
-  const bool shared = decode_shared_form(fp8, win, balanced);
-  const int units = cache_dtype == YR_F32 || shared
-                        ? Hkv
-                        : Hkv / decode_heads_per_wg(Hkv, head_dim, fp8);
-  const int min_chunk =
-      cache_dtype == YR_F32 || shared ? kDecodeMinChunk : kDecodeMinChunkMfma;
-  int chunk = decode_chunk(B, max_cache_len, units, min_chunk);
-  int nsplit = decode_nsplit(max_cache_len, chunk);
-  // With a window the matrix-core sweep can split the visible rows alone
-  // (normally window - 1 + sinks of them) instead of the whole cache, so that
-  // no workgroup starts on rows nobody reads; the workspace is sized for the
-  // finer split of the whole cache, so this applies when it needs fewer chunks.
-  int vis_split = 0;
-  if (window > 0 && cache_dtype != YR_F32) {
-    const int span = (int)std::min<long long>(max_cache_len, (long long)window + sinks);
-    const int cw = decode_chunk(B, span, units, min_chunk, 1024);
-    const int nw = decode_nsplit(span, cw);
-    if (nw < nsplit) {
-      chunk = cw;
-      nsplit = nw;
-      vis_split = 1;
-    }
-  }
-  if ((long long)B * Hkv * nsplit > 0x7fffffffLL) return bad(YR_ERR_INVALID, "grid too large");
-  size_t rows = (size_t)B * Hq * nsplit;
-  // head-per-wave sweep of a large cache, four or eight KV heads per
-  // workgroup: split the key blocks evenly over one workgroup per CU instead
-  int stream_wg = 0, stream_hpw = 0;
-  if (balanced) {
-    stream_wg = decode_stream_wgs();
-    if (stream_wg <= 0) return bad(YR_ERR_HIP, "cannot query the device's compute units");
-    stream_hpw = Hkv / units;
-    rows = ((size_t)stream_wg + (size_t)B * units) * (size_t)(Hq / units);
-  }
-  char *ws = static_cast<char *>(workspace);
-  DecodeArgs d{};
-  d.q = q;
-  d.k_cache = k_cache;
-  d.v_cache = v_cache;
-  d.in_dtype = cache_dtype;
-  d.seqlens = seqlens;
-  d.q_pos = q_pos;
-  d.B = B;
-  d.max_cache_len = max_cache_len;
-  d.Hq = Hq;
-  d.Hkv = Hkv;
-  d.head_dim = head_dim;
-  d.theta = inv_freq_f64;
-  d.softmax_scale = softmax_scale;
-  d.out = out;
-  d.out_dtype = out_dtype;
-  d.lse = lse;
-  d.part_o = reinterpret_cast<float *>(ws + kHeader);
-  d.part_lse = reinterpret_cast<float *>(ws + kHeader + align_up(rows * head_dim * 4, 256));
-  d.chunk = chunk;
-  d.nsplit = nsplit;
-  d.dev_flag = flag_of(workspace);
-  d.window = window;
-  d.sinks = sinks;
-  d.k_scale = k_scale;
-  d.v_scale = v_scale;
-  d.vis_split = vis_split;
-  d.stream_wg = stream_wg;
-  d.stream_hpw = stream_hpw;
-  d.shared_form = shared ? 1 : 0;
-  const hipError_t e = launch_decode(d, (hipStream_t)stream);
-  if (e != hipSuccess) return fail_hip(e, fn);
-  return YR_OK;
-}
-
-}  // namespace
 
 int attn_decode(const void *q, const void *k_cache, const void *v_cache, int in_dtype,
                 const int *seqlens, const int *q_pos, int B, int max_cache_len, int Hq, int Hkv,
@@ -403,9 +428,9 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, int in_
                 size_t workspace_bytes, void *stream) {
   if (in_dtype != YR_F32 && in_dtype != YR_BF16)
     return fail(YR_ERR_UNSUPPORTED, "attn_decode: in_dtype must be YR_F32 or YR_BF16");
-  return decode_impl("attn_decode", q, k_cache, v_cache, in_dtype, nullptr, nullptr, seqlens,
-                     q_pos, B, max_cache_len, Hq, Hkv, head_dim, inv_freq_f64, softmax_scale,
-                     window, sinks, out, out_dtype, lse, workspace, workspace_bytes, stream);
+  return decode_impl({"attn_decode", q, k_cache, v_cache, in_dtype, nullptr, nullptr, seqlens,
+                      q_pos, B, max_cache_len, Hq, Hkv, head_dim, inv_freq_f64, softmax_scale,
+                      window, sinks, out, out_dtype, lse, workspace, workspace_bytes, stream});
 }
 
 int attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
@@ -414,10 +439,10 @@ int attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
                     const double *inv_freq_f64, float softmax_scale, int window, int sinks,
                     void *out, int out_dtype, float *lse, void *workspace,
                     size_t workspace_bytes, void *stream) {
-  return decode_impl("attn_decode_fp8", q, k_cache, v_cache, YR_FP8_E4M3, k_scale, v_scale,
-                     seqlens, q_pos, B, max_cache_len, Hq, Hkv, head_dim, inv_freq_f64,
-                     softmax_scale, window, sinks, out, out_dtype, lse, workspace,
-                     workspace_bytes, stream);
+  return decode_impl({"attn_decode_fp8", q, k_cache, v_cache, YR_FP8_E4M3, k_scale, v_scale,
+                      seqlens, q_pos, B, max_cache_len, Hq, Hkv, head_dim, inv_freq_f64,
+                      softmax_scale, window, sinks, out, out_dtype, lse, workspace,
+                      workspace_bytes, stream});
 }
 
 int yr_read_device_error(const void *workspace, void *stream, int *flags) {

@@ -20,6 +20,7 @@
 #include "device_common.h"
 #include "yr_internal.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace yr {
@@ -1219,18 +1220,35 @@ int decode_heads_per_wg(int Hkv, int head_dim, bool fp8) {
   return heads_per_wg(Hkv, head_dim, fp8 ? 1 : 2);
 }
 
-int decode_stream_wgs() {
+namespace {
+constexpr int kMaxDevices = 64;
+
+// Device that owns `stream` (the current device for the null stream).
+hipError_t stream_device(hipStream_t stream, int *dev) {
+  hipDevice_t d = 0;
+  hipError_t e = stream != nullptr ? hipStreamGetDevice(stream, &d) : hipGetDevice(&d);
+  if (e != hipSuccess) return e;
+  if (d < 0 || d >= kMaxDevices) return hipErrorInvalidDevice;
+  *dev = (int)d;
+  return hipSuccess;
+}
+
+}  // namespace
+
+int decode_stream_wgs(hipStream_t stream) {
   // one workgroup per CU (the head-per-wave ring takes most of a CU's LDS);
-  // the CU count is read once per device
-  static int cached[64] = {0};
+  // the CU count is read once per device (a racing first call on two threads
+  // reads it twice and stores the same value)
+  static std::atomic<int> cached[kMaxDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  if (stream_device(stream, &dev) != hipSuccess) return 0;
+  const int c = cached[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     return 0;
   n = n < kDecodeStreamMaxWg ? n : kDecodeStreamMaxWg;
-  if (dev < 64) cached[dev] = n;
+  cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 

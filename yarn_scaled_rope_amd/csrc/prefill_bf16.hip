@@ -87,6 +87,67 @@ __device__ __forceinline__ void static_for(F &&f) {
   }
 }
 
+// Work item `item` of a packed ragged batch: (q-tile, sequence, query head).
+// In causal prefill the work of q-tile t grows with t in every sequence, so
+// the items run longest first: tile index from the top down, and at each
+// index every sequence that has a tile there and every query head.  Only
+// existing tiles are numbered (a short sequence leaves no idle workgroups
+// behind when a long one still has tiles), and the items of one tile index
+// are spread over the 8 XCDs (consecutive workgroups go to consecutive XCDs)
+// as runs of consecutive heads, so that the query heads of a KV head share
+// one L2.  Every wave of the workgroup computes the same answer: a binary
+// search over the tile index on S(t) = sum_b max(0, tiles_b - t), the number
+// of q-tiles at index t or above, with the sequences spread over the lanes.
+// Returns false for workgroups past the last item.
+__device__ __forceinline__ bool packed_item(const int *__restrict__ cu, int B, long long T,
+                                            int max_seqlen, int Hq, int ntiles, int item,
+                                            int *tile, int *bo, int *ho) {
+  const int lane = threadIdx.x & 63;
+  auto tiles_of = [&](int bb) {
+    long long s0;
+    int n;
+    seq_bounds(cu, bb, T, max_seqlen, &s0, &n);
+    return (n + kBQ - 1) / kBQ;
+  };
+  auto count_from = [&](int t) {
+    int acc = 0;
+    for (int bb = lane; bb < B; bb += 64) acc += max(0, tiles_of(bb) - t);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    return __builtin_amdgcn_readfirstlane(acc);
+  };
+  if ((long long)Hq * count_from(0) <= item) return false;
+  int lo = 0, hi = ntiles - 1;  // Hq * S(lo) > item throughout
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((long long)Hq * count_from(mid) > item) lo = mid; else hi = mid - 1;
+  }
+  const int above = count_from(lo + 1);
+  const int cnt = count_from(lo) - above;           // sequences with a tile at index lo
+  const long long first = (long long)Hq * above;    // items at higher tile indices
+  const int nt = cnt * Hq;
+  int j = (int)(item - first);
+  if (first % kXcds == 0 && nt % kXcds == 0) j = (j % kXcds) * (nt / kXcds) + j / kXcds;
+  int k = j / Hq;
+  *ho = j % Hq;
+  *tile = lo;
+  // the k-th sequence (in batch order) that has a tile at index lo
+  for (int base = 0; base < B; base += 64) {
+    const int bb = base + lane;
+    const bool has = bb < B && tiles_of(bb) > lo;
+    const unsigned long long m = __ballot(has);
+    const int c = __popcll(m);
+    if (k < c) {
+      const unsigned long long below = m & ((1ull << lane) - 1ull);
+      const unsigned long long w = __ballot(has && __popcll(below) == k);
+      *bo = base + __ffsll((long long)w) - 1;
+      return true;
+    }
+    k -= c;
+  }
+  return false;  // not reached: cnt > k
+}
+
 // EXT: keys from a cache with a prefix (chunked prefill) and / or a sliding
 // window with sinks; without it those are compiled out (plain causal).
 template <int D, bool OUT_F32, bool ROTATE_Q, bool EXT>
@@ -95,7 +156,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const uint16_t *__restrict__ v, const int *__restrict__ cu, int B, int max_seqlen,
     long long T, int Hq, int Hkv, const double *__restrict__ theta, float scale_log2,
     void *__restrict__ out, float *__restrict__ lse, int ntiles, int *flag, int kv_len,
-    const int *__restrict__ ctx, int window, int sinks) {
+    const int *__restrict__ ctx, int window, int sinks, int permuted) {
   constexpr int KSTEPS = D / 16;     // MFMA k-steps over the head dim
   constexpr int DBLK = D / 32;       // 32-row blocks of O^T
   constexpr int CH = D / 8;          // 16-byte chunks per row
@@ -155,12 +216,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     b = ranked_b;
     if (b >= B) return;
   } else {
-    const int per = B * Hq;
-    tile = ntiles - 1 - (int)(blockIdx.x / per);
-    int r = (int)(blockIdx.x % per);
-    if (per % kXcds == 0) r = (r % kXcds) * (per / kXcds) + r / kXcds;
-    b = r / Hq;
-    h = r % Hq;
+    const int nwg = (int)gridDim.x;
+    int item = (int)blockIdx.x;
+    if (permuted) item = (int)(((long long)(nwg - 1 - item) + nwg / 3) % nwg);
+    if (!packed_item(cu, B, T, max_seqlen, Hq, ntiles, item, &tile, &b, &h)) return;
   }
   const int hk = h / (Hq / Hkv);
   long long s0;
@@ -552,7 +611,8 @@ hipError_t launch_one(const PrefillArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_F32, ROT, EXT>), dim3((unsigned)blocks), dim3(kThreads),
                      0, s, (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                      a.cu_seqlens, a.B, a.max_seqlen, a.T, a.Hq, a.Hkv, a.theta, scale_log2, a.out,
-                     a.lse, ntiles, a.dev_flag, a.kv_cache_len, a.ctx_lens, a.window, a.sinks);
+                     a.lse, ntiles, a.dev_flag, a.kv_cache_len, a.ctx_lens, a.window, a.sinks,
+                     a.permuted_order);
   return hipGetLastError();
 }
 

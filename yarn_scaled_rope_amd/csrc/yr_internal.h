@@ -56,6 +56,7 @@ struct PrefillArgs {
   const int *ctx_lens;   // NULL = no cached prefix
   int window;            // 0 = plain causal
   int sinks;
+  int permuted_order;    // 1: workgroups take the work items in a permuted order
 };
 
 struct DecodeArgs {
@@ -145,8 +146,9 @@ inline bool decode_stream_form(int B, int max_cache_len, int Hkv, int head_dim, 
 inline bool decode_shared_form(bool fp8, bool win, bool stream) {
   return (win || fp8) && !stream;
 }
-// workgroups of the balanced split on the current device (its CU count)
-int decode_stream_wgs();
+// workgroups of the balanced split on the device of `stream` (its CU count,
+// at most kDecodeStreamMaxWg); 0 if the device cannot be queried
+int decode_stream_wgs(hipStream_t stream);
 inline int decode_nsplit(int max_cache_len, int chunk) {
   return (max_cache_len + chunk - 1) / chunk;
 }

@@ -296,6 +296,21 @@ def sample_rows(seq_lens, hq: int, hkv: int, n_random: int = 32, seed: int = 7,
     return out
 
 
+def tile_edge_rows(seq_lens, hq: int, hkv: int, group: int, tile: int = 256):
+    """(token, head) rows of one KV group: the first and last row of every
+    `tile`-row block of every sequence, for all query heads of the group."""
+    g = hq // hkv
+    out = []
+    start = 0
+    for n in seq_lens:
+        for r0 in range(0, n, tile):
+            for r in sorted({r0, min(n, r0 + tile) - 1}):
+                for h in range(group * g, (group + 1) * g):
+                    out.append((start + r, h))
+        start += n
+    return out
+
+
 # ------------------------------------------------------- algorithmic counts
 def prefill_causal_flops(seq_lens, hq: int, head_dim: int) -> int:
     """Algorithmic FLOPs of causal prefill: QK^T and PV (2 FLOP per
