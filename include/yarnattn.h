@@ -23,8 +23,9 @@
  *  - Layouts are dense row-major with the last dimension contiguous.
  *    Element types: YR_F32 (float) or YR_BF16 (bfloat16 bit patterns).
  *  - Thread safety: the library keeps no global state besides the per-thread
- *    error message and per-device constants it looks up once; concurrent
- *    calls are safe when their outputs and workspaces do not overlap.
+ *    error message, per-device constants it looks up once, and the fixed
+ *    scratch of attn_decode_noalloc; concurrent calls are safe when their
+ *    outputs and workspaces do not overlap (attn_decode_noalloc: see there).
  *
  * Sources are cited by page title and section ("Arch 03 -- Long Context"
  * slide deck; "Long-context models", blog.ecitis.org; "LLM context window
@@ -322,6 +323,32 @@ int attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
                     const double *inv_freq_f64, float softmax_scale, int window, int sinks,
                     void *out, int out_dtype, float *lse, void *workspace,
                     size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): same arguments and results as attn_decode, without the
+ * workspace.  The partials live in a fixed scratch array of the library,
+ * 32 MiB per device (one copy on every device the library runs on, held until
+ * the process ends); the call allocates nothing.
+ *
+ *   dev_error   device int or NULL: receives the device error word
+ *               (YR_DEVERR_SEQLENS / YR_DEVERR_QPOS bits, 0 when the lengths
+ *               are in range), written by the call's first workgroup
+ * Returns YR_ERR_WORKSPACE, launching nothing, when the split this call needs
+ * (the same one attn_decode picks for these sizes) takes more than the fixed
+ * scratch holds; attn_decode has no such limit.
+ * Every call on a device shares that device's scratch and leaves its
+ * contents behind: calls that may overlap on one device (other streams,
+ * other threads) race and must be serialised by the caller.  Calls on one
+ * stream are ordered and safe.
+ */
+int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                        int in_dtype, const int *seqlens, const int *q_pos, int B,
+                        int max_cache_len, int Hq, int Hkv, int head_dim,
+                        const double *inv_freq_f64, float softmax_scale, int window,
+                        int sinks, void *out, int out_dtype, float *lse, int *dev_error,
+                        void *stream);
 
 /*
  * yr_read_device_error -- synchronise `stream`, read the device error word of

@@ -224,6 +224,34 @@ def test_decode_fp8_rejects_before_launch(lib, kw, status):
     assert lib.yr_last_error()
 
 
+def decode_noalloc_call(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, in_dtype=ops.YR_BF16, seqlens=FAKE, qpos=None, B=2,
+             Lmax=1024, Hq=8, Hkv=2, D=128, theta=FAKE, scale=0.1, window=0, sinks=0, out=FAKE,
+             out_dtype=ops.YR_BF16, lse=FAKE, err=None, stream=None)
+    a.update(kw)
+    return lib.attn_decode_noalloc(a["q"], a["kc"], a["vc"], a["in_dtype"], a["seqlens"],
+                                   a["qpos"], a["B"], a["Lmax"], a["Hq"], a["Hkv"], a["D"],
+                                   a["theta"], a["scale"], a["window"], a["sinks"], a["out"],
+                                   a["out_dtype"], a["lse"], a["err"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=80), ops.YR_ERR_UNSUPPORTED),
+    (dict(in_dtype=ops.YR_FP8_E4M3), ops.YR_ERR_UNSUPPORTED),
+    (dict(Hq=8, Hkv=3), ops.YR_ERR_INVALID),
+    (dict(B=0), ops.YR_ERR_INVALID),
+    (dict(out=None), ops.YR_ERR_NULL),
+    (dict(seqlens=None), ops.YR_ERR_NULL),
+    (dict(window=1), ops.YR_ERR_INVALID),
+    # a split needing more than the fixed 32 MiB: 1024 sequences of 8192 keys,
+    # 32 query heads, 4 chunks each -> 131072 partial rows of 516 bytes
+    (dict(B=1024, Lmax=8192, Hq=32, Hkv=8), ops.YR_ERR_WORKSPACE),
+])
+def test_decode_noalloc_rejects_before_launch(lib, kw, status):
+    assert decode_noalloc_call(lib, **kw) == status
+    assert lib.yr_last_error()
+
+
 def test_rope_rejects_and_empty(lib):
     assert lib.rope_apply(FAKE, ops.YR_BF16, 4, 2, 7, FAKE, FAKE, None) == ops.YR_ERR_INVALID
     assert lib.rope_apply(FAKE, 9, 4, 2, 8, FAKE, FAKE, None) == ops.YR_ERR_UNSUPPORTED

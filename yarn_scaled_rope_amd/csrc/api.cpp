@@ -38,11 +38,14 @@ int fail_hip(hipError_t err, const char *where) {
 
 namespace {
 
-// attn_decode and attn_decode_fp8: validation, the choice of sweep form and
-// split, the workspace layout and the launch.  cache_dtype is the storage
-// type of the caches (q is YR_F32 with an fp32 cache, else YR_BF16).  The
-// workspace is checked against attn_decode_workspace_bytes, the bound for any
-// split of these sizes.
+// attn_decode, attn_decode_fp8 and attn_decode_noalloc: validation, the
+// choice of sweep form and split, the workspace layout and the launch.
+// cache_dtype is the storage type of the caches (q is YR_F32 with an fp32
+// cache, else YR_BF16).  The scratch memory comes either from the caller's
+// workspace (checked against attn_decode_workspace_bytes, the bound for any
+// split of these sizes) or, when fixed_scratch is set, from the library's
+// per-device scratch array, checked against the bytes this call's split
+// actually needs.
 struct DecodeCall {
   const char *fn;
   const void *q, *k_cache, *v_cache;
@@ -58,6 +61,8 @@ struct DecodeCall {
   float *lse;
   void *workspace;
   size_t workspace_bytes;
+  bool fixed_scratch;
+  int *dev_error;  // fixed_scratch: where the kernels write the device error word (or NULL)
   void *stream;
 };
 
@@ -90,11 +95,13 @@ int decode_impl(const DecodeCall &c) {
     return bad(YR_ERR_NULL, "q, caches, seqlens and out are required");
   if (cache_dtype == YR_FP8_E4M3 && (!c.k_scale || !c.v_scale))
     return bad(YR_ERR_NULL, "k_scale and v_scale are required");
-  if (!c.workspace) return bad(YR_ERR_NULL, "workspace is required");
-  if ((reinterpret_cast<uintptr_t>(c.workspace) & 255) != 0)
-    return bad(YR_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  const size_t need = attn_decode_workspace_bytes(B, max_cache_len, Hq, head_dim);
-  if (c.workspace_bytes < need) return bad(YR_ERR_WORKSPACE, "workspace too small");
+  if (!c.fixed_scratch) {
+    if (!c.workspace) return bad(YR_ERR_NULL, "workspace is required");
+    if ((reinterpret_cast<uintptr_t>(c.workspace) & 255) != 0)
+      return bad(YR_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    const size_t need = attn_decode_workspace_bytes(B, max_cache_len, Hq, head_dim);
+    if (c.workspace_bytes < need) return bad(YR_ERR_WORKSPACE, "workspace too small");
+  }
   hipStream_t stream = (hipStream_t)c.stream;
 
   // the matrix-core kernel launches one workgroup per group of KV heads, the
@@ -138,7 +145,20 @@ int decode_impl(const DecodeCall &c) {
   }
   const size_t o_bytes = align_up(rows * head_dim * 4, 256);
   char *ws = static_cast<char *>(c.workspace);
-  int *flag = flag_of(c.workspace);
+  int *flag = c.fixed_scratch ? c.dev_error : flag_of(c.workspace);
+  if (c.fixed_scratch) {
+    const size_t need = kHeader + o_bytes + align_up(rows * 4, 256);
+    if (need > kDecodeScratchBytes) {
+      std::snprintf(msg, sizeof msg,
+                    "%s: this call needs %zu bytes of scratch, more than the fixed %zu", c.fn,
+                    need, (size_t)kDecodeScratchBytes);
+      return fail(YR_ERR_WORKSPACE, msg);
+    }
+    void *p = nullptr;
+    const hipError_t e = decode_fixed_scratch(stream, &p);
+    if (e != hipSuccess) return fail_hip(e, c.fn);
+    ws = static_cast<char *>(p);
+  }
   DecodeArgs d{};
   d.q = c.q;
   d.k_cache = c.k_cache;
@@ -430,7 +450,8 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, int in_
     return fail(YR_ERR_UNSUPPORTED, "attn_decode: in_dtype must be YR_F32 or YR_BF16");
   return decode_impl({"attn_decode", q, k_cache, v_cache, in_dtype, nullptr, nullptr, seqlens,
                       q_pos, B, max_cache_len, Hq, Hkv, head_dim, inv_freq_f64, softmax_scale,
-                      window, sinks, out, out_dtype, lse, workspace, workspace_bytes, stream});
+                      window, sinks, out, out_dtype, lse, workspace, workspace_bytes, false,
+                      nullptr, stream});
 }
 
 int attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
@@ -442,7 +463,20 @@ int attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
   return decode_impl({"attn_decode_fp8", q, k_cache, v_cache, YR_FP8_E4M3, k_scale, v_scale,
                       seqlens, q_pos, B, max_cache_len, Hq, Hkv, head_dim, inv_freq_f64,
                       softmax_scale, window, sinks, out, out_dtype, lse, workspace,
-                      workspace_bytes, stream});
+                      workspace_bytes, false, nullptr, stream});
+}
+
+int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache, int in_dtype,
+                        const int *seqlens, const int *q_pos, int B, int max_cache_len, int Hq,
+                        int Hkv, int head_dim, const double *inv_freq_f64, float softmax_scale,
+                        int window, int sinks, void *out, int out_dtype, float *lse,
+                        int *dev_error, void *stream) {
+  if (in_dtype != YR_F32 && in_dtype != YR_BF16)
+    return fail(YR_ERR_UNSUPPORTED, "attn_decode_noalloc: in_dtype must be YR_F32 or YR_BF16");
+  return decode_impl({"attn_decode_noalloc", q, k_cache, v_cache, in_dtype, nullptr, nullptr,
+                      seqlens, q_pos, B, max_cache_len, Hq, Hkv, head_dim, inv_freq_f64,
+                      softmax_scale, window, sinks, out, out_dtype, lse, nullptr, 0, true,
+                      dev_error, stream});
 }
 
 int yr_read_device_error(const void *workspace, void *stream, int *flags) {

@@ -21,6 +21,7 @@
 #include "yr_internal.h"
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 namespace yr {
@@ -1233,6 +1234,10 @@ hipError_t stream_device(hipStream_t stream, int *dev) {
   return hipSuccess;
 }
 
+// Fixed scratch of attn_decode_noalloc (partials of the split sweep and the
+// merge).  The name is a host-side stand-in: host code uses the device
+// address that hipGetSymbolAddress returns for each device, never the name.
+__device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
 }  // namespace
 
 int decode_stream_wgs(hipStream_t stream) {
@@ -1250,6 +1255,35 @@ int decode_stream_wgs(hipStream_t stream) {
   n = n < kDecodeStreamMaxWg ? n : kDecodeStreamMaxWg;
   cached[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+hipError_t decode_fixed_scratch(hipStream_t stream, void **ptr) {
+  // looked up once per device, with that device current (each device holds
+  // its own copy of the array at its own address)
+  static std::atomic<void *> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = stream_device(stream, &dev);
+  if (e != hipSuccess) return e;
+  void *p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+      int cur = 0;
+      e = hipGetDevice(&cur);
+      if (e != hipSuccess) return e;
+      if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+      if (e != hipSuccess) return e;
+      if (e2 != hipSuccess) return e2;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 int decode_chunk(int B, int max_cache_len, int units, int min_chunk, int target) {

@@ -149,6 +149,12 @@ inline bool decode_shared_form(bool fp8, bool win, bool stream) {
 // workgroups of the balanced split on the device of `stream` (its CU count,
 // at most kDecodeStreamMaxWg); 0 if the device cannot be queried
 int decode_stream_wgs(hipStream_t stream);
+// Fixed scratch of attn_decode_noalloc: a file-scope device array of this
+// many bytes (one per device the library runs on, held until the process
+// ends).  decode_fixed_scratch() returns its address on the device of
+// `stream`, looked up once per device.
+constexpr size_t kDecodeScratchBytes = 32u << 20;
+hipError_t decode_fixed_scratch(hipStream_t stream, void **ptr);
 inline int decode_nsplit(int max_cache_len, int chunk) {
   return (max_cache_len + chunk - 1) / chunk;
 }

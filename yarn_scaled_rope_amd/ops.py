@@ -69,6 +69,8 @@ def _declare(lib):
         "attn_decode": (i, [vp, vp, vp, i, vp, vp, i, i, i, i, i, vp, f, i, i, vp, i, vp, vp, sz, vp]),
         "attn_decode_fp8": (i, [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, f, i, i, vp, i, vp, vp,
                                 sz, vp]),
+        "attn_decode_noalloc": (i, [vp, vp, vp, i, vp, vp, i, i, i, i, i, vp, f, i, i, vp, i, vp, vp,
+                                    vp]),
         "yr_read_device_error": (i, [vp, vp, vp]),
         "yr_status_string": (ctypes.c_char_p, [i]),
         "yr_last_error": (ctypes.c_char_p, []),
@@ -406,6 +408,33 @@ def attn_decode(q, k_cache, v_cache, seqlens, inv_freq_f64, softmax_scale: float
                            _ptr(q_pos), B, lmax, hq, hkv, D, _ptr(inv_freq_f64),
                            float(softmax_scale), int(window), int(sinks), _ptr(out), out_code,
                            _ptr(lse), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+    return out, lse
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, seqlens, inv_freq_f64, softmax_scale: float,
+                        out, lse=None, q_pos=None, dev_error=None, window: int = 0,
+                        sinks: int = 0, stream=None):
+    """attn_decode without a workspace: the library's fixed per-device scratch
+    holds the partials, and nothing is allocated (the caller passes `out`,
+    and `lse` if wanted).  Calls that may overlap on one device race on that
+    scratch.  Returns (out, lse)."""
+    _ndim(q, "q", 3)
+    in_code = _dtype_code(q)
+    if out is None:
+        raise YarnAttnError(YR_ERR_NULL, "out is required (nothing is allocated)")
+    out_code = _dtype_code(out)
+    _decode_checks(q, k_cache, v_cache, seqlens, q_pos, inv_freq_f64, out, out_code, lse, None,
+                   q.dtype)
+    if dev_error is not None:
+        _need(dev_error, "dev_error", torch.int32)
+        _on_device(dev_error=dev_error)
+    B, hq, D = q.shape
+    _, lmax, hkv, _ = k_cache.shape
+    lib = load_library()
+    _check(lib.attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), in_code, _ptr(seqlens),
+                                   _ptr(q_pos), B, lmax, hq, hkv, D, _ptr(inv_freq_f64),
+                                   float(softmax_scale), int(window), int(sinks), _ptr(out),
+                                   out_code, _ptr(lse), _ptr(dev_error), _stream(stream)))
     return out, lse
 
 
