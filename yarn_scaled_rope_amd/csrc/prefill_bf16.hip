@@ -28,8 +28,11 @@
 //     ahead, then issues the score MFMAs of tile j+1 and, independent of
 //     them, the softmax of tile j (VALU and transcendental work), then the PV
 //     MFMAs of tile j.  One barrier per step.
-//   * The running max is lazy: it moves only when a row max exceeds it by
-//     more than 2^8, so the O rescale is skipped on most tiles.
+//   * The running max is lazy: every exponent stays at most 2^8 against it,
+//     so the O rescale is skipped on most tiles.  Tiles that need no mask
+//     are exponentiated against the current reference straight away; a
+//     lane's tile sum bounds each of its P, so only a sum above 2^8 (rare)
+//     sends the wave through the row max and a second pass.
 //   * Tiles wholly above a wave's diagonal are skipped by that wave; masking
 //     runs only on tiles that cross the diagonal or the sequence end.
 //   * Workgroups run longest-first (q-tile index from the last tile down) and
@@ -395,7 +398,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   // lazy rescale of the running state; returns -m for the exp2 argument
   // nx: the scores of the next tile, already issued against the old -m_run,
   // which move to the new reference with this tile's
-  auto softmax_front = [&](int j, f32x16 (&s)[KB], f32x16 (&nx)[KB], bool may_mask) YR_INLINE -> float {
+  auto softmax_front = [&](int j, f32x16 (&s)[KB], f32x16 (&nx)[KB], bool may_mask,
+                           float thresh = 8.0f) YR_INLINE -> float {
     const int key0 = j * kBC;
     const bool wmask = window > 0 && key0 <= P + tw0 + 31 - window && key0 + kBC > sinks;
     if (may_mask && ((key0 + kBC - 1 > P + tw0) || (key0 + kBC > nk) || wmask)) {
@@ -420,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     // the tile's row max less m_run (the scores carry -m_run already)
     mx = half_max(mx);
     const bool first = m_run == -INFINITY;
-    const bool grow = first ? mx > -INFINITY : mx > 8.0f;  // lazy running max
+    const bool grow = first ? mx > -INFINITY : mx > thresh;  // lazy running max
     if (__any(grow)) {
       const float m_new = grow ? (first ? mx : m_run + mx) : m_run;
       // 0 when m_run = -inf; 1 for a row that has seen no visible key yet
@@ -515,12 +519,39 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   // first, right after the barrier, and the row max, exp / convert work of
   // tile i and its PV MFMAs follow (measured 1-1.5% faster than issuing the
   // scores after the row max).
+  // P = exp2(s - m) of a whole tile into bf16 fragments; returns the lane's
+  // sum of the tile's P (its 32 keys of its row)
+  auto exp_tile = [&](f32x16 (&s)[KB], bf16x8 (&pf)[KS]) YR_INLINE -> float {
+    float ts = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(s[ks >> 1][(ks & 1) * 8 + 2 * e]);
+        const float p1 = __builtin_amdgcn_exp2f(s[ks >> 1][(ks & 1) * 8 + 2 * e + 1]);
+        ts += p0 + p1;
+        w[e] = pack_bf16x2(p0, p1);
+      }
+      pf[ks] = as_bf16x8(w);
+    }
+    return ts;
+  };
   auto step_clear = [&](auto par, int i, f32x16 (&cur)[KB], f32x16 (&nxt)[KB]) YR_INLINE {
     stage(par, i);
     scores(nextp(par), nxt);
-    const float neg_m = softmax_front(tile_of(i), cur, nxt, false);
+    // Optimistic softmax: exponentiate against the current reference first.
+    // Every P of the tile is at most 2^8 when the lane's tile sum is (P >= 0),
+    // which is the lazy-max bound; only when a sum exceeds it (or is not a
+    // number, or the row has no reference yet) does the wave take the row
+    // max, move the reference to it and exponentiate again.
     bf16x8 pf[KS];
-    softmax_back(cur, neg_m, pf);
+    float ts = exp_tile(cur, pf);
+    if (__any(!(ts <= 256.f) || m_run == -INFINITY)) {
+      softmax_front(tile_of(i), cur, nxt, false, 0.f);
+      ts = exp_tile(cur, pf);
+    }
+    l_part += ts;
     pv(par, pf);
   };
 
