@@ -389,10 +389,64 @@ def bench_next(args, torch, ops, wl, pstate, dstate):
                        "inputs": "the decode line's cache, as E4M3 codes with per-KV-head "
                                  "scales amax/448"}}
         fp8_state = {"codes": codes, "scales": scales}
+    # many sequences: the balanced split over a 256-sequence batch
+    lb = wl.DECODE_B256
+    log(f"generating {lb.name} inputs")
+    linp = wl.make_decode(lb)
+
+    def upb(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    lq, lkc, lvc = upb(linp["q"]), upb(linp["k_cache"]), upb(linp["v_cache"])
+    lsl = torch.from_numpy(linp["seqlens"]).cuda()
+    _, lf64, lt = ops.yarn_rope_freqs(lb.head_dim, lb.base, lb.factor, lb.original_max_position)
+    lth = torch.from_numpy(lf64).cuda()
+    lws = torch.empty(ops.attn_decode_workspace_bytes(lb.batch, lb.max_cache_len, lb.hq,
+                                                      lb.head_dim), dtype=torch.uint8,
+                      device="cuda")
+    lout = torch.empty_like(lq)
+    log("large-batch decode timed")
+    lscale = lt / math.sqrt(lb.head_dim)
+    ms = _event_ms(torch, lambda: ops.attn_decode(lq, lkc, lvc, lsl, lth, lscale, out=lout,
+                                                  want_lse=False, workspace=lws, stream=stream),
+                   args.warmup, args.decode_steps, stream)
+    if ops.read_device_error(lws) != 0:
+        raise SystemExit("device range check failed (large-batch decode)")
+    nbytes = wl.decode_kv_bytes(linp["seqlens"], lb.hkv, lb.head_dim)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res["large_batch_decode"] = {
+        "metric": "decode KV GB/s", "value": round(gbs, 2), "unit": "GB/s",
+        "ms_per_call": round(ms, 4), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "bytes_per_launch": int(nbytes),
+        "config": {"workload": lb.name, "batch": lb.batch, "sum_seqlens": int(linp["seqlens"].sum()),
+                   "hq": lb.hq, "hkv": lb.hkv, "head_dim": lb.head_dim, "seed": 1000 + lb.index}}
+    del lkc, lvc
+    # keep the host copies of the 32 sequences the CPU baseline reads
+    linp["k_cache"] = np.array(linp["k_cache"][:32])
+    linp["v_cache"] = np.array(linp["v_cache"][:32])
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on bounded samples of the next rows")
         cpu_next(res, chunk_host, pstate, dstate, fp8_state if dstate is not None else None,
                  wl, torch, args.cpu_next_seconds)
+        from oracle import attention as oatt
+        from oracle import freqs as ofreqs
+        th = ofreqs.yarn_theta(lb.head_dim, lb.base, lb.factor, lb.original_max_position)
+        sc = ofreqs.softmax_scale(lb.head_dim, ofreqs.attention_temperature(lb.factor))
+        q64 = wl.as_f64(linp["q"][:32], "bf16")
+        kc64, vc64 = wl.as_f64(linp["k_cache"], "bf16"), wl.as_f64(linp["v_cache"], "bf16")
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            oatt.decode(q64, kc64, vc64, linp["seqlens"][:32], th, sc)
+            passes += 1
+            if time.perf_counter() - t0 >= args.cpu_next_seconds:
+                break
+        dt = time.perf_counter() - t0
+        nb = wl.decode_kv_bytes(linp["seqlens"][:32], lb.hkv, lb.head_dim) * passes
+        res["large_batch_decode"]["cpu_baseline"] = {
+            "value": round(nb / dt / 1e9, 3), "unit": "GB/s", "cores": int(oracle_threads()),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"fp64 decode of sequences 0-31 of the same {lb.name} inputs, "
+                      f"{passes} whole passes"}
     if dstate is not None:
         del codes, fp8_state
     # the roofline object of each row, in the main line's form (no counters
@@ -619,12 +673,14 @@ N_XCD = 8       # GRBM_GUI_ACTIVE counts once per XCD
 
 def summarize(dirnames: str, out_path: str, command: str):
     """Condense rocprofv3 CSV output under one or more directories (comma
-    separated) into a short text file: kernel statistics, the mean of every
-    counter per dispatch, and per kernel the derived figures the counters
-    allow -- matrix-core busy fraction SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x
-    GRBM_GUI_ACTIVE / XCDs), MFMA FLOPs SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
-    per dispatch, and with a kernel trace of the same command the shader
-    clock GRBM_GUI_ACTIVE / XCDs / duration and the MFMA rate."""
+    separated) into a short text file: kernel statistics, dispatch durations
+    by kernel and grid size (one kernel serves several workloads), the mean
+    of every counter per dispatch by kernel and grid size, and per kernel and
+    grid the figures the counters allow -- matrix-core busy fraction
+    SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM_GUI_ACTIVE / XCDs), MFMA FLOPs
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 per dispatch, and with a kernel trace
+    of the same dispatches the shader clock GRBM_GUI_ACTIVE / XCDs / duration
+    and the MFMA rate."""
     import csv
     dirs = [d for d in dirnames.split(",") if d]
     lines = ["# rocprofv3 summary", f"# command: {command}", ""]
@@ -635,44 +691,57 @@ def summarize(dirnames: str, out_path: str, command: str):
             lines.append(f"## kernel stats ({os.path.relpath(p, dirname)})")
             lines.append("name | calls | total_ns | avg_ns | min_ns | max_ns | pct")
             for r in rows:
-                name = r.get("Name", "")[:110]
-                durations[name] = float(r.get("AverageNs") or 0)
-                lines.append(f"{name} | {r.get('Calls')} | {r.get('TotalDurationNs')} | "
-                             f"{r.get('AverageNs')} | {r.get('MinNs')} | {r.get('MaxNs')} | "
-                             f"{r.get('Percentage')}")
+                lines.append(f"{r.get('Name', '')[:110]} | {r.get('Calls')} | "
+                             f"{r.get('TotalDurationNs')} | {r.get('AverageNs')} | {r.get('MinNs')} | "
+                             f"{r.get('MaxNs')} | {r.get('Percentage')}")
+            lines.append("")
+        for p in glob.glob(os.path.join(dirname, "**", "*kernel_trace.csv"), recursive=True):
+            groups = {}
+            for r in csv.DictReader(open(p)):
+                try:
+                    dur = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+                except (KeyError, ValueError):
+                    continue
+                key = (r.get("Kernel_Name", "")[:110], r.get("Grid_Size", r.get("Grid_Size_X", "")))
+                groups.setdefault(key, []).append(dur)
+            if not groups:
+                continue
+            lines.append(f"## dispatches by kernel and grid size ({os.path.relpath(p, dirname)})")
+            lines.append("name | grid size (threads) | calls | avg_ns | min_ns | max_ns")
+            for (name, grid), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+                durations[(name, grid)] = sum(d) / len(d)
+                lines.append(f"{name} | {grid} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.0f} | "
+                             f"{max(d):.0f}")
             lines.append("")
     derived = []
     for dirname in dirs:
         for p in glob.glob(os.path.join(dirname, "**", "*counter_collection.csv"), recursive=True):
-            rows = list(csv.DictReader(open(p)))
-            # sum the per-instance values of a counter within a dispatch first
             per = {}
-            for r in rows:
-                key = (r.get("Kernel_Name", "")[:110], r.get("Counter_Name", ""),
-                       r.get("Dispatch_Id", ""))
+            for r in csv.DictReader(open(p)):
+                key = (r.get("Kernel_Name", "")[:110], r.get("Grid_Size", ""),
+                       r.get("Counter_Name", ""), r.get("Dispatch_Id", ""))
                 per[key] = per.get(key, 0.0) + float(r.get("Counter_Value", 0) or 0)
             agg = {}
-            for (kname, cname, _), val in per.items():
-                agg.setdefault((kname, cname), []).append(val)
+            for (kname, grid, cname, _), val in per.items():
+                agg.setdefault((kname, grid, cname), []).append(val)
             lines.append(f"## counters ({os.path.relpath(p, dirname)}): mean per dispatch")
-            lines.append("kernel | counter | dispatches | mean | min | max")
-            for (kname, cname), vals in sorted(agg.items()):
-                lines.append(f"{kname} | {cname} | {len(vals)} | {sum(vals) / len(vals):.6g} | "
-                             f"{min(vals):.6g} | {max(vals):.6g}")
+            lines.append("kernel | grid size | counter | dispatches | mean | min | max")
+            for (kname, grid, cname), vals in sorted(agg.items()):
+                lines.append(f"{kname} | {grid} | {cname} | {len(vals)} | "
+                             f"{sum(vals) / len(vals):.6g} | {min(vals):.6g} | {max(vals):.6g}")
             lines.append("")
-            kernels = sorted({k for k, _ in agg})
-            for kname in kernels:
-                m = {c: sum(v) / len(v) for (k, c), v in agg.items() if k == kname}
+            for kname, grid in sorted({(k, g) for k, g, _ in agg}):
+                m = {c: sum(v) / len(v) for (k, g, c), v in agg.items() if k == kname and g == grid}
                 busy, gui = m.get("SQ_VALU_MFMA_BUSY_CYCLES"), m.get("GRBM_GUI_ACTIVE")
                 mops = m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
                 if not busy or not gui:
                     continue
                 cyc = gui / N_XCD
-                d = {"kernel": kname, "kernel_cycles": cyc,
+                d = {"kernel": kname, "grid": grid, "kernel_cycles": cyc,
                      "mfma_busy_frac": busy / (N_SIMD * cyc)}
                 if mops:
                     d["mfma_flops_per_dispatch"] = mops * 512
-                dur = durations.get(kname)
+                dur = durations.get((kname, grid))
                 if dur:
                     d["duration_ms"] = dur / 1e6
                     d["shader_clock_ghz"] = cyc / dur
@@ -684,18 +753,18 @@ def summarize(dirnames: str, out_path: str, command: str):
         lines.append("## matrix-core utilisation (derived, mean per dispatch)")
         lines.append(f"# busy frac = SQ_VALU_MFMA_BUSY_CYCLES / ({N_SIMD} SIMDs x GRBM_GUI_ACTIVE/"
                      f"{N_XCD}); FLOPs = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; clock = "
-                     f"GRBM_GUI_ACTIVE/{N_XCD} / kernel-trace duration; peak "
-                     f"{PEAK_BF16_TFLOPS} TFLOP/s")
-        lines.append("kernel | mfma busy | kernel cycles | MFMA FLOP/dispatch | duration ms | "
+                     f"GRBM_GUI_ACTIVE/{N_XCD} / kernel-trace duration of the same kernel and grid; "
+                     f"peak {PEAK_BF16_TFLOPS} TFLOP/s")
+        lines.append("kernel | grid | mfma busy | kernel cycles | MFMA FLOP/dispatch | duration ms | "
                      "clock GHz | MFMA TFLOP/s | frac of peak")
 
         def f(d, k, fmt):
             return format(d[k], fmt) if k in d else "-"
         for d in derived:
-            lines.append(f"{d['kernel']} | {d['mfma_busy_frac']:.3f} | {d['kernel_cycles']:.4g} | "
-                         f"{f(d, 'mfma_flops_per_dispatch', '.4g')} | {f(d, 'duration_ms', '.4f')} | "
-                         f"{f(d, 'shader_clock_ghz', '.3f')} | {f(d, 'mfma_tflops', '.1f')} | "
-                         f"{f(d, 'frac_of_peak', '.4f')}")
+            lines.append(f"{d['kernel']} | {d['grid']} | {d['mfma_busy_frac']:.3f} | "
+                         f"{d['kernel_cycles']:.4g} | {f(d, 'mfma_flops_per_dispatch', '.4g')} | "
+                         f"{f(d, 'duration_ms', '.4f')} | {f(d, 'shader_clock_ghz', '.3f')} | "
+                         f"{f(d, 'mfma_tflops', '.1f')} | {f(d, 'frac_of_peak', '.4f')}")
         lines.append("")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")

@@ -243,9 +243,9 @@ def decode_noalloc_call(lib, **kw):
     (dict(out=None), ops.YR_ERR_NULL),
     (dict(seqlens=None), ops.YR_ERR_NULL),
     (dict(window=1), ops.YR_ERR_INVALID),
-    # a split needing more than the fixed 32 MiB: 1024 sequences of 8192 keys,
-    # 32 query heads, 4 chunks each -> 131072 partial rows of 516 bytes
-    (dict(B=1024, Lmax=8192, Hq=32, Hkv=8), ops.YR_ERR_WORKSPACE),
+    # a split needing more than the fixed 32 MiB: 4096 sequences of at most
+    # 64 keys, 32 query heads, one chunk each -> 131072 partial rows of 516 bytes
+    (dict(B=4096, Lmax=64, Hq=32, Hkv=8), ops.YR_ERR_WORKSPACE),
 ])
 def test_decode_noalloc_rejects_before_launch(lib, kw, status):
     assert decode_noalloc_call(lib, **kw) == status

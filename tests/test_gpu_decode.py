@@ -107,6 +107,45 @@ def test_decode_balanced_split(hq, hkv, D, use_qpos):
     assert e_out <= BF16_TOL and e_lse <= BF16_TOL
 
 
+@pytest.mark.parametrize("B,lmax,hq,hkv,window,sinks", [
+    (300, 2048, 32, 8, 0, 0),      # two head groups per sequence
+    (1024, 600, 16, 4, 0, 0),      # one head group, many short sequences
+    (140, 4096, 32, 8, 4000, 4),   # windows that reach 512K visible keys in all
+])
+def test_decode_balanced_split_large_batch(B, lmax, hq, hkv, window, sinks):
+    """Batches of hundreds of sequences take the balanced split too (each
+    workgroup finds its first piece from chunk sums over its threads, the
+    merge its pieces the same way): lengths from 1 key up, with 1, 31, 32
+    and 33 among them, against the oracle in full."""
+    cfg = _cfg("bf16", hq, hkv, 128)
+    # every cache row drawn, then lengths of 1 .. lmax (rows past them NaN)
+    inp = wl.make_decode(cfg, seed=83 + B, batch=B, max_cache_len=lmax, min_cache_len=lmax)
+    lens = np.random.Generator(np.random.PCG64(84 + B)).integers(
+        1, lmax, size=B, endpoint=True).astype(np.int32)
+    lens[:4] = [1, 31, 32, 33]
+    lens[4] = lmax
+    for name in ("k_cache", "v_cache"):
+        for b in range(B):
+            inp[name][b, lens[b]:] = wl.BF16_NAN_BITS
+    inp["seqlens"] = lens
+    say(f"decode balanced split B={B} lmax={lmax} hq={hq} hkv={hkv} window={window} "
+        f"sum(L)={int(lens.sum())}")
+    th_dev, scale = lib_theta(128, cfg.base, cfg.factor, cfg.original_max_position)
+    out, lse = ops.attn_decode(to_dev(inp["q"], "bf16"), to_dev(inp["k_cache"], "bf16"),
+                               to_dev(inp["v_cache"], "bf16"), torch.from_numpy(lens).cuda(),
+                               th_dev, scale, out_dtype=ops.YR_F32, window=window, sinks=sinks)
+    torch.cuda.synchronize()
+    th, sc = oracle_theta(128, cfg.base, cfg.factor, cfg.original_max_position)
+    ro, rl = oatt.decode(wl.as_f64(inp["q"], "bf16"), LazyF64(inp["k_cache"], "bf16"),
+                         LazyF64(inp["v_cache"], "bf16"), lens, th, sc, window=window,
+                         sinks=sinks)
+    got, gl = to_f64(out), lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(gl))
+    e_out, e_lse = max_abs(got, ro), max_abs(gl, rl)
+    print(f"max-abs out {e_out:.3e} lse {e_lse:.3e}")
+    assert e_out <= BF16_TOL and e_lse <= BF16_TOL
+
+
 @pytest.mark.parametrize("window,sinks,lmax", [(4096, 4, 60000), (100, 0, 60000), (1, 3, 60000),
                                                (60000, 4, 70000), (70000, 2, 60000)])
 def test_decode_balanced_split_window(window, sinks, lmax):

@@ -67,14 +67,14 @@ def test_noalloc_flags_bad_seqlens_and_rejects_large_splits():
     ops.attn_decode_noalloc(d["q"], d["kc"], d["vc"], bad, th_dev, scale, out, dev_error=err)
     torch.cuda.synchronize()
     assert int(err.item()) == ops.YR_DEVERR_SEQLENS
-    # a split larger than the fixed scratch (1024 sequences of 8192 keys, 32
-    # query heads: 131072 partial rows) is refused before anything is read or
-    # launched, so the buffer pointers below are never dereferenced
+    # a split larger than the fixed scratch (4096 sequences of at most 64
+    # keys, 32 query heads: 131072 partial rows) is refused before anything is
+    # read or launched, so the buffer pointers below are never dereferenced
     import ctypes
     lib = ops.load_library()
     p = ctypes.c_void_p(d["q"].data_ptr())
     st = lib.attn_decode_noalloc(p, p, p, ops.YR_BF16, ctypes.c_void_p(d["sl"].data_ptr()), None,
-                                 1024, 8192, 32, 8, 128, ctypes.c_void_p(th_dev.data_ptr()), scale,
+                                 4096, 64, 32, 8, 128, ctypes.c_void_p(th_dev.data_ptr()), scale,
                                  0, 0, p, ops.YR_BF16, None, None, None)
     assert st == ops.YR_ERR_WORKSPACE
     assert b"fixed" in lib.yr_last_error()

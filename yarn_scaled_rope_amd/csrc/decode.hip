@@ -572,31 +572,69 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
     return (decode_visible_rows(bb, seqlens, qpos, Lmax, window, sinks) + kBlk - 1) / kBlk;
   };
   const int ngr = Hkv / HW;
-  int r = 0, r1 = 0;
+  // STREAM: [r, r1) is this workgroup's range; (bcur, basecur) the sequence
+  // that holds block r and the index of that sequence's first block.  Each
+  // thread sums the blocks of a contiguous chunk of sequences, a scan over
+  // the chunks (LDS) gives the total and each chunk's first block, and the
+  // thread whose chunk holds block r walks it to the sequence: O(B / threads)
+  // per workgroup, whatever the batch size.
+  long long r = 0, r1 = 0, basecur = 0;
+  int bcur = 0;
   if constexpr (STREAM) {
-    long long tb = 0;
-    for (int bb = 0; bb < B; ++bb) tb += (long long)ngr * nblocks_of(bb);
+    __shared__ int scan[NT];
+    __shared__ int first_b;
+    __shared__ long long first_base;
+    const int t = threadIdx.x;
+    const int cpt = (B + NT - 1) / NT;
+    const int bb0 = min(B, t * cpt), bb1 = min(B, bb0 + cpt);
+    int loc = 0;
+    for (int bb = bb0; bb < bb1; ++bb) loc += nblocks_of(bb);
+    scan[t] = loc;
+    __syncthreads();
+    for (int off = 1; off < NT; off <<= 1) {
+      const int v = t >= off ? scan[t - off] : 0;
+      __syncthreads();
+      scan[t] += v;
+      __syncthreads();
+    }
+    const long long tb = (long long)ngr * scan[NT - 1];
     const long long per = tb > 0 ? (tb + gridDim.x - 1) / gridDim.x : 1;
     const long long rs = (long long)blockIdx.x * per;
-    if (rs >= tb) return;
-    r = (int)rs;
-    r1 = (int)min(tb, rs + per);
+    if (rs >= tb) return;  // uniform: every thread read the same total
+    const long long before = (long long)ngr * (t > 0 ? scan[t - 1] : 0);
+    const long long after = (long long)ngr * scan[t];
+    if (rs >= before && rs < after) {
+      long long base = before;
+      int bb = bb0;
+      for (;; ++bb) {
+        const long long nb = (long long)ngr * nblocks_of(bb);
+        if (rs < base + nb) break;
+        base += nb;
+      }
+      first_b = bb;
+      first_base = base;
+    }
+    __syncthreads();
+    bcur = first_b;
+    basecur = first_base;
+    r = rs;
+    r1 = min(tb, rs + per);
   }
   for (;;) {  // STREAM: one pass per piece; otherwise a single pass
   int hg, split, b, c0, cnt = 0;
   if constexpr (STREAM) {
     // the segment (sequence b, head group hg) holding block r, and the piece
-    // of it in this range; split = index of this piece's partial
-    int base = 0, bb = 0, nbk = 0;
-    for (;; ++bb) {
-      nbk = nblocks_of(bb);
-      if (r < base + ngr * nbk) break;
-      base += ngr * nbk;
+    // of it in this range; split = index of this piece's partial.  Later
+    // pieces lie in later segments: step forward from the previous one.
+    int nbk = nblocks_of(bcur);
+    while (r >= basecur + (long long)ngr * nbk) {
+      basecur += (long long)ngr * nbk;
+      nbk = nblocks_of(++bcur);
     }
-    b = bb;
-    hg = (r - base) / nbk;
-    const int blk0 = (r - base) % nbk;
-    cnt = min(nbk - blk0, r1 - r);
+    b = bcur;
+    hg = (int)((r - basecur) / nbk);
+    const int blk0 = (int)((r - basecur) % nbk);
+    cnt = (int)min((long long)(nbk - blk0), r1 - r);
     c0 = blk0 * kBlk;
     split = (int)blockIdx.x + b * ngr + hg;
   } else if constexpr (SH) {
@@ -1041,12 +1079,32 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     auto nblocks_of = [&](int bb) {
       return (decode_visible_rows(bb, seqlens, qpos, Lmax, window, sinks) + kBlk - 1) / kBlk;
     };
-    long long tb = 0, base = 0;
-    for (int bb = 0; bb < B; ++bb) {
-      const long long n = (long long)ngr * nblocks_of(bb);
-      if (bb < b) base += n;
-      tb += n;
+    // blocks of the whole batch and of the sequences before b: strided
+    // sums over the threads, then the waves' sums through LDS
+    int all = 0, lt = 0;
+    for (int bb = threadIdx.x; bb < B; bb += 256) {
+      const int n = nblocks_of(bb);
+      all += n;
+      if (bb < b) lt += n;
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      all += __shfl_xor(all, off);
+      lt += __shfl_xor(lt, off);
+    }
+    __shared__ int red[2][MW];
+    if (lane == 0) {
+      red[0][wave] = all;
+      red[1][wave] = lt;
+    }
+    __syncthreads();
+    all = lt = 0;
+#pragma unroll
+    for (int w = 0; w < MW; ++w) {
+      all += red[0][w];
+      lt += red[1][w];
+    }
+    const long long tb = (long long)ngr * all, base = (long long)ngr * lt;
     const long long per = tb > 0 ? (tb + nwg - 1) / nwg : 1;
     const int nbk = nblocks_of(b);
     const long long s0 = base + (long long)hg * nbk;  // first block of the segment

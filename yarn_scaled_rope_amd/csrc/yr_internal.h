@@ -118,12 +118,13 @@ int decode_heads_per_wg(int Hkv, int head_dim, bool fp8);
 // workgroup) when the caches hold at least kDecodeStreamMinKeys keys in all:
 // the key blocks are cut evenly over one workgroup per CU (at most
 // kDecodeStreamMaxWg).
-// Every workgroup and every merge workgroup walks the B sequence lengths to
-// find its pieces, so the split is kept to batches of at most
-// kDecodeStreamMaxB sequences.
+// Workgroups find their pieces, and merge workgroups the pieces of their
+// query head, from sums of the B sequences' block counts spread over their
+// threads (O(B / threads) each); kDecodeStreamMaxB bounds the batch (and the
+// workspace the split needs, (workgroups + B) partials per head group).
 constexpr long long kDecodeStreamMinKeys = 512 * 1024;
 constexpr int kDecodeStreamMaxWg = 1024;
-constexpr int kDecodeStreamMaxB = 128;
+constexpr int kDecodeStreamMaxB = 16384;
 inline bool decode_stream_eligible(int B, int max_cache_len) {
   return B <= kDecodeStreamMaxB && (long long)B * max_cache_len >= kDecodeStreamMinKeys;
 }

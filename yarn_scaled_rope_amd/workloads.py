@@ -113,9 +113,14 @@ LLAMA2_7B_16K_SWA = PrefillConfig("llama2_7b_prefill_16k_window4k_sinks4", 6, (1
 DECODE_B16_SWA = DecodeConfig("decode_b16_gqa_window4k_sinks4", 7, 16, 131072, 32768, 32, 8,
                               128, "bf16", 500000.0, 8.0, 16384, window=4096, sinks=4)
 
+# Many sequences: 256 caches of 512 .. 4096 tokens (Llama-3-8B GQA layer),
+# a serving batch past the 128 sequences the balanced split used to stop at.
+DECODE_B256 = DecodeConfig("decode_b256_gqa_512_4k", 9, 256, 4096, 512, 32, 8, 128, "bf16",
+                           500000.0, 8.0, 16384)
+
 PREFILL_CONFIGS = {c.name: c for c in (TINY_F32, LLAMA2_7B_16K, LLAMA3_8B_128K,
                                        LLAMA3_70B_RAGGED, LLAMA2_7B_16K_SWA)}
-DECODE_CONFIGS = {c.name: c for c in (DECODE_B16, DECODE_B16_SWA)}
+DECODE_CONFIGS = {c.name: c for c in (DECODE_B16, DECODE_B16_SWA, DECODE_B256)}
 CHUNK_CONFIGS = {CHUNK_4X4K.name: CHUNK_4X4K}
 
 
