@@ -90,7 +90,8 @@ extern "C" {
  * gamma = (r_i - alpha) / (beta - alpha).  All arithmetic is fp64; the fp32
  * table is the round-to-nearest-even of the fp64 table.
  *
- *   head_dim               even, 2..1024 (rotary dim = head dim)
+ *   head_dim               even, 2..1024 (rotary dim = head dim); >= 4 for
+ *                          YR_ROPE_NTK (d/(d-2) is undefined at d = 2)
  *   base                   > 1
  *   factor                 s >= 1 (ignored by YR_ROPE_PLAIN)
  *   original_max_position  L >= 1 (YR_ROPE_YARN only)
@@ -116,7 +117,7 @@ int yarn_rope_freqs(int head_dim, double base, double factor,
  * is the plain one bit for bit.  The logit temperature stays 1 (only YaRN
  * rescales logits).  A caller re-derives the table when the sequence grows.
  *
- *   head_dim               even, 2..1024;  base > 1
+ *   head_dim               even, 4..1024;  base > 1
  *   seq_len                >= 0, the current sequence length
  *   original_max_position  L_train >= 1
  *   inv_freq_f32, inv_freq_f64   host tables of head_dim/2 entries or NULL

@@ -1,0 +1,104 @@
+"""Drive the host-only, sanitizer-instrumented build of the C ABI: every entry
+point with good and bad arguments (fake device pointers are never touched:
+validation and planning run, the stubbed launch reports no device), the
+frequency tables against the oracle, and the workspace queries.  Run by
+tests/test_host_sanitized.py in a child process with the sanitizer runtime
+preloaded; any sanitizer report aborts the process."""
+
+import ctypes
+import math
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+from oracle import freqs as ofreqs  # noqa: E402
+from yarn_scaled_rope_amd import ops  # noqa: E402
+
+
+def main(path):
+    lib = ops._declare(ctypes.CDLL(path))
+    F = ctypes.c_void_p(1 << 20)
+    n = 0
+    # frequency tables, every rule, against the oracle
+    for d, base, s, L in ((64, 1e4, 4.0, 64), (128, 1e4, 4.0, 4096), (128, 5e5, 8.0, 16384),
+                          (256, 1e6, 32.0, 32768), (2, 10.0, 1.0, 1), (1024, 5e5, 2.0, 100)):
+        for m, name in enumerate(("plain", "pi", "ntk", "yarn")):
+            if name == "ntk" and d < 4:
+                assert lib.yarn_rope_freqs(d, base, s, L, 1.0, 32.0, m, None, None, None) == \
+                    ops.YR_ERR_INVALID
+                continue
+            f32 = np.zeros(d // 2, np.float32)
+            f64 = np.zeros(d // 2, np.float64)
+            t = ctypes.c_double()
+            st = lib.yarn_rope_freqs(d, base, s, L, 1.0, 32.0, m, f32.ctypes.data_as(ctypes.c_void_p),
+                                     f64.ctypes.data_as(ctypes.c_void_p), ctypes.byref(t))
+            assert st == 0, st
+            assert np.array_equal(f32, ofreqs.to_fp32(ofreqs.theta_for(name, d, base, s, L)))
+            n += 1
+        st = lib.yarn_rope_dynamic_ntk_freqs(d, base, 3 * L, L, None, None, None)
+        assert st == (0 if d >= 4 else ops.YR_ERR_INVALID)
+    for bad in ((3, 1e4, 4.0, 64, 1.0, 32.0, 3), (64, 0.5, 4.0, 64, 1.0, 32.0, 3),
+                (64, 1e4, 0.5, 64, 1.0, 32.0, 3), (64, 1e4, 4.0, 64, 5.0, 2.0, 3),
+                (64, 1e4, math.nan, 64, 1.0, 32.0, 2), (64, 1e4, 4.0, 64, 1.0, 32.0, 9)):
+        assert lib.yarn_rope_freqs(*bad, None, None, None) == ops.YR_ERR_INVALID
+        n += 1
+    # prefill: bad arguments, then good ones that reach the (stubbed) launch
+    for kw in (dict(), dict(D=96), dict(Hq=6, Hkv=4), dict(B=0), dict(T=-1), dict(scale=0.0),
+               dict(q=None), dict(ws=None), dict(ws_bytes=10), dict(flags=8), dict(window=-1),
+               dict(flags=2), dict(flags=1, theta=None), dict(in_dtype=0, out_dtype=0)):
+        a = dict(q=F, k=F, v=F, in_dtype=1, cu=F, B=2, max_seqlen=100, T=150, Hq=8, Hkv=2, D=128,
+                 theta=F, flags=0, scale=0.1, window=0, sinks=0, out=F, out_dtype=1, lse=F, ws=F,
+                 ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        st = lib.attn_prefill_fwd(*a.values())
+        assert st != ops.YR_OK, (kw, st)
+        assert lib.yr_last_error()
+        n += 1
+    for kw in (dict(), dict(D=80), dict(max_seqlen=4096, Lmax=1024), dict(ctx=None), dict(window=7, sinks=2)):
+        a = dict(q=F, kc=F, vc=F, in_dtype=1, cu=F, ctx=F, B=2, max_seqlen=64, Tq=100, Lmax=1024, Hq=8,
+                 Hkv=2, D=128, theta=F, scale=0.1, window=0, sinks=0, out=F, out_dtype=1, lse=F, ws=F,
+                 ws_bytes=256, stream=None)
+        a.update(kw)
+        assert lib.attn_prefill_chunk(*a.values()) != ops.YR_OK
+        n += 1
+    # decode: every form of the plan (chunks, windows, balanced split, FP8,
+    # fp32), bad sizes, and the fixed-scratch variant
+    for kw in (dict(), dict(B=16, Lmax=131072), dict(B=300, Lmax=4096), dict(B=20000, Lmax=64),
+               dict(window=4096, sinks=4, B=16, Lmax=131072), dict(in_dtype=0, out_dtype=0),
+               dict(D=64, Hq=64, Hkv=8), dict(Hq=128, Hkv=2), dict(window=1), dict(ws_bytes=100),
+               dict(seqlens=None), dict(B=1 << 20, Lmax=1 << 20)):
+        a = dict(q=F, kc=F, vc=F, in_dtype=1, seqlens=F, qpos=None, B=3, Lmax=1000, Hq=32, Hkv=8,
+                 D=128, theta=F, scale=0.1, window=0, sinks=0, out=F, out_dtype=1, lse=F, ws=F,
+                 ws_bytes=1 << 40, stream=None)
+        a.update(kw)
+        st = lib.attn_decode(*a.values())
+        assert st != ops.YR_OK
+        st8 = lib.attn_decode_fp8(a["q"], a["kc"], a["vc"], F, F, a["seqlens"], None, a["B"],
+                                  a["Lmax"], a["Hq"], a["Hkv"], a["D"], F, 0.1, a["window"],
+                                  a["sinks"], F, 1, F, F, a["ws_bytes"], None)
+        assert st8 != ops.YR_OK
+        stn = lib.attn_decode_noalloc(a["q"], a["kc"], a["vc"], a["in_dtype"], a["seqlens"], None,
+                                      a["B"], a["Lmax"], a["Hq"], a["Hkv"], a["D"], F, 0.1,
+                                      a["window"], a["sinks"], F, a["out_dtype"], F, None, None)
+        assert stn != ops.YR_OK
+        n += 3
+    for B, L, hq, d in ((1, 1, 1, 64), (16, 131072, 32, 128), (300, 4096, 32, 128), (1, 1 << 24, 64, 128)):
+        assert lib.attn_decode_workspace_bytes(B, L, hq, d) >= 256
+        assert lib.attn_prefill_workspace_bytes(B * L, hq, d, 1) >= 256
+    # rope
+    assert lib.rope_apply(F, 1, 10, 2, 8, F, F, None) == ops.YR_ERR_HIP
+    assert lib.rope_apply_packed(F, F, 1, F, 2, 8, 10, 2, 8, F, None, None) == ops.YR_ERR_HIP
+    assert lib.rope_apply(F, 1, 10, 2, 7, F, F, None) == ops.YR_ERR_INVALID
+    flags = ctypes.c_int(0)
+    assert lib.yr_read_device_error(F, None, ctypes.byref(flags)) == ops.YR_ERR_HIP
+    for st in range(-1, 8):
+        assert lib.yr_status_string(st)
+    print(f"host ABI calls under the sanitizers: {n} groups, no report")
+
+
+if __name__ == "__main__":
+    main(sys.argv[1])

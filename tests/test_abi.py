@@ -83,6 +83,7 @@ def test_freqs_s1_is_plain_bitwise(lib):
     (64, 10000.0, 4.0, 0, 1.0, 32.0, "yarn"),        # L < 1
     (64, 10000.0, 4.0, 64, 32.0, 32.0, "yarn"),      # alpha >= beta
     (64, 10000.0, float("nan"), 64, 1.0, 32.0, "ntk"),
+    (2, 10000.0, 4.0, 64, 1.0, 32.0, "ntk"),         # d/(d-2) undefined at d = 2
 ])
 def test_freqs_rejects(lib, args):
     with pytest.raises(ops.YarnAttnError) as e:

@@ -31,8 +31,6 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 8;  // keys per lane group per iteration (loads in flight)
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int kMfmaStages = 2;  // LDS stages per wave, matrix-core kernel
-constexpr int kMfmaLdsBudget = 128 * 1024;  // ring bytes per workgroup
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -345,7 +343,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define YR_LDS __attribute__((address_space(3)))
 
-constexpr int kBlk = 32;  // keys per block (the MFMA row count)
 
 // V chunk swizzle by key row mod 4: bits 1-2 distinct (conflict-free for 16
 // lanes on 32 banks) and, with 16 chunks per row, bits 2-3 distinct too
@@ -394,16 +391,6 @@ struct MfmaSmem {
   float cs[D / 2], sn[D / 2];        // cos / sin of the query position
 };
 
-// Ring bytes of a workgroup of W waves (one KV head each).
-constexpr int mfma_ring_bytes(int W, int D, int EB) { return W * kMfmaStages * 2 * kBlk * D * EB; }
-// KV heads per workgroup of the head-per-wave form: the largest of 8, 4, 2,
-// 1 that divides Hkv and keeps the ring within the budget (head_dim 128: 4
-// with a bf16 cache, 8 with FP8).
-constexpr int heads_per_wg(int Hkv, int D, int EB) {
-  return (Hkv % 8 == 0 && mfma_ring_bytes(8, D, EB) <= kMfmaLdsBudget) ? 8
-         : (Hkv % 4 == 0 && mfma_ring_bytes(4, D, EB) <= kMfmaLdsBudget) ? 4
-         : Hkv % 2 == 0 ? 2 : 1;
-}
 
 // s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
 template <int N>
@@ -1275,10 +1262,6 @@ hipError_t launch_merge(const DecodeArgs &a, hipStream_t s) {
 
 }  // namespace
 
-int decode_heads_per_wg(int Hkv, int head_dim, bool fp8) {
-  return heads_per_wg(Hkv, head_dim, fp8 ? 1 : 2);
-}
-
 namespace {
 constexpr int kMaxDevices = 64;
 
@@ -1342,16 +1325,6 @@ hipError_t decode_fixed_scratch(hipStream_t stream, void **ptr) {
   }
   *ptr = p;
   return hipSuccess;
-}
-
-int decode_chunk(int B, int max_cache_len, int units, int min_chunk, int target) {
-  // At least `target` workgroups (several per CU); chunks are powers of two,
-  // at most 2048 keys so that a workgroup's start-up and combine stay small
-  // next to its sweep, and at least min_chunk.
-  int chunk = 2048;
-  while (chunk > min_chunk && (long long)B * units * decode_nsplit(max_cache_len, chunk) < target)
-    chunk >>= 1;
-  return chunk;
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {

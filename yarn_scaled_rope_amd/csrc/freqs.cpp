@@ -38,6 +38,9 @@ extern "C" int yarn_rope_freqs(int head_dim, double base, double factor,
   if (method != YR_ROPE_PLAIN && method != YR_ROPE_PI && method != YR_ROPE_NTK &&
       method != YR_ROPE_YARN)
     return yr::fail(YR_ERR_INVALID, "yarn_rope_freqs: unknown method");
+  if (method == YR_ROPE_NTK && head_dim < 4)
+    return yr::fail(YR_ERR_INVALID, "yarn_rope_freqs: NTK-aware scaling needs head_dim >= 4 "
+                                    "(the base is raised to s^(d/(d-2)))");
   if (method != YR_ROPE_PLAIN && (!std::isfinite(factor) || !(factor >= 1.0)))
     return yr::fail(YR_ERR_INVALID, "yarn_rope_freqs: factor s must be finite and >= 1");
   if (method == YR_ROPE_YARN) {

@@ -99,6 +99,21 @@ hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 
+// Matrix-core decode geometry shared by the kernels and the host plan.
+constexpr int kBlk = 32;                    // keys per block (the MFMA row count)
+constexpr int kMfmaStages = 2;              // LDS stages per wave
+constexpr int kMfmaLdsBudget = 128 * 1024;  // ring bytes per workgroup
+// Ring bytes of a workgroup of W waves (one KV head each).
+constexpr int mfma_ring_bytes(int W, int D, int EB) { return W * kMfmaStages * 2 * kBlk * D * EB; }
+// KV heads per workgroup of the head-per-wave form: the largest of 8, 4, 2,
+// 1 that divides Hkv and keeps the ring within the budget (head_dim 128: 4
+// with a bf16 cache, 8 with FP8).
+constexpr int heads_per_wg(int Hkv, int D, int EB) {
+  return (Hkv % 8 == 0 && mfma_ring_bytes(8, D, EB) <= kMfmaLdsBudget) ? 8
+         : (Hkv % 4 == 0 && mfma_ring_bytes(4, D, EB) <= kMfmaLdsBudget) ? 4
+         : Hkv % 2 == 0 ? 2 : 1;
+}
+
 // Decode split geometry: keys per chunk and number of chunks for a cache
 // length bound, with `units` workgroups per (sequence, chunk).  Pure function
 // of its arguments so that workspace sizing and the launch agree.
