@@ -267,77 +267,86 @@ def _event_ms(torch, fn, warmup: int, steps: int, stream) -> float:
 
 def bench_next(args, torch, ops, wl, pstate, dstate):
     """Chunked prefill (4 chunks of 4096 tokens after 28K..124K cached
-    tokens), and a 4096-token window with 4 sinks on the prefill and decode
-    inputs already resident.  Each line: algorithmic work / mean call time."""
+    tokens), a 4096-token window with 4 sinks on the prefill and decode
+    inputs already resident, FP8-cache decode and a 256-sequence decode.
+    Each line: algorithmic work / mean call time.  --only-next restricts the
+    rows (for profiling one of them)."""
     import numpy as np
     stream = torch.cuda.current_stream()
     res = {}
+    only = set(args.only_next.split(",")) if args.only_next else None
 
-    cfg = wl.CHUNK_4X4K
-    D = cfg.head_dim
-    _, f64, t = ops.yarn_rope_freqs(D, cfg.base, cfg.factor, cfg.original_max_position)
-    theta = torch.from_numpy(f64).cuda()
-    scale = t / math.sqrt(D)
-    log(f"generating {cfg.name} inputs")
-    inp = wl.make_chunk(cfg)
+    def want(row):
+        return only is None or row in only
 
-    def up(a):
-        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    if want("chunked_prefill"):
+        cfg = wl.CHUNK_4X4K
+        D = cfg.head_dim
+        _, f64, t = ops.yarn_rope_freqs(D, cfg.base, cfg.factor, cfg.original_max_position)
+        theta = torch.from_numpy(f64).cuda()
+        scale = t / math.sqrt(D)
+        log(f"generating {cfg.name} inputs")
+        inp = wl.make_chunk(cfg)
 
-    # host copy of sequence 0 (its cached rows and new tokens) for the oracle
-    # sample, before the full caches are dropped
-    n0, ctx0 = int(cfg.chunk_lens[0]), int(cfg.ctx_lens[0])
-    chunk_host = {"q": np.array(inp["q"][:n0]), "k": np.array(inp["k_cache"][0:1, :ctx0 + n0]),
-                  "v": np.array(inp["v_cache"][0:1, :ctx0 + n0]), "n": n0, "ctx": ctx0}
-    q, kc = up(inp["q"]), up(inp["k_cache"])
-    del inp["k_cache"]
-    vc = up(inp["v_cache"])
-    del inp["v_cache"]
-    cu = torch.from_numpy(inp["cu_seqlens_q"]).cuda()
-    ctx = torch.from_numpy(inp["ctx_lens"]).cuda()
-    out = torch.empty((q.shape[0], cfg.hq, D), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((cfg.hq, q.shape[0]), dtype=torch.float32, device="cuda")
-    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
-    nq = max(cfg.chunk_lens)
-    log("chunked prefill timed")
-    ms = _event_ms(torch, lambda: ops.attn_prefill_chunk(q, kc, vc, cu, ctx, nq, theta, scale,
-                                                         out=out, lse=lse, workspace=ws,
-                                                         stream=stream),
-                   args.warmup, max(5, args.steps // 2), stream)
-    if ops.read_device_error(ws) != 0:
-        raise SystemExit("device range check failed (chunked prefill)")
-    flops = wl.prefill_visible_flops(cfg.chunk_lens, cfg.hq, D, ctx_lens=cfg.ctx_lens)
-    tf = flops / (ms * 1e-3) / 1e12
-    res["chunked_prefill"] = {
-        "metric": "chunked prefill TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
-        "ms_per_call": round(ms, 4), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-        "flops_per_launch": flops,
-        "config": {"workload": cfg.name, "ctx_lens": list(cfg.ctx_lens),
-                   "chunk_lens": list(cfg.chunk_lens), "max_cache_len": cfg.max_cache_len,
-                   "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": D, "seed": 1000 + cfg.index}}
-    del q, kc, vc, out, lse
+        def up(a):
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
 
-    pc = wl.LLAMA2_7B_16K_SWA
-    p = pstate
-    out = torch.empty_like(p["q"])
-    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
-    log("windowed prefill timed")
-    ms = _event_ms(torch, lambda: ops.attn_prefill_fwd(p["q"], p["krot"], p["v"], p["cu"],
-                                                       p["maxlen"], p["theta"], p["scale"],
-                                                       out=out, want_lse=False, workspace=ws,
-                                                       k_rotated=True, window=pc.window,
-                                                       sinks=pc.sinks, stream=stream),
-                   args.warmup, args.steps, stream)
-    flops = wl.prefill_visible_flops(pc.seq_lens, pc.hq, pc.head_dim, pc.window, pc.sinks)
-    tf = flops / (ms * 1e-3) / 1e12
-    res["window_prefill"] = {
-        "metric": "windowed prefill TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
-        "ms_per_call": round(ms, 4), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-        "flops_per_launch": flops,
-        "config": {"workload": pc.name, "inputs": "those of the prefill line",
-                   "window": pc.window, "sinks": pc.sinks}}
+        # host copy of sequence 0 (its cached rows and new tokens) for the oracle
+        # sample, before the full caches are dropped
+        n0, ctx0 = int(cfg.chunk_lens[0]), int(cfg.ctx_lens[0])
+        chunk_host = {"q": np.array(inp["q"][:n0]), "k": np.array(inp["k_cache"][0:1, :ctx0 + n0]),
+                      "v": np.array(inp["v_cache"][0:1, :ctx0 + n0]), "n": n0, "ctx": ctx0}
+        q, kc = up(inp["q"]), up(inp["k_cache"])
+        del inp["k_cache"]
+        vc = up(inp["v_cache"])
+        del inp["v_cache"]
+        cu = torch.from_numpy(inp["cu_seqlens_q"]).cuda()
+        ctx = torch.from_numpy(inp["ctx_lens"]).cuda()
+        out = torch.empty((q.shape[0], cfg.hq, D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((cfg.hq, q.shape[0]), dtype=torch.float32, device="cuda")
+        ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+        nq = max(cfg.chunk_lens)
+        log("chunked prefill timed")
+        ms = _event_ms(torch, lambda: ops.attn_prefill_chunk(q, kc, vc, cu, ctx, nq, theta, scale,
+                                                             out=out, lse=lse, workspace=ws,
+                                                             stream=stream),
+                       args.warmup, max(5, args.steps // 2), stream)
+        if ops.read_device_error(ws) != 0:
+            raise SystemExit("device range check failed (chunked prefill)")
+        flops = wl.prefill_visible_flops(cfg.chunk_lens, cfg.hq, D, ctx_lens=cfg.ctx_lens)
+        tf = flops / (ms * 1e-3) / 1e12
+        res["chunked_prefill"] = {
+            "metric": "chunked prefill TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
+            "ms_per_call": round(ms, 4), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "flops_per_launch": flops,
+            "config": {"workload": cfg.name, "ctx_lens": list(cfg.ctx_lens),
+                       "chunk_lens": list(cfg.chunk_lens), "max_cache_len": cfg.max_cache_len,
+                       "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": D, "seed": 1000 + cfg.index}}
+        del q, kc, vc, out, lse
 
-    if dstate is not None:
+    if want("window_prefill"):
+        pc = wl.LLAMA2_7B_16K_SWA
+        p = pstate
+        out = torch.empty_like(p["q"])
+        ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+        log("windowed prefill timed")
+        ms = _event_ms(torch, lambda: ops.attn_prefill_fwd(p["q"], p["krot"], p["v"], p["cu"],
+                                                           p["maxlen"], p["theta"], p["scale"],
+                                                           out=out, want_lse=False, workspace=ws,
+                                                           k_rotated=True, window=pc.window,
+                                                           sinks=pc.sinks, stream=stream),
+                       args.warmup, args.steps, stream)
+        flops = wl.prefill_visible_flops(pc.seq_lens, pc.hq, pc.head_dim, pc.window, pc.sinks)
+        tf = flops / (ms * 1e-3) / 1e12
+        res["window_prefill"] = {
+            "metric": "windowed prefill TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
+            "ms_per_call": round(ms, 4), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "flops_per_launch": flops,
+            "config": {"workload": pc.name, "inputs": "those of the prefill line",
+                       "window": pc.window, "sinks": pc.sinks}}
+
+    fp8_state = None
+    if dstate is not None and (want("window_decode") or want("fp8_decode")):
         dc = wl.DECODE_B16_SWA
         d = dstate
         out = torch.empty_like(d["q"])
@@ -389,45 +398,45 @@ def bench_next(args, torch, ops, wl, pstate, dstate):
                        "inputs": "the decode line's cache, as E4M3 codes with per-KV-head "
                                  "scales amax/448"}}
         fp8_state = {"codes": codes, "scales": scales}
-    # many sequences: the balanced split over a 256-sequence batch
-    lb = wl.DECODE_B256
-    log(f"generating {lb.name} inputs")
-    linp = wl.make_decode(lb)
+    if want("large_batch_decode"):
+        # many sequences: the balanced split over a 256-sequence batch
+        lb = wl.DECODE_B256
+        log(f"generating {lb.name} inputs")
+        linp = wl.make_decode(lb)
 
-    def upb(a):
-        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        def upb(a):
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
 
-    lq, lkc, lvc = upb(linp["q"]), upb(linp["k_cache"]), upb(linp["v_cache"])
-    lsl = torch.from_numpy(linp["seqlens"]).cuda()
-    _, lf64, lt = ops.yarn_rope_freqs(lb.head_dim, lb.base, lb.factor, lb.original_max_position)
-    lth = torch.from_numpy(lf64).cuda()
-    lws = torch.empty(ops.attn_decode_workspace_bytes(lb.batch, lb.max_cache_len, lb.hq,
-                                                      lb.head_dim), dtype=torch.uint8,
-                      device="cuda")
-    lout = torch.empty_like(lq)
-    log("large-batch decode timed")
-    lscale = lt / math.sqrt(lb.head_dim)
-    ms = _event_ms(torch, lambda: ops.attn_decode(lq, lkc, lvc, lsl, lth, lscale, out=lout,
-                                                  want_lse=False, workspace=lws, stream=stream),
-                   args.warmup, args.decode_steps, stream)
-    if ops.read_device_error(lws) != 0:
-        raise SystemExit("device range check failed (large-batch decode)")
-    nbytes = wl.decode_kv_bytes(linp["seqlens"], lb.hkv, lb.head_dim)
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    res["large_batch_decode"] = {
-        "metric": "decode KV GB/s", "value": round(gbs, 2), "unit": "GB/s",
-        "ms_per_call": round(ms, 4), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-        "bytes_per_launch": int(nbytes),
-        "config": {"workload": lb.name, "batch": lb.batch, "sum_seqlens": int(linp["seqlens"].sum()),
-                   "hq": lb.hq, "hkv": lb.hkv, "head_dim": lb.head_dim, "seed": 1000 + lb.index}}
-    del lkc, lvc
-    # keep the host copies of the 32 sequences the CPU baseline reads
-    linp["k_cache"] = np.array(linp["k_cache"][:32])
-    linp["v_cache"] = np.array(linp["v_cache"][:32])
-    if not args.no_cpu_baseline:
+        lq, lkc, lvc = upb(linp["q"]), upb(linp["k_cache"]), upb(linp["v_cache"])
+        lsl = torch.from_numpy(linp["seqlens"]).cuda()
+        _, lf64, lt = ops.yarn_rope_freqs(lb.head_dim, lb.base, lb.factor, lb.original_max_position)
+        lth = torch.from_numpy(lf64).cuda()
+        lws = torch.empty(ops.attn_decode_workspace_bytes(lb.batch, lb.max_cache_len, lb.hq,
+                                                          lb.head_dim), dtype=torch.uint8,
+                          device="cuda")
+        lout = torch.empty_like(lq)
+        log("large-batch decode timed")
+        lscale = lt / math.sqrt(lb.head_dim)
+        ms = _event_ms(torch, lambda: ops.attn_decode(lq, lkc, lvc, lsl, lth, lscale, out=lout,
+                                                      want_lse=False, workspace=lws, stream=stream),
+                       args.warmup, args.decode_steps, stream)
+        if ops.read_device_error(lws) != 0:
+            raise SystemExit("device range check failed (large-batch decode)")
+        nbytes = wl.decode_kv_bytes(linp["seqlens"], lb.hkv, lb.head_dim)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res["large_batch_decode"] = {
+            "metric": "decode KV GB/s", "value": round(gbs, 2), "unit": "GB/s",
+            "ms_per_call": round(ms, 4), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "bytes_per_launch": int(nbytes),
+            "config": {"workload": lb.name, "batch": lb.batch, "sum_seqlens": int(linp["seqlens"].sum()),
+                       "hq": lb.hq, "hkv": lb.hkv, "head_dim": lb.head_dim, "seed": 1000 + lb.index}}
+        del lkc, lvc
+        # keep the host copies of the 32 sequences the CPU baseline reads
+        linp["k_cache"] = np.array(linp["k_cache"][:32])
+        linp["v_cache"] = np.array(linp["v_cache"][:32])
+    if not args.no_cpu_baseline and only is None:
         log("timing the fp64 CPU oracle on bounded samples of the next rows")
-        cpu_next(res, chunk_host, pstate, dstate, fp8_state if dstate is not None else None,
-                 wl, torch, args.cpu_next_seconds)
+        cpu_next(res, chunk_host, pstate, dstate, fp8_state, wl, torch, args.cpu_next_seconds)
         from oracle import attention as oatt
         from oracle import freqs as ofreqs
         th = ofreqs.yarn_theta(lb.head_dim, lb.base, lb.factor, lb.original_max_position)
@@ -447,8 +456,7 @@ def bench_next(args, torch, ops, wl, pstate, dstate):
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"fp64 decode of sequences 0-31 of the same {lb.name} inputs, "
                       f"{passes} whole passes"}
-    if dstate is not None:
-        del codes, fp8_state
+    del fp8_state
     # the roofline object of each row, in the main line's form (no counters
     # are taken for these paths: traffic null)
     for row in res.values():
@@ -846,6 +854,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true")
+    ap.add_argument("--only-next", default=None,
+                    help="comma-separated next rows to run (chunked_prefill, window_prefill, "
+                         "window_decode, fp8_decode, large_batch_decode); default all")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cpu-next-seconds", type=float, default=3.0)
     ap.add_argument("--copy-probe", action="store_true")

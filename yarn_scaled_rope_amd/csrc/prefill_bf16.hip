@@ -394,27 +394,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     }
   };
 
-  // softmax front half of tile j: mask (diagonal/tail tiles only), row max,
-  // lazy rescale of the running state; returns -m for the exp2 argument
-  // nx: the scores of the next tile, already issued against the old -m_run,
-  // which move to the new reference with this tile's
-  auto softmax_front = [&](int j, f32x16 (&s)[KB], f32x16 (&nx)[KB], bool may_mask,
-                           float thresh = 8.0f) YR_INLINE -> float {
-    const int key0 = j * kBC;
-    const bool wmask = window > 0 && key0 <= P + tw0 + 31 - window && key0 + kBC > sinks;
-    if (may_mask && ((key0 + kBC - 1 > P + tw0) || (key0 + kBC > nk) || wmask)) {
-      const int pos = P + tq;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int key = key0 + kb * 32 + (rr >> 2) * 8 + hh * 4 + (rr & 3);
-          const bool hide = key > pos || key >= nk ||
-                            (window > 0 && key <= pos - window && key >= sinks);
-          if (hide) s[kb][rr] = -INFINITY;
-        }
-      }
-    }
+  // Slow path of the softmax (a tile sum above 2^8, or a row without a
+  // reference yet): move each row's reference to its running maximum, so that
+  // the tile's P are at most 1 afterwards.  The tile's scores and the
+  // already issued scores of the next tile (nx, computed against the old
+  // reference) shift with it, and O and the row sum are rescaled.  A row that
+  // has seen no visible key keeps -inf (alpha 1).
+  auto move_reference = [&](f32x16 (&s)[KB], f32x16 (&nx)[KB]) YR_INLINE {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -424,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     // the tile's row max less m_run (the scores carry -m_run already)
     mx = half_max(mx);
     const bool first = m_run == -INFINITY;
-    const bool grow = first ? mx > -INFINITY : mx > thresh;  // lazy running max
+    const bool grow = first ? mx > -INFINITY : mx > 0.f;
     if (__any(grow)) {
       const float m_new = grow ? (first ? mx : m_run + mx) : m_run;
       // 0 when m_run = -inf; 1 for a row that has seen no visible key yet
@@ -446,24 +432,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       const float nm = m_run == -INFINITY ? 0.f : -m_run;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) negm[rr] = nm;
-    }
-    return 0.f;
-  };
-
-  // softmax back half: P = exp2(s*scale - m) in bf16, row sum.  The 8
-  // accumulator slots 8 (ks & 1) .. +7 of block ks >> 1 form k-step ks.
-  auto softmax_back = [&](f32x16 (&s)[KB], float neg_m, bf16x8 (&pf)[KS]) YR_INLINE {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(s[ks >> 1][(ks & 1) * 8 + 2 * e]);
-        const float p1 = __builtin_amdgcn_exp2f(s[ks >> 1][(ks & 1) * 8 + 2 * e + 1]);
-        l_part += p0 + p1;
-        w[e] = pack_bf16x2(p0, p1);
-      }
-      pf[ks] = as_bf16x8(w);
     }
   };
 
@@ -501,24 +469,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     if (i + NS < count) copy_tile(kst(par), kseq, tile_of(i + NS), false);
     if (i + NS - 1 < count) copy_tile(vst(prevp(par)), vseq, tile_of(i + NS - 1), true);
   };
-  // General step (diagonal, window-edge and tail tiles, the last step): every
-  // check.
-  auto step = [&](auto par, int i, f32x16 (&cur)[KB], f32x16 (&nxt)[KB]) YR_INLINE {
-    stage(par, i);
-    if (i + 1 < count && active(tile_of(i + 1))) scores(nextp(par), nxt);
-    if (active(tile_of(i))) {
-      const float neg_m = softmax_front(tile_of(i), cur, nxt, true);
-      bf16x8 pf[KS];
-      softmax_back(cur, neg_m, pf);
-      pv(par, pf);
-    }
-  };
-  // Clear step: tiles i and i+1 of the list need no mask for any row (below
-  // the diagonal of the workgroup's first row, inside the window of its last
-  // row) and every wave works on both, so the score MFMAs of tile i+1 go out
-  // first, right after the barrier, and the row max, exp / convert work of
-  // tile i and its PV MFMAs follow (measured 1-1.5% faster than issuing the
-  // scores after the row max).
   // P = exp2(s - m) of a whole tile into bf16 fragments; returns the lane's
   // sum of the tile's P (its 32 keys of its row)
   auto exp_tile = [&](f32x16 (&s)[KB], bf16x8 (&pf)[KS]) YR_INLINE -> float {
@@ -537,6 +487,77 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     }
     return ts;
   };
+  // Mask of a diagonal, window-edge, sink or tail tile: the keys of the tile
+  // this lane's row sees, as offsets c from the tile's first key, are
+  // c <= hi (causal, and inside the sequence) and c >= lo (inside the
+  // window), or c < se (a sink).  Slot rr of block kb holds offset
+  // 32 kb + 8 (rr >> 2) + 4 hh + (rr & 3); the lane half's 4 hh goes into
+  // the bounds, so each slot compares a constant.
+  auto apply_mask = [&](int j, f32x16 (&s)[KB]) YR_INLINE {
+    const int key0 = j * kBC;
+    const int pos = P + tq;
+    const int hi = min(pos, nk - 1) - key0 - 4 * hh;
+    if (window > 0) {
+      const int lo = pos - window + 1 - key0 - 4 * hh;
+      const int se = sinks - key0 - 4 * hh;
+      const unsigned span = (unsigned)(hi - lo);
+      if (key0 < sinks) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int c = kb * 32 + (rr >> 2) * 8 + (rr & 3);
+            const bool vis = c <= hi && (c >= lo || c < se);
+            s[kb][rr] = vis ? s[kb][rr] : -INFINITY;
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int c = kb * 32 + (rr >> 2) * 8 + (rr & 3);
+            // lo <= c <= hi as one unsigned compare (empty when hi < lo)
+            const bool vis = hi >= lo && (unsigned)(c - lo) <= span;
+            s[kb][rr] = vis ? s[kb][rr] : -INFINITY;
+          }
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int c = kb * 32 + (rr >> 2) * 8 + (rr & 3);
+          s[kb][rr] = c <= hi ? s[kb][rr] : -INFINITY;
+        }
+    }
+  };
+  // General step (diagonal, window-edge and tail tiles, the last step): every
+  // check.  The mask goes first; then the same optimistic softmax as the
+  // clear steps (a row that has seen no key yet takes the row max path).
+  auto step = [&](auto par, int i, f32x16 (&cur)[KB], f32x16 (&nxt)[KB]) YR_INLINE {
+    stage(par, i);
+    if (i + 1 < count && active(tile_of(i + 1))) scores(nextp(par), nxt);
+    if (active(tile_of(i))) {
+      const int j = tile_of(i);
+      const int key0 = j * kBC;
+      const bool wmask = window > 0 && key0 <= P + tw0 + 31 - window && key0 + kBC > sinks;
+      if ((key0 + kBC - 1 > P + tw0) || (key0 + kBC > nk) || wmask) apply_mask(j, cur);
+      bf16x8 pf[KS];
+      float ts = exp_tile(cur, pf);
+      if (__any(!(ts <= 256.f) || m_run == -INFINITY)) {
+        move_reference(cur, nxt);
+        ts = exp_tile(cur, pf);
+      }
+      l_part += ts;
+      pv(par, pf);
+    }
+  };
+  // Clear step: tiles i and i+1 of the list need no mask for any row (below
+  // the diagonal of the workgroup's first row, inside the window of its last
+  // row) and every wave works on both, so the score MFMAs of tile i+1 go out
+  // first, right after the barrier, and the row max, exp / convert work of
+  // tile i and its PV MFMAs follow (measured 1-1.5% faster than issuing the
+  // scores after the row max).
   auto step_clear = [&](auto par, int i, f32x16 (&cur)[KB], f32x16 (&nxt)[KB]) YR_INLINE {
     stage(par, i);
     scores(nextp(par), nxt);
@@ -548,7 +569,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     bf16x8 pf[KS];
     float ts = exp_tile(cur, pf);
     if (__any(!(ts <= 256.f) || m_run == -INFINITY)) {
-      softmax_front(tile_of(i), cur, nxt, false, 0.f);
+      move_reference(cur, nxt);
       ts = exp_tile(cur, pf);
     }
     l_part += ts;
