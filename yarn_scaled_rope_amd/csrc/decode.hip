@@ -1038,21 +1038,29 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(
 // nwg > 0: the partials of a balanced split (decode_mfma_kernel<..., STREAM>)
 // over nwg workgroups of hpw KV heads each; the pieces of this query head's
 // segment are found from seqlens the same way the split found them.
-template <int D, bool OUT_F32>
+// PERWAVE: a workgroup takes 4 query heads of one sequence, one per wave (for
+// few partials per head: the sequence's place in the batch is found once for
+// the 4 heads, and no wave waits on the others); otherwise its 4 waves share
+// the partials of one head.
+template <int D, bool OUT_F32, bool PERWAVE>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float *__restrict__ part_o, const float *__restrict__ part_lse,
     const int *__restrict__ seqlens, int Hq, int Lmax, int chunk, int nsplit, int vis_split,
     void *__restrict__ out, float *__restrict__ lse, int B, int Hkv, int nwg, int hpw,
     const int *__restrict__ qpos, int window, int sinks) {
   constexpr int PER = D / 64;  // output elements per lane
-  constexpr int MW = 4;        // waves; wave w takes partials w, w+4, ...
+  constexpr int NW = 4;        // waves of the workgroup
+  // waves sharing one head: wave w takes partials w, w + MW, ...
+  constexpr int MW = PERWAVE ? 1 : NW;
   constexpr int U = 4;         // partials per wave in flight
   __shared__ float sm_num[MW][D];
   __shared__ float sm_den[MW];
-  const int b = blockIdx.x / Hq;
-  const int h = blockIdx.x % Hq;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int hpb = PERWAVE ? Hq / NW : Hq;  // workgroups per sequence
+  const int b = blockIdx.x / hpb;
+  const int h = PERWAVE ? (blockIdx.x % hpb) * NW + wave : blockIdx.x % hpb;
+  const int wv = PERWAVE ? 0 : wave;  // this wave's first partial
   int L = seqlens[b];
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
   // partials written: every chunk of the visible rows, or the chunks of
@@ -1079,7 +1087,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
       all += __shfl_xor(all, off);
       lt += __shfl_xor(lt, off);
     }
-    __shared__ int red[2][MW];
+    __shared__ int red[2][NW];
     if (lane == 0) {
       red[0][wave] = all;
       red[1][wave] = lt;
@@ -1087,7 +1095,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     __syncthreads();
     all = lt = 0;
 #pragma unroll
-    for (int w = 0; w < MW; ++w) {
+    for (int w = 0; w < NW; ++w) {
       all += red[0][w];
       lt += red[1][w];
     }
@@ -1109,7 +1117,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   float w0[U], x0[U][PER];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int pu = wave + u * MW;
+    const int pu = wv + u * MW;
     w0[u] = -INFINITY;
 #pragma unroll
     for (int i = 0; i < PER; ++i) x0[u][i] = 0.f;
@@ -1140,7 +1148,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 #pragma unroll
     for (int i = 0; i < PER; ++i) num[i] = fmaf(e, x0[u][i], num[i]);
   }
-  int p = wave + U * MW;
+  int p = wv + U * MW;
   for (; p + (U - 1) * MW < nv; p += U * MW) {
     float w[U], x[U][PER];
 #pragma unroll
@@ -1165,21 +1173,27 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 #pragma unroll
     for (int i = 0; i < PER; ++i) num[i] = fmaf(e, part_o[rw * D + lane + 64 * i], num[i]);
   }
+  if constexpr (!PERWAVE) {
 #pragma unroll
-  for (int i = 0; i < PER; ++i) sm_num[wave][lane + 64 * i] = num[i];
-  if (lane == 0) sm_den[wave] = den;
-  __syncthreads();
-  if (wave != 0) return;
-  den = 0.f;
+    for (int i = 0; i < PER; ++i) sm_num[wave][lane + 64 * i] = num[i];
+    if (lane == 0) sm_den[wave] = den;
+    __syncthreads();
+    if (wave != 0) return;
+    den = 0.f;
 #pragma unroll
-  for (int w = 0; w < MW; ++w) den += sm_den[w];
+    for (int w = 0; w < MW; ++w) den += sm_den[w];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < MW; ++w) t += sm_num[w][lane + 64 * i];
+      num[i] = t;
+    }
+  }
   const long long orow = ((long long)b * Hq + h) * D;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    float t = 0.f;
-#pragma unroll
-    for (int w = 0; w < MW; ++w) t += sm_num[w][lane + 64 * i];
-    const float y = none ? 0.f : t / den;
+    const float y = none ? 0.f : num[i] / den;
     if (OUT_F32)
       ((float *)out)[orow + lane + 64 * i] = y;
     else
@@ -1246,18 +1260,28 @@ hipError_t launch_mfma(const DecodeArgs &a, hipStream_t s) {
   }
 }
 
+template <int D, bool OUT_F32, bool PERWAVE>
+hipError_t launch_merge_k(const DecodeArgs &a, hipStream_t s) {
+  const dim3 grid((unsigned)(PERWAVE ? a.B * (a.Hq / 4) : a.B * a.Hq)), block(256);
+  hipLaunchKernelGGL((decode_merge_kernel<D, OUT_F32, PERWAVE>), grid, block, 0, s, a.part_o,
+                     a.part_lse, a.seqlens, a.Hq, a.max_cache_len, a.chunk, a.nsplit,
+                     a.vis_split, a.out, a.lse, a.B, a.Hkv, a.stream_wg, a.stream_hpw, a.q_pos,
+                     a.window, a.sinks);
+  return hipGetLastError();
+}
+
+// One wave per query head when a head has few partials: a balanced split
+// with at least as many (sequence, head group) segments as workgroups (a
+// segment then spans about two pieces), or at most 8 chunks per head.
 template <int D>
 hipError_t launch_merge(const DecodeArgs &a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.B * a.Hq)), block(256);
+  const bool few = a.stream_wg > 0
+                       ? (long long)a.B * (a.Hkv / a.stream_hpw) >= a.stream_wg
+                       : a.nsplit <= 8;
+  const bool perwave = a.Hq % 4 == 0 && few;
   if (a.out_dtype == YR_F32)
-    hipLaunchKernelGGL((decode_merge_kernel<D, true>), grid, block, 0, s, a.part_o, a.part_lse,
-                       a.seqlens, a.Hq, a.max_cache_len, a.chunk, a.nsplit, a.vis_split, a.out,
-                       a.lse, a.B, a.Hkv, a.stream_wg, a.stream_hpw, a.q_pos, a.window, a.sinks);
-  else
-    hipLaunchKernelGGL((decode_merge_kernel<D, false>), grid, block, 0, s, a.part_o, a.part_lse,
-                       a.seqlens, a.Hq, a.max_cache_len, a.chunk, a.nsplit, a.vis_split, a.out,
-                       a.lse, a.B, a.Hkv, a.stream_wg, a.stream_hpw, a.q_pos, a.window, a.sinks);
-  return hipGetLastError();
+    return perwave ? launch_merge_k<D, true, true>(a, s) : launch_merge_k<D, true, false>(a, s);
+  return perwave ? launch_merge_k<D, false, true>(a, s) : launch_merge_k<D, false, false>(a, s);
 }
 
 }  // namespace
