@@ -82,11 +82,16 @@ def test_fp32_ragged(lens, hq, hkv, D):
     # many heads per KV head, several sequences sharing the grid
     ((1000, 999, 1, 77), 64, 8, 128, ops.YR_BF16),
     ((600, 257), 128, 16, 64, ops.YR_F32),
+    # many sequences: 100 (each lane of the work-item search holds up to 4),
+    # and 300 (past the 256 it holds in registers: it reads them per probe)
+    (tuple((i * 53) % 400 + 1 for i in range(100)), 8, 2, 128, ops.YR_BF16),
+    (tuple((i * 37) % 290 + 1 for i in range(300)), 4, 2, 64, ops.YR_BF16),
 ])
 def test_bf16_ragged_full(lens, hq, hkv, D, out_dtype):
     cfg = wl.PrefillConfig("t", 60, lens, hq, hkv, D, "bf16", 500000.0, 8.0, 64)
     inp = wl.make_prefill(cfg)
-    say(f"prefill bf16 lens={lens} hq={hq} hkv={hkv} D={D} out={out_dtype}")
+    shown = lens if len(lens) <= 8 else f"{len(lens)} sequences"
+    say(f"prefill bf16 lens={shown} hq={hq} hkv={hkv} D={D} out={out_dtype}")
     out, lse = _run(inp, hq, hkv, D, cfg.base, cfg.factor, cfg.original_max_position,
                     out_dtype=out_dtype, pad_rows=128)
     ro, rl = _oracle(inp, D, cfg.base, cfg.factor, cfg.original_max_position)

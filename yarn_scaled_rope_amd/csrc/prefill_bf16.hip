@@ -101,20 +101,42 @@ __device__ __forceinline__ void static_for(F &&f) {
 // one L2.  Every wave of the workgroup computes the same answer: a binary
 // search over the tile index on S(t) = sum_b max(0, tiles_b - t), the number
 // of q-tiles at index t or above, with the sequences spread over the lanes.
-// Returns false for workgroups past the last item.
+// Up to 256 sequences, each lane reads the bounds of its sequences once and
+// the search runs on registers (reading cu_seqlens again for every probe put
+// a chain of dependent loads in front of every workgroup's first tile).
+// Returns false for workgroups past the last item; else the item and the
+// bounds of its sequence (as seq_bounds gives them).
 __device__ __forceinline__ bool packed_item(const int *__restrict__ cu, int B, long long T,
                                             int max_seqlen, int Hq, int ntiles, int item,
-                                            int *tile, int *bo, int *ho) {
+                                            int *tile, int *bo, int *ho, long long *so,
+                                            int *no) {
+  constexpr int NC = 4;  // sequences per lane held in registers
   const int lane = threadIdx.x & 63;
+  auto tiles_of_n = [](int n) { return (n + kBQ - 1) / kBQ; };
   auto tiles_of = [&](int bb) {
     long long s0;
     int n;
     seq_bounds(cu, bb, T, max_seqlen, &s0, &n);
-    return (n + kBQ - 1) / kBQ;
+    return tiles_of_n(n);
   };
+  const bool cached = B <= 64 * NC;
+  long long cs[NC];
+  int cn[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    cs[c] = 0;
+    cn[c] = 0;
+    const int bb = lane + 64 * c;
+    if (cached && bb < B) seq_bounds(cu, bb, T, max_seqlen, &cs[c], &cn[c]);
+  }
   auto count_from = [&](int t) {
     int acc = 0;
-    for (int bb = lane; bb < B; bb += 64) acc += max(0, tiles_of(bb) - t);
+    if (cached) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc += max(0, tiles_of_n(cn[c]) - t);
+    } else {
+      for (int bb = lane; bb < B; bb += 64) acc += max(0, tiles_of(bb) - t);
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
     return __builtin_amdgcn_readfirstlane(acc);
@@ -137,13 +159,29 @@ __device__ __forceinline__ bool packed_item(const int *__restrict__ cu, int B, l
   // the k-th sequence (in batch order) that has a tile at index lo
   for (int base = 0; base < B; base += 64) {
     const int bb = base + lane;
-    const bool has = bb < B && tiles_of(bb) > lo;
+    int n_l = 0;
+    long long s_l = 0;
+    if (cached) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        if (base == 64 * c) {
+          n_l = cn[c];
+          s_l = cs[c];
+        }
+    } else if (bb < B) {
+      seq_bounds(cu, bb, T, max_seqlen, &s_l, &n_l);
+    }
+    const bool has = bb < B && tiles_of_n(n_l) > lo;
     const unsigned long long m = __ballot(has);
     const int c = __popcll(m);
     if (k < c) {
       const unsigned long long below = m & ((1ull << lane) - 1ull);
       const unsigned long long w = __ballot(has && __popcll(below) == k);
-      *bo = base + __ffsll((long long)w) - 1;
+      const int src = __ffsll((long long)w) - 1;
+      *bo = base + src;
+      *no = __shfl(n_l, src);
+      *so = ((long long)__shfl((int)(s_l >> 32), src) << 32) |
+            (unsigned)__shfl((int)(s_l & 0xffffffff), src);
       return true;
     }
     k -= c;
@@ -191,6 +229,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   // q-tiles and heads; consecutive blocks spread a tile's heads over the XCDs
   // so that the heads of one KV head share an L2.
   int tile, b, h;
+  long long s0;
+  int n;
   if (kv_len > 0 && B <= kMaxRankedSeqs) {
     __shared__ int ranked_b;
     const int per = ntiles * Hq;
@@ -218,16 +258,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     __syncthreads();
     b = ranked_b;
     if (b >= B) return;
+    seq_bounds(cu, b, T, max_seqlen, &s0, &n);
   } else {
     const int nwg = (int)gridDim.x;
     int item = (int)blockIdx.x;
     if (permuted) item = (int)(((long long)(nwg - 1 - item) + nwg / 3) % nwg);
-    if (!packed_item(cu, B, T, max_seqlen, Hq, ntiles, item, &tile, &b, &h)) return;
+    if (!packed_item(cu, B, T, max_seqlen, Hq, ntiles, item, &tile, &b, &h, &s0, &n)) return;
   }
   const int hk = h / (Hq / Hkv);
-  long long s0;
-  int n;
-  seq_bounds(cu, b, T, max_seqlen, &s0, &n);
   // uniform across the workgroup: keep them in scalar registers so the
   // per-tile buffer descriptors need no per-lane fix-up
   n = __builtin_amdgcn_readfirstlane(n);
