@@ -51,18 +51,25 @@ __device__ __forceinline__ float half_sum(float x) {
 // polynomials of the Cephes library (sinf/cosf), and the quadrant picks the
 // signs.  Max abs error ~1e-7 (about 1.5 fp32 ulp of 1.0).
 __device__ __forceinline__ void rope_cos_sin(double pos, double theta, float *c, float *s) {
+#pragma clang fp contract(off)  // the product is rounded before the shift, as rint saw it
   constexpr double kTwoOverPi = 0.63661977236758134308;
   constexpr double kPio2Hi = 1.5707963267948966192;    // nearest double to pi/2
   constexpr double kPio2Lo = 6.123233995736766036e-17;  // pi/2 - kPio2Hi
+  // 1.5 * 2^52: adding it rounds a value of magnitude below 2^51 to an
+  // integer (to nearest, ties to even, as rint does) held in the low bits of
+  // the sum's mantissa, so the quadrant count and its value mod 4 cost one
+  // add and one subtract instead of a rint and a 64-bit conversion
+  constexpr double kShift = 6755399441055744.0;
   const double x = pos * theta;
-  const double kq = rint(x * kTwoOverPi);
+  const double t = x * kTwoOverPi + kShift;
+  const double kq = t - kShift;
   double r = fma(-kq, kPio2Hi, x);
   r = fma(-kq, kPio2Lo, r);
   const float rf = (float)r, z = rf * rf;
   const float sp = fmaf(rf * z, fmaf(z, fmaf(z, -1.9515295891e-4f, 8.3321608736e-3f), -1.6666654611e-1f), rf);
   const float cp = fmaf(z * z, fmaf(z, fmaf(z, 2.443315711809948e-5f, -1.388731625493765e-3f), 4.166664568298827e-2f),
                         fmaf(-0.5f, z, 1.0f));
-  const int quad = (int)((long long)kq & 3);
+  const int quad = (int)(__double_as_longlong(t) & 3);
   float ss = (quad & 1) ? cp : sp;
   float cc = (quad & 1) ? sp : cp;
   if (quad == 1 || quad == 2) cc = -cc;
