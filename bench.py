@@ -251,18 +251,24 @@ def bench_decode(args, torch, ops, wl):
 
 
 # ------------------------------------------------------------------ next rows
+QUEUED_TIMING = ("calls back to back after an unsynchronised burst of untimed calls "
+                 "(the device stays busy at its working clock; host issue time excluded)")
+
+
 def _queued_ms(torch, fns, warmup: int, steps: int, stream) -> float:
     """Mean duration (ms) of one call when `steps` calls run back to back on
-    the stream, call i being fns[i % len(fns)].  The calls are queued behind a
-    GPU-side delay, so the host's time to issue them (the Python binding and
-    the launches) does not open gaps between them; for short calls this is
-    the device's throughput rather than the host's."""
-    for i in range(warmup):
-        fns[i % len(fns)]()
+    the stream, call i being fns[i % len(fns)].  One call and a device
+    synchronisation absorb first-call costs; then `warmup` more calls go out
+    with no synchronisation, so the device is busy (at the clock it holds
+    under this load, not ramping up from idle) while the host queues the
+    timed calls behind them, and the host's time to issue a call (the Python
+    binding and the launches) does not open gaps between them."""
+    fns[0]()
     torch.cuda.synchronize()
+    for i in range(max(warmup, 4)):
+        fns[i % len(fns)]()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(2e6))  # ~1 ms of device time while the calls are queued
     a.record(stream)
     for i in range(steps):
         fns[i % len(fns)]()
@@ -350,18 +356,18 @@ def bench_next(args, torch, ops, wl, pstate, dstate):
         out = torch.empty_like(p["q"])
         ws = torch.empty(256, dtype=torch.uint8, device="cuda")
         log("windowed prefill timed")
-        ms = _event_ms(torch, lambda: ops.attn_prefill_fwd(p["q"], p["krot"], p["v"], p["cu"],
-                                                           p["maxlen"], p["theta"], p["scale"],
-                                                           out=out, want_lse=False, workspace=ws,
-                                                           k_rotated=True, window=pc.window,
-                                                           sinks=pc.sinks, stream=stream),
-                       args.warmup, args.steps, stream)
+        ms = _queued_ms(torch, [lambda: ops.attn_prefill_fwd(p["q"], p["krot"], p["v"], p["cu"],
+                                                             p["maxlen"], p["theta"], p["scale"],
+                                                             out=out, want_lse=False, workspace=ws,
+                                                             k_rotated=True, window=pc.window,
+                                                             sinks=pc.sinks, stream=stream)],
+                        args.warmup, args.steps, stream)
         flops = wl.prefill_visible_flops(pc.seq_lens, pc.hq, pc.head_dim, pc.window, pc.sinks)
         tf = flops / (ms * 1e-3) / 1e12
         res["window_prefill"] = {
             "metric": "windowed prefill TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
             "ms_per_call": round(ms, 4), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-            "flops_per_launch": flops,
+            "flops_per_launch": flops, "timing": QUEUED_TIMING,
             "config": {"workload": pc.name, "inputs": "those of the prefill line",
                        "window": pc.window, "sinks": pc.sinks}}
 
@@ -393,8 +399,7 @@ def bench_next(args, torch, ops, wl, pstate, dstate):
             "metric": "windowed decode KV GB/s", "value": round(gbs, 2), "unit": "GB/s",
             "ms_per_call": round(ms, 4), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "bytes_per_launch": int(nbytes),
-            "timing": "calls back to back behind a device-side delay (host issue time "
-                      "excluded), windows of 8 cache lengths 4096 rows apart in turn",
+            "timing": QUEUED_TIMING + ", windows of 8 cache lengths 4096 rows apart in turn",
             "config": {"workload": dc.name, "inputs": "those of the decode line",
                        "window": dc.window, "sinks": dc.sinks}}
         # FP8 (E4M3) copy of the same cache, one scale per KV head (amax / 448
@@ -415,17 +420,18 @@ def bench_next(args, torch, ops, wl, pstate, dstate):
             codes.append(q8)
         out = torch.empty_like(d["q"])
         log("fp8 decode timed")
-        ms = _event_ms(torch, lambda: ops.attn_decode_fp8(d["q"], codes[0], codes[1], scales[0],
-                                                          scales[1], d["sl"], d["theta"],
-                                                          d["scale"], out=out, want_lse=False,
-                                                          workspace=d["ws"], stream=stream),
-                       args.warmup, args.decode_steps, stream)
+        # 2.7 GB per call, far past the last-level cache: calls back to back
+        ms = _queued_ms(torch, [lambda: ops.attn_decode_fp8(d["q"], codes[0], codes[1], scales[0],
+                                                            scales[1], d["sl"], d["theta"],
+                                                            d["scale"], out=out, want_lse=False,
+                                                            workspace=d["ws"], stream=stream)],
+                        args.warmup, args.decode_steps, stream)
         nbytes = wl.decode_kv_bytes(d["seqlens"], wl.DECODE_B16.hkv, wl.DECODE_B16.head_dim, 1)
         gbs = nbytes / (ms * 1e-3) / 1e9
         res["fp8_decode"] = {
             "metric": "FP8-cache decode KV GB/s", "value": round(gbs, 2), "unit": "GB/s",
             "ms_per_call": round(ms, 4), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "bytes_per_launch": int(nbytes),
+            "bytes_per_launch": int(nbytes), "timing": QUEUED_TIMING,
             "config": {"workload": wl.DECODE_B16.name + "_fp8_e4m3",
                        "inputs": "the decode line's cache, as E4M3 codes with per-KV-head "
                                  "scales amax/448"}}
@@ -449,9 +455,11 @@ def bench_next(args, torch, ops, wl, pstate, dstate):
         lout = torch.empty_like(lq)
         log("large-batch decode timed")
         lscale = lt / math.sqrt(lb.head_dim)
-        ms = _event_ms(torch, lambda: ops.attn_decode(lq, lkc, lvc, lsl, lth, lscale, out=lout,
-                                                      want_lse=False, workspace=lws, stream=stream),
-                       args.warmup, args.decode_steps, stream)
+        # 2.5 GB per call: calls back to back, as the FP8 row
+        ms = _queued_ms(torch, [lambda: ops.attn_decode(lq, lkc, lvc, lsl, lth, lscale, out=lout,
+                                                        want_lse=False, workspace=lws,
+                                                        stream=stream)],
+                        args.warmup, args.decode_steps, stream)
         if ops.read_device_error(lws) != 0:
             raise SystemExit("device range check failed (large-batch decode)")
         nbytes = wl.decode_kv_bytes(linp["seqlens"], lb.hkv, lb.head_dim)
@@ -459,7 +467,7 @@ def bench_next(args, torch, ops, wl, pstate, dstate):
         res["large_batch_decode"] = {
             "metric": "decode KV GB/s", "value": round(gbs, 2), "unit": "GB/s",
             "ms_per_call": round(ms, 4), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "bytes_per_launch": int(nbytes),
+            "bytes_per_launch": int(nbytes), "timing": QUEUED_TIMING,
             "config": {"workload": lb.name, "batch": lb.batch, "sum_seqlens": int(linp["seqlens"].sum()),
                        "hq": lb.hq, "hkv": lb.hkv, "head_dim": lb.head_dim, "seed": 1000 + lb.index}}
         del lkc, lvc
