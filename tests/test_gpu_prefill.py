@@ -164,7 +164,14 @@ def test_deterministic():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("lens,hq,hkv", [((1000, 999, 1, 77, 513), 64, 8), ((700, 300, 1300), 12, 3)])
+@pytest.mark.parametrize("lens,hq,hkv", [
+    ((1000, 999, 1, 77, 513), 64, 8),
+    ((700, 300, 1300), 12, 3),
+    # 256 sequences (the most the work-item search holds in registers) and
+    # 257 (one past: it reads the bounds per probe)
+    (tuple((i * 29) % 300 + 1 for i in range(256)), 4, 1),
+    (tuple((i * 29) % 300 + 1 for i in range(257)), 4, 1),
+])
 def test_deterministic_under_permuted_order(lens, hq, hkv):
     """Workgroups taking their (q-tile, sequence, head) items in a permuted
     order (reversed and rotated instead of longest first) give the same bits:
@@ -175,7 +182,8 @@ def test_deterministic_under_permuted_order(lens, hq, hkv):
     th_dev, scale = lib_theta(128, cfg.base, cfg.factor, cfg.original_max_position)
     cu = torch.from_numpy(inp["cu_seqlens"]).cuda()
     q, k, v = to_dev(inp["q"], "bf16"), to_dev(inp["k"], "bf16"), to_dev(inp["v"], "bf16")
-    say(f"prefill permuted order lens={lens} hq={hq} hkv={hkv}")
+    shown = lens if len(lens) <= 8 else f"{len(lens)} sequences"
+    say(f"prefill permuted order lens={shown} hq={hq} hkv={hkv}")
     a, al = ops.attn_prefill_fwd(q, k, v, cu, max(lens), th_dev, scale)
     b, bl = ops.attn_prefill_fwd(q, k, v, cu, max(lens), th_dev, scale, permuted_order=True)
     torch.cuda.synchronize()
