@@ -345,7 +345,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     js = min((min(sinks, lo) + kBC - 1) / kBC, jw);
   }
   const int count = js + (last - jw + 1);
-  auto tile_of = [&](int i) YR_INLINE { return i < js ? i : jw + (i - js); };
+  // With a window the workgroup sweeps its window tiles rotated: list
+  // position js + s holds the window tile congruent to s modulo the window's
+  // length in tiles.  Workgroups of neighbouring q-tiles (windows a few tiles
+  // apart, launched together) then read the same tile at the same step, so
+  // L2 serves them; swept from its start, each would read a tile a few steps
+  // after the other, about an L2's worth of traffic later.
+  const int nw = last - jw + 1;
+  const int r0 = window > 0 ? (nw - jw % nw) % nw : 0;
+  auto tile_of = [&](int i) YR_INLINE {
+    if constexpr (!EXT) {
+      return i;
+    } else {
+      if (i < js) return i;
+      int p = i - js + r0;
+      p = p >= nw ? p - nw : p;
+      return jw + p;
+    }
+  };
   // prologue copies (K of tiles 0..NS-1, V of tiles 0..NS-2 of the list) go
   // out before the query work so that they are in flight meanwhile
   static_for<0, NS>([&](auto ic) YR_INLINE {
@@ -634,13 +651,30 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   // [c0, c1)).  Steps before it and after it take the general body; a clear
   // step i needs tiles i and i+1 in the run.  Separate loops keep each body's
   // registers to itself.
-  int c0 = count, c1 = count;
+  // In list positions the clear tiles [jc, jd] form one run, or two when the
+  // rotation wraps them: [c0, c1) and [c2, c3), c1 <= c2.
+  int c0 = count, c1 = count, c2 = count, c3 = count;
   {
     const int jd = (P + q0 + 1) / kBC - 1;  // last tile wholly below the first row's diagonal
     const int jc = window > 0 ? max(jw, (P + qend - window + kBC - 1) / kBC) : 0;
     if (jd >= jc) {
-      c0 = js + (jc - jw);
-      c1 = js + (jd - jw) + 1;
+      if constexpr (!EXT) {
+        c0 = jc;
+        c1 = jd + 1;
+      } else {
+        int a = jc - jw - r0;
+        a = a < 0 ? a + nw : a;
+        const int len = jd - jc + 1;
+        if (a + len <= nw) {
+          c0 = js + a;
+          c1 = c0 + len;
+        } else {
+          c0 = js;
+          c1 = js + (a + len - nw);
+          c2 = js + a;
+          c3 = count;
+        }
+      }
     }
   }
   auto general_block = [&](int i) YR_INLINE {
@@ -649,11 +683,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       if (i + I < count) step(std::integral_constant<int, I % NS>{}, i + I, sbuf(ic), obuf(ic));
     });
   };
-  int i = 0;
-  for (; i < c0; i += BL) general_block(i);
   // the unmasked run in blocks of 4 steps (two stage / buffer cycles; +0.5-1%
   // over blocks of 2), its remainder in blocks of 2
   constexpr int BLC = 4;
+  int i = 0;
+  for (; i < c0; i += BL) general_block(i);
   for (; i + BLC < c1; i += BLC) {
     static_for<0, BLC>([&](auto ic) YR_INLINE {
       constexpr int I = decltype(ic)::value;
@@ -665,6 +699,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       constexpr int I = decltype(ic)::value;
       step_clear(std::integral_constant<int, I % NS>{}, i + I, sbuf(ic), obuf(ic));
     });
+  }
+  if constexpr (EXT) {  // the second run, where the rotation wraps the first
+    for (; i < c2; i += BL) general_block(i);
+    for (; i + BLC < c3; i += BLC) {
+      static_for<0, BLC>([&](auto ic) YR_INLINE {
+        constexpr int I = decltype(ic)::value;
+        step_clear(std::integral_constant<int, I % NS>{}, i + I, sbuf(ic), obuf(ic));
+      });
+    }
+    for (; i + BL < c3; i += BL) {
+      static_for<0, BL>([&](auto ic) YR_INLINE {
+        constexpr int I = decltype(ic)::value;
+        step_clear(std::integral_constant<int, I % NS>{}, i + I, sbuf(ic), obuf(ic));
+      });
+    }
   }
   for (; i < count; i += BL) general_block(i);
 
