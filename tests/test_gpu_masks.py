@@ -31,6 +31,11 @@ def _tol(dtype):
     ("bf16", (513, 1000), 4, 4, 64, 1, 0),
     ("bf16", (2000,), 8, 1, 128, 257, 70),     # sinks over more than one key tile
     ("bf16", (777,), 8, 2, 128, 5000, 3),      # window longer than the sequence
+    # windows of several key tiles over long sequences: the rotated window
+    # sweep puts the unmasked tiles in one run of the list for some q-tiles
+    # and in two (wrapped) for others
+    ("bf16", (3000, 1500), 4, 2, 64, 700, 4),
+    ("bf16", (4100,), 8, 8, 128, 1500, 0),
     ("f32", (1, 130, 400), 4, 2, 64, 50, 2),
     ("f32", (300,), 2, 2, 128, 1, 0),
 ])
