@@ -29,15 +29,17 @@
 //     them, the softmax of tile j (VALU and transcendental work), then the PV
 //     MFMAs of tile j.  One barrier per step.
 //   * The running max is lazy: every exponent stays at most 2^8 against it,
-//     so the O rescale is skipped on most tiles.  Tiles that need no mask
-//     are exponentiated against the current reference straight away; a
-//     lane's tile sum bounds each of its P, so only a sum above 2^8 (rare)
-//     sends the wave through the row max and a second pass.
-//   * Tiles wholly above a wave's diagonal are skipped by that wave; masking
-//     runs only on tiles that cross the diagonal or the sequence end.
+//     so the O rescale is skipped on most tiles.  Every tile is exponentiated
+//     against the current reference straight away; a lane's tile sum bounds
+//     each of its P, so only a sum above 2^8 (rare) or a row without a
+//     reference yet sends the wave through the row max and a second pass.
+//   * Tiles wholly above a wave's diagonal (or before its window) are
+//     skipped by that wave; masking runs only on tiles that cross the
+//     diagonal, a window edge, the sinks or the sequence end.
 //   * Workgroups run longest-first (q-tile index from the last tile down) and
 //     are spread over the 8 XCDs so that the query heads of one KV head land
-//     on one XCD and share its L2.
+//     on one XCD and share its L2; with a window, each sweeps its window
+//     rotated so that neighbouring q-tiles read the same tile together.
 #include "device_common.h"
 #include "yr_internal.h"
 
