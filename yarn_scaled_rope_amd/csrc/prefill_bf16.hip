@@ -115,6 +115,56 @@ __device__ __forceinline__ bool packed_item(const int *__restrict__ cu, int B, l
   constexpr int NC = 4;  // sequences per lane held in registers
   const int lane = threadIdx.x & 63;
   auto tiles_of_n = [](int n) { return (n + kBQ - 1) / kBQ; };
+  // Up to kScalarSeqs sequences the whole search is uniform: every value is
+  // read with a uniform address into scalar registers, and the probes need
+  // no cross-lane reduction (a probe's chain of six dependent lane shuffles
+  // was most of the search time).
+  constexpr int kScalarSeqs = 16;
+  if (B <= kScalarSeqs) {
+    int tn[kScalarSeqs];
+#pragma unroll
+    for (int bb = 0; bb < kScalarSeqs; ++bb) {
+      tn[bb] = 0;
+      if (bb < B) {
+        long long s0b;
+        int nb;
+        seq_bounds(cu, bb, T, max_seqlen, &s0b, &nb);
+        tn[bb] = __builtin_amdgcn_readfirstlane(tiles_of_n(nb));
+      }
+    }
+    auto count_u = [&](int t) {
+      int acc = 0;
+#pragma unroll
+      for (int bb = 0; bb < kScalarSeqs; ++bb) acc += max(0, tn[bb] - t);
+      return acc;
+    };
+    if ((long long)Hq * count_u(0) <= item) return false;
+    int lo = 0, hi = ntiles - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((long long)Hq * count_u(mid) > item) lo = mid; else hi = mid - 1;
+    }
+    const int above = count_u(lo + 1);
+    const int cnt = count_u(lo) - above;
+    const long long first = (long long)Hq * above;
+    const int nt = cnt * Hq;
+    int j = (int)(item - first);
+    if (first % kXcds == 0 && nt % kXcds == 0) j = (j % kXcds) * (nt / kXcds) + j / kXcds;
+    int k = j / Hq;
+    *ho = j % Hq;
+    *tile = lo;
+    int bsel = 0;
+#pragma unroll
+    for (int bb = 0; bb < kScalarSeqs; ++bb) {
+      if (tn[bb] > lo) {
+        if (k == 0) bsel = bb;
+        --k;
+      }
+    }
+    *bo = bsel;
+    seq_bounds(cu, bsel, T, max_seqlen, so, no);
+    return true;
+  }
   auto tiles_of = [&](int bb) {
     long long s0;
     int n;
