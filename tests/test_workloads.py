@@ -46,6 +46,28 @@ def test_decode_inputs_nan_tails():
         assert np.all(np.isfinite(wl.bf16_bits_to_f32(d["v_cache"][b, :L])))
 
 
+def test_prefill_sparse_q_draws_only_the_named_rows():
+    cfg = wl.PrefillConfig("t", 3, (40, 25), 4, 2, 64, "bf16", 10000.0, 1.0, 64)
+    a = wl.make_prefill(cfg, q_tokens=[64, 3, 3, 41])
+    nz = np.flatnonzero(np.any(a["q"] != 0, axis=(1, 2)))
+    assert list(nz) == [3, 41, 64]
+    # the rows are drawn in ascending token order, before k and v
+    rng = np.random.Generator(np.random.PCG64(1000 + cfg.index))
+    want = wl._draw(rng, (3, 4, 64), "bf16")
+    assert np.array_equal(a["q"][[3, 41, 64]], want)
+    assert np.array_equal(a["k"], wl._draw(rng, (65, 2, 64), "bf16"))
+
+
+def test_decode_given_seqlens():
+    d = wl.make_decode(wl.DECODE_B16, batch=2, max_cache_len=50, seqlens=[7, 50])
+    assert list(d["seqlens"]) == [7, 50]
+    assert np.all(np.isnan(wl.bf16_bits_to_f32(d["k_cache"][0, 7:])))
+    assert np.all(np.isfinite(wl.bf16_bits_to_f32(d["k_cache"][1])))
+    f = wl.make_decode_fp8(wl.DECODE_B16, batch=2, max_cache_len=30, seqlens=[30, 0])
+    assert list(f["seqlens"]) == [30, 0]
+    assert np.all(f["v_cache"][1] == wl.E4M3_NAN_CODE)
+
+
 def test_sample_rows_cover_edges_and_tails():
     rows = wl.sample_rows((300, 65), 8, 2, n_random=5)
     toks = {t for t, _ in rows}

@@ -165,27 +165,49 @@ def cu_seqlens_of(seq_lens) -> np.ndarray:
     return cu
 
 
-def make_prefill(cfg: PrefillConfig, seed: int | None = None, seq_lens=None):
-    """Packed ragged prefill inputs: q [T, Hq, D], k, v [T, Hkv, D]."""
+def make_prefill(cfg: PrefillConfig, seed: int | None = None, seq_lens=None, q_tokens=None):
+    """Packed ragged prefill inputs: q [T, Hq, D], k, v [T, Hkv, D].
+
+    q_tokens (optional): only these token rows of q are drawn (in ascending
+    order, before k and v); every other row of q is zero.  For batches whose
+    q is too large to draw in full when only a few rows are checked."""
     lens = tuple(cfg.seq_lens if seq_lens is None else seq_lens)
     rng = np.random.Generator(np.random.PCG64(1000 + cfg.index if seed is None else seed))
     T = int(sum(lens))
-    q = _draw(rng, (T, cfg.hq, cfg.head_dim), cfg.dtype)
+    if q_tokens is None:
+        q = _draw(rng, (T, cfg.hq, cfg.head_dim), cfg.dtype)
+    else:
+        toks = np.unique(np.asarray(q_tokens, dtype=np.int64))
+        assert toks.size == 0 or (toks[0] >= 0 and toks[-1] < T)
+        q = np.zeros((T, cfg.hq, cfg.head_dim), dtype=np.uint16 if cfg.dtype == "bf16"
+                     else np.float32)
+        q[toks] = _draw(rng, (toks.size, cfg.hq, cfg.head_dim), cfg.dtype)
     k = _draw(rng, (T, cfg.hkv, cfg.head_dim), cfg.dtype)
     v = _draw(rng, (T, cfg.hkv, cfg.head_dim), cfg.dtype)
     return {"q": q, "k": k, "v": v, "cu_seqlens": cu_seqlens_of(lens),
             "seq_lens": lens, "dtype": cfg.dtype}
 
 
+def _seqlens(rng, B, lmin, lmax, seqlens):
+    """Cache lengths ~ U{lmin..lmax}, or the given ones (then nothing is drawn
+    for them)."""
+    if seqlens is None:
+        return rng.integers(lmin, lmax, size=B, endpoint=True).astype(np.int32)
+    out = np.asarray(seqlens, dtype=np.int32)
+    assert out.shape == (B,) and np.all(out >= 0) and np.all(out <= lmax)
+    return out
+
+
 def make_decode(cfg: DecodeConfig, seed: int | None = None, batch=None,
-                max_cache_len=None, min_cache_len=None):
+                max_cache_len=None, min_cache_len=None, seqlens=None):
     """Decode inputs: q [B, Hq, D]; k_cache, v_cache [B, Lmax, Hkv, D] with
-    NaN rows past each sequence's length; seqlens [B] ~ U{min..max}."""
+    NaN rows past each sequence's length; seqlens [B] ~ U{min..max} unless
+    given."""
     B = cfg.batch if batch is None else batch
     lmax = cfg.max_cache_len if max_cache_len is None else max_cache_len
     lmin = cfg.min_cache_len if min_cache_len is None else min_cache_len
     rng = np.random.Generator(np.random.PCG64(1000 + cfg.index if seed is None else seed))
-    seqlens = rng.integers(lmin, lmax, size=B, endpoint=True).astype(np.int32)
+    seqlens = _seqlens(rng, B, lmin, lmax, seqlens)
     q = _draw(rng, (B, cfg.hq, cfg.head_dim), cfg.dtype)
     caches = []
     for _ in range(2):
@@ -212,16 +234,17 @@ def e4m3_codes(x: np.ndarray) -> np.ndarray:
 
 
 def make_decode_fp8(cfg: DecodeConfig, seed: int | None = None, batch=None, max_cache_len=None,
-                    min_cache_len=None):
+                    min_cache_len=None, seqlens=None):
     """FP8-cache decode inputs: the cache lengths, q (bf16) and K/V values
     drawn like make_decode; per-KV-head scales 2^-6 * (1 + h/4) for K and
     2^-6 * (1 + h/8) for V; each cache element stored as the E4M3 code of
-    value / scale; rows past a sequence's length hold the NaN code."""
+    value / scale; rows past a sequence's length hold the NaN code.  The
+    cache lengths are drawn as in make_decode unless given."""
     B = cfg.batch if batch is None else batch
     lmax = cfg.max_cache_len if max_cache_len is None else max_cache_len
     lmin = cfg.min_cache_len if min_cache_len is None else min_cache_len
     rng = np.random.Generator(np.random.PCG64(1000 + cfg.index if seed is None else seed))
-    seqlens = rng.integers(lmin, lmax, size=B, endpoint=True).astype(np.int32)
+    seqlens = _seqlens(rng, B, lmin, lmax, seqlens)
     q = _draw(rng, (B, cfg.hq, cfg.head_dim), "bf16")
     h = np.arange(cfg.hkv, dtype=np.float32)
     scales = [(np.float32(2.0 ** -6) * (1.0 + h / 4.0)).astype(np.float32),
