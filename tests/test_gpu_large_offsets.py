@@ -1,9 +1,10 @@
 """Inputs whose element offsets pass 2^31, against the oracle: a packed
 prefill batch whose queries and outputs hold 2.6e9 elements (the checked rows
-all lie past element 2^31), and decode caches of 2^21 - 100 rows per sequence,
-so that the second sequence's rows start 100 rows before element (FP8: byte)
-2^31 and run past it.  An offset computed in 32 bits anywhere on these paths
-reads or writes the wrong rows.
+all lie past element 2^31), the rotation of those queries in place, and
+caches of 2^21 - 100 rows per sequence for decode and chunked prefill, so that
+the second sequence's rows start 100 rows before element (FP8: byte) 2^31 and
+run past it.  An offset computed in 32 bits anywhere on these paths reads or
+writes the wrong rows.
 
 To keep the host side short, the prefill queries are drawn only for the
 checked tokens (every other query row is zero, which the kernel processes like
@@ -16,6 +17,7 @@ import torch
 
 from oracle import attention as oatt
 from oracle import fp8 as ofp8
+from oracle import rope as orope
 from tests._gpu_util import (BF16_TOL, LazyF64, lib_theta, max_abs, oracle_theta, say, to_dev,
                              to_f64)
 from yarn_scaled_rope_amd import ops
@@ -61,6 +63,23 @@ def test_prefill_offsets_past_2_to_31():
     print(f"{len(rows)} (row, head) pairs, max-abs out {e_out:.3e} lse {e_lse:.3e}")
     assert np.all(np.isfinite(got_o))
     assert e_out <= BF16_TOL and e_lse <= BF16_TOL
+
+    # the same queries rotated in place by rope_apply_packed: each checked
+    # element within one bf16 ulp of the exact rotation at its position
+    say("rope_apply_packed in place past 2^31 elements")
+    qd = to_dev(inp["q"], "bf16")
+    ops.rope_apply_packed(qd, torch.from_numpy(inp["cu_seqlens"]).cuda(), max(lens), th_dev,
+                          dst=qd)
+    torch.cuda.synchronize()
+    got = to_f64(qd.index_select(0, tix))
+    del qd
+    torch.cuda.empty_cache()
+    starts = inp["cu_seqlens"][np.searchsorted(inp["cu_seqlens"], toks, side="right") - 1]
+    ref = orope.rotate(wl.as_f64(inp["q"][toks], "bf16"), np.asarray(toks) - starts, th)
+    mag = np.maximum(np.abs(ref), 1e-30)
+    ulp = 2.0 ** (np.floor(np.log2(mag)) - 7)
+    print(f"rotation max-abs {max_abs(got, ref):.3e}")
+    assert np.all(np.abs(got - ref) <= ulp + 1e-6)
 
 
 def _decode_cfg():
@@ -125,3 +144,32 @@ def test_decode_fp8_offsets_past_2_to_31():
     print(f"max-abs out {e_out:.3e} lse {e_lse:.3e}")
     assert np.all(np.isfinite(got_o))
     assert e_out <= BF16_TOL and e_lse <= BF16_TOL
+
+
+@pytest.mark.timeout(400)
+def test_chunk_offsets_past_2_to_31():
+    ctx, qlens = (1000, 30000), (300, 700)
+    cfg = wl.ChunkConfig("offsets", 33, ctx, qlens, LMAX, 32, 8, 128, "bf16", 500000.0, 8.0,
+                         16384)
+    inp = wl.make_chunk(cfg, seed=4545)
+    th_dev, scale = lib_theta(cfg.head_dim, cfg.base, cfg.factor, cfg.original_max_position)
+    th, sc = oracle_theta(cfg.head_dim, cfg.base, cfg.factor, cfg.original_max_position)
+    q = to_dev(inp["q"], "bf16")
+    kc = to_dev(inp["k_cache"], "bf16")
+    vc = to_dev(inp["v_cache"], "bf16")
+    cu = torch.from_numpy(inp["cu_seqlens_q"]).cuda()
+    cl = torch.from_numpy(inp["ctx_lens"]).cuda()
+    for window, sinks in ((0, 0), (4096, 4)):
+        say(f"chunked prefill past 2^31 elements: Lmax={LMAX} ctx={ctx} chunks={qlens} "
+            f"W={window} S={sinks}")
+        out, lse = ops.attn_prefill_chunk(q, kc, vc, cu, cl, max(qlens), th_dev, scale,
+                                          window=window, sinks=sinks, out_dtype=ops.YR_F32)
+        torch.cuda.synchronize()
+        ro, rl = oatt.prefill_chunk(LazyF64(inp["q"], "bf16"), LazyF64(inp["k_cache"], "bf16"),
+                                    LazyF64(inp["v_cache"], "bf16"), inp["cu_seqlens_q"],
+                                    inp["ctx_lens"], th, sc, window=window, sinks=sinks)
+        got_o, got_l = to_f64(out), lse.cpu().numpy().astype(np.float64)
+        e_out, e_lse = max_abs(got_o, ro), max_abs(got_l, rl)
+        print(f"W={window}: max-abs out {e_out:.3e} lse {e_lse:.3e}")
+        assert np.all(np.isfinite(got_o))
+        assert e_out <= BF16_TOL and e_lse <= BF16_TOL
