@@ -114,7 +114,7 @@ DECODE_B16_SWA = DecodeConfig("decode_b16_gqa_window4k_sinks4", 7, 16, 131072, 3
                               128, "bf16", 500000.0, 8.0, 16384, window=4096, sinks=4)
 
 # Many sequences: 256 caches of 512 .. 4096 tokens (Llama-3-8B GQA layer),
-# a serving batch past the 128 sequences the balanced split used to stop at.
+# a serving batch of many short caches.
 DECODE_B256 = DecodeConfig("decode_b256_gqa_512_4k", 9, 256, 4096, 512, 32, 8, 128, "bf16",
                            500000.0, 8.0, 16384)
 
