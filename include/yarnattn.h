@@ -211,6 +211,8 @@ size_t attn_prefill_workspace_bytes(long long T, int Hkv, int head_dim, int in_d
  *                  Hkv, head_dim, in_dtype) bytes when the library rotates the
  *                  keys (it holds them), else >= YR_WORKSPACE_HEADER_BYTES
  *   head_dim       64 or 128;  Hq % Hkv == 0
+ * With T = 0 (every sequence empty) q, k, v and out may be NULL; cu_seqlens
+ * is still checked on the device.
  */
 int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
                      const int *cu_seqlens, int B, int max_seqlen, long long T,
@@ -245,6 +247,8 @@ int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
  *   out, lse         as attn_prefill_fwd ([Tq, Hq, head_dim], float[Hq, Tq])
  *   workspace        device, 256-byte aligned, >= YR_WORKSPACE_HEADER_BYTES
  *                    (holds the device error word)
+ * With Tq = 0 q, the caches and out may be NULL; cu_seqlens_q and ctx_lens
+ * are still checked on the device.
  */
 int attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cache, int in_dtype,
                        const int *cu_seqlens_q, const int *ctx_lens, int B, int max_seqlen_q,

@@ -213,6 +213,41 @@ def test_chunk_bad_ctx_sets_flag():
     assert ops.read_device_error(ws) == 0
 
 
+@pytest.mark.parametrize("window,sinks", [(0, 0), (100, 3)])
+def test_chunk_with_empty_chunks(window, sinks):
+    """Sequences with no new token (n_b = 0) among others: they produce
+    nothing, the others match the oracle."""
+    cfg = wl.ChunkConfig("t", 89, (500, 0, 40, 1000), (0, 130, 0, 7), 1200, 8, 2, 128, "bf16",
+                         500000.0, 8.0, 16384)
+    inp = wl.make_chunk(cfg)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    say(f"chunk with empty chunks ctx={cfg.ctx_lens} qlens={cfg.chunk_lens} W={window} S={sinks}")
+    out, lse = _chunk_run(inp, cfg, window, sinks, ws=ws)
+    assert ops.read_device_error(ws) == 0
+    ro, rl = _chunk_oracle(inp, cfg, window, sinks)
+    e_out, e_lse = max_abs(to_f64(out), ro), max_abs(lse.cpu().numpy(), rl)
+    print(f"max-abs out {e_out:.3e} lse {e_lse:.3e}")
+    assert e_out <= BF16_TOL and e_lse <= BF16_TOL
+
+
+def test_chunk_without_new_tokens():
+    """Tq = 0: the call succeeds with empty q / out (NULL data pointers) and
+    still checks ctx_lens on the device."""
+    cfg = wl.ChunkConfig("t", 90, (10, 20), (0, 0), 64, 4, 2, 64, "bf16", 500000.0, 8.0, 16384)
+    inp = wl.make_chunk(cfg)
+    th_dev, scale = lib_theta(cfg.head_dim, cfg.base, cfg.factor, cfg.original_max_position)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    q = torch.empty((0, cfg.hq, cfg.head_dim), dtype=torch.bfloat16, device="cuda")
+    kc, vc = to_dev(inp["k_cache"], "bf16"), to_dev(inp["v_cache"], "bf16")
+    cu = torch.zeros(3, dtype=torch.int32, device="cuda")
+    say("chunk with no new tokens")
+    for ctx, flagged in (((10, 20), 0), ((10, 65), ops.YR_DEVERR_CTX_LENS)):
+        cl = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+        out, lse = ops.attn_prefill_chunk(q, kc, vc, cu, cl, 1, th_dev, scale, workspace=ws)
+        assert tuple(out.shape) == (0, cfg.hq, cfg.head_dim) and tuple(lse.shape) == (cfg.hq, 0)
+        assert ops.read_device_error(ws) == flagged
+
+
 # ------------------------------------------------------------ windowed decode
 def _decode_run(inp, cfg, window, sinks, q_pos=None, out_dtype=ops.YR_F32):
     dt = inp["dtype"]

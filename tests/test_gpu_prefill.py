@@ -196,6 +196,60 @@ def test_deterministic_under_permuted_order(lens, hq, hkv):
     assert max_abs(np.stack([got[t, h] for t, h in rows]), ro) <= BF16_TOL
 
 
+@pytest.mark.parametrize("dtype,lens,window,sinks", [
+    ("bf16", (0, 300, 0, 1, 0, 129, 0), 0, 0),
+    ("bf16", (0, 300, 0, 1, 0, 129, 0), 64, 2),
+    ("f32", (0, 65, 0, 3), 0, 0),
+])
+def test_zero_length_sequences(dtype, lens, window, sinks):
+    """Empty sequences anywhere in the batch produce nothing and leave the
+    others' rows as the oracle gives them."""
+    hq, hkv, D = 8, 2, 128
+    cfg = wl.PrefillConfig("t", 66, lens, hq, hkv, D, dtype, 500000.0, 8.0, 64)
+    inp = wl.make_prefill(cfg)
+    say(f"prefill {dtype} with empty sequences lens={lens} W={window} S={sinks}")
+    th_dev, scale = lib_theta(D, cfg.base, cfg.factor, cfg.original_max_position)
+    ws = torch.empty(ops.attn_prefill_workspace_bytes(sum(lens), hkv, D,
+                                                      ops.YR_BF16 if dtype == "bf16" else ops.YR_F32),
+                     dtype=torch.uint8, device="cuda")
+    out, lse = ops.attn_prefill_fwd(to_dev(inp["q"], dtype), to_dev(inp["k"], dtype),
+                                    to_dev(inp["v"], dtype),
+                                    torch.from_numpy(inp["cu_seqlens"]).cuda(), max(lens), th_dev,
+                                    scale, window=window, sinks=sinks, workspace=ws)
+    assert ops.read_device_error(ws) == 0
+    th, sc = oracle_theta(D, cfg.base, cfg.factor, cfg.original_max_position)
+    ro, rl = oatt.prefill(wl.as_f64(inp["q"], dtype), wl.as_f64(inp["k"], dtype),
+                          wl.as_f64(inp["v"], dtype), inp["cu_seqlens"], th, sc,
+                          window=window, sinks=sinks)
+    tol = F32_TOL if dtype == "f32" else BF16_TOL
+    e_out, e_lse = max_abs(to_f64(out), ro), max_abs(lse.cpu().numpy(), rl)
+    print(f"max-abs out {e_out:.3e} lse {e_lse:.3e}")
+    assert e_out <= tol and e_lse <= tol
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_empty_batch(dtype):
+    """T = 0: every sequence empty.  The call succeeds (the empty tensors'
+    NULL data pointers are accepted), writes nothing, and still checks
+    cu_seqlens on the device."""
+    hq, hkv, D = 8, 2, 128
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.empty((0, hq, D), dtype=tdt, device="cuda")
+    k = torch.empty((0, hkv, D), dtype=tdt, device="cuda")
+    v = torch.empty((0, hkv, D), dtype=tdt, device="cuda")
+    th_dev, scale = lib_theta(D, 500000.0, 8.0, 16384)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    say(f"prefill {dtype} empty batch")
+    cu = torch.zeros(4, dtype=torch.int32, device="cuda")
+    out, lse = ops.attn_prefill_fwd(q, k, v, cu, 1, th_dev, scale, workspace=ws)
+    assert tuple(out.shape) == (0, hq, D) and tuple(lse.shape) == (hq, 0)
+    assert ops.read_device_error(ws) == 0
+    # a cu_seqlens that does not end at T = 0 is still flagged
+    bad = torch.tensor([0, 5], dtype=torch.int32, device="cuda")
+    ops.attn_prefill_fwd(q, k, v, bad, 5, th_dev, scale, workspace=ws)
+    assert ops.read_device_error(ws) == ops.YR_DEVERR_CU_SEQLENS
+
+
 def test_bad_cu_seqlens_sets_device_flag():
     T, hq, hkv, D = 256, 4, 2, 128
     th_dev, scale = lib_theta(D, 10000.0, 4.0, 64)

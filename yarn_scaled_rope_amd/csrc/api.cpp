@@ -300,7 +300,8 @@ int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
     return fail(YR_ERR_INVALID, "attn_prefill_fwd: softmax_scale must be finite and > 0");
   if (window < 0 || sinks < 0) return fail(YR_ERR_INVALID, "attn_prefill_fwd: window and sinks must be >= 0");
-  if (!q || !k || !v || !cu_seqlens || !out || !workspace)
+  // an empty batch (T = 0) reads and writes no rows: its data pointers may be NULL
+  if (!cu_seqlens || !workspace || ((!q || !k || !v || !out) && T > 0))
     return fail(YR_ERR_NULL, "attn_prefill_fwd: q, k, v, cu_seqlens, out and workspace are required");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return fail(YR_ERR_WORKSPACE, "attn_prefill_fwd: workspace must be 256-byte aligned");
@@ -389,7 +390,9 @@ int attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cache, 
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
     return fail(YR_ERR_INVALID, "attn_prefill_chunk: softmax_scale must be finite and > 0");
   if (window < 0 || sinks < 0) return fail(YR_ERR_INVALID, "attn_prefill_chunk: window and sinks must be >= 0");
-  if (!q || !k_cache || !v_cache || !cu_seqlens_q || !ctx_lens || !out || !workspace)
+  // no new token (Tq = 0): nothing is read or written, so q, the caches and out may be NULL
+  if (!cu_seqlens_q || !ctx_lens || !workspace ||
+      ((!q || !k_cache || !v_cache || !out) && Tq > 0))
     return fail(YR_ERR_NULL, "attn_prefill_chunk: q, caches, cu_seqlens_q, ctx_lens, out and "
                              "workspace are required");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
