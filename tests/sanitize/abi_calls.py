@@ -58,6 +58,18 @@ def main(path):
         assert st != ops.YR_OK, (kw, st)
         assert lib.yr_last_error()
         n += 1
+    # an empty batch passes validation with NULL data pointers (the stubbed
+    # launch then reports no device); one row with them does not
+    for T, want in ((0, ops.YR_ERR_HIP), (1, ops.YR_ERR_NULL)):
+        a = dict(q=None, k=None, v=None, in_dtype=1, cu=F, B=2, max_seqlen=1, T=T, Hq=8, Hkv=2,
+                 D=128, theta=F, flags=0, scale=0.1, window=0, sinks=0, out=None, out_dtype=1,
+                 lse=None, ws=F, ws_bytes=1 << 30, stream=None)
+        assert lib.attn_prefill_fwd(*a.values()) == want, T
+        a = dict(q=None, kc=None, vc=None, in_dtype=1, cu=F, ctx=F, B=2, max_seqlen=1, Tq=T,
+                 Lmax=64, Hq=8, Hkv=2, D=128, theta=F, scale=0.1, window=0, sinks=0, out=None,
+                 out_dtype=1, lse=None, ws=F, ws_bytes=256, stream=None)
+        assert lib.attn_prefill_chunk(*a.values()) == want, T
+        n += 2
     for kw in (dict(), dict(D=80), dict(max_seqlen=4096, Lmax=1024), dict(ctx=None), dict(window=7, sinks=2)):
         a = dict(q=F, kc=F, vc=F, in_dtype=1, cu=F, ctx=F, B=2, max_seqlen=64, Tq=100, Lmax=1024, Hq=8,
                  Hkv=2, D=128, theta=F, scale=0.1, window=0, sinks=0, out=F, out_dtype=1, lse=F, ws=F,
