@@ -332,3 +332,29 @@ def test_library_yarn_ramp_midpoint(lib, s):
     assert abs(f64[1] - want) <= 4 * np.spacing(want)
     assert f64[0] == 1.0     # pair 0 turns L / 2 pi > beta times: unscaled
     assert t == pytest.approx(0.1 * math.log(s) + 1.0, rel=1e-15)
+
+
+def test_last_error_is_per_thread(lib):
+    """Each thread reads the message of its own last failing call: threads
+    that fail in different ways at once keep their own messages."""
+    import threading
+    barrier = threading.Barrier(4)
+    seen = {}
+
+    def worker(i):
+        kw = (dict(D=96), dict(Hq=6, Hkv=4), dict(window=-1), dict(ws_bytes=100))[i]
+        barrier.wait()
+        for _ in range(200):
+            st = prefill_call(lib, **kw)
+            msg = lib.yr_last_error()
+        seen[i] = (st, msg)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert [seen[i][0] for i in range(4)] == [ops.YR_ERR_UNSUPPORTED, ops.YR_ERR_INVALID,
+                                              ops.YR_ERR_INVALID, ops.YR_ERR_WORKSPACE]
+    assert b"head_dim" in seen[0][1] and b"Hq" in seen[1][1]
+    assert b"window" in seen[2][1] and b"workspace" in seen[3][1]
