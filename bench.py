@@ -40,10 +40,12 @@ Other modes:
                               matrix-core utilisation, MFMA FLOPs and shader
                               clock of each dispatch when the counters for
                               them are there
-    --counters-json FETCH_DIR WRITE_DIR [--command "c1 ;; c2"]
+    --counters-json FETCH_DIR WRITE_DIR [--command "c1 ;; c2"] [--counters-row ROW]
                               HBM bytes per launch of the prefill and decode
                               kernels from FETCH_SIZE / WRITE_SIZE runs of
-                              `bench.py --copy-probe`, into profiles/
+                              `bench.py --copy-probe`, into profiles/; with
+                              --counters-row, of one next row's kernels from
+                              runs of `bench.py --only-next ROW --copy-probe`
 """
 
 from __future__ import annotations
@@ -82,6 +84,34 @@ def source_digest(paths) -> str:
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+# The kernels of each next row, for its counter summary: (kind, workload,
+# the row kernel's name up to its distinguishing template arguments, the
+# kernel launched after each of its dispatches in the same call or None,
+# sources, note).  In a run of `--only-next ROW` (with --no-decode for the
+# 256-sequence row, whose split kernel is the decode line's) the row kernel's
+# dispatches are that row's alone.
+NEXT_COUNTER_ROWS = {
+    "chunked_prefill": ("prefill_bf16", "llama3_8b_chunked_prefill_4x4k",
+                        "prefill_bf16_kernel<128, false, true, true>", None, ATTN_SOURCES,
+                        "one attn_prefill_chunk launch"),
+    "window_prefill": ("prefill_bf16", "llama2_7b_prefill_16k_window4k_sinks4",
+                       "prefill_bf16_kernel<128, false, true, true>", None, ATTN_SOURCES,
+                       "one windowed attn_prefill_fwd launch (keys pre-rotated)"),
+    "window_decode": ("decode", "decode_b16_gqa_window4k_sinks4",
+                      "decode_mfma_kernel<128, 4, 1, false, true, true, false>",
+                      "decode_merge_kernel", DECODE_SOURCES,
+                      "split + merge kernels of one windowed attn_decode call"),
+    "fp8_decode": ("decode", "decode_b16_gqa_32k_128k_fp8_e4m3",
+                   "decode_mfma_kernel<128, 8, 2, true, false, false, true>",
+                   "decode_merge_kernel", DECODE_SOURCES,
+                   "split + merge kernels of one attn_decode_fp8 call"),
+    "large_batch_decode": ("decode", "decode_b256_gqa_512_4k",
+                           "decode_mfma_kernel<128, 4, 2, false, false, false, true>",
+                           "decode_merge_kernel", DECODE_SOURCES,
+                           "split + merge kernels of one attn_decode call"),
+}
 
 
 def log(msg: str):
@@ -497,15 +527,16 @@ def bench_next(args, torch, ops, wl, pstate, dstate):
             "sample": f"fp64 decode of sequences 0-31 of the same {lb.name} inputs, "
                       f"{passes} whole passes"}
     del fp8_state
-    # the roofline object of each row, in the main line's form (no counters
-    # are taken for these paths: traffic null)
-    for row in res.values():
+    # the roofline object of each row, in the main line's form; traffic from
+    # the row's counter summary when it matches the kernel sources
+    for name, row in res.items():
         hbm = row["unit"] == "GB/s"
+        kind, wname, _, _, srcs, _ = NEXT_COUNTER_ROWS[name]
         row["roofline"] = {"bound": "hbm" if hbm else "mfma", "achieved": row["value"],
                            "peak": PEAK_HBM_GBS if hbm else PEAK_BF16_TFLOPS,
                            "unit": row["unit"],
                            "frac": row["frac_hbm_peak" if hbm else "frac_mfma_peak"],
-                           "traffic": None}
+                           "traffic": traffic_from_profiles(kind, wname, source_digest(srcs))}
     return res
 
 
@@ -819,13 +850,16 @@ def summarize(dirnames: str, out_path: str, command: str):
     print(out_path)
 
 
-def counters_json(fetch_dir: str, write_dir: str, workload: str, commands):
+def counters_json(fetch_dir: str, write_dir: str, workload: str, commands, row=None):
     """Per-launch HBM bytes of the prefill and decode kernels from two
     rocprofv3 --pmc runs of `bench.py --copy-probe` (FETCH_SIZE, WRITE_SIZE;
     KiB per dispatch).  Each counter is scaled by what it reads for the 1 GiB
     device copy of the probe (WRITE_SIZE of that copy picks it out; FETCH_SIZE
     is taken from the same kernel in the other run).  Writes
-    profiles/{kind}_{workload}_hbm_counters.json for both kernels."""
+    profiles/{kind}_{workload}_hbm_counters.json for both kernels, or with
+    `row` for that next row's kernels only (NEXT_COUNTER_ROWS): the row
+    kernel's dispatches, plus the dispatch right after each of them when the
+    row has a second kernel."""
     import csv
 
     def load(d, counter):
@@ -852,6 +886,36 @@ def counters_json(fetch_dir: str, write_dir: str, workload: str, commands):
     def mean(rows, key):
         v = [x[2] for x in rows if key in x[1]]
         return sum(v) / len(v) if v else None
+
+    def follower_mean(rows, key, nxt):
+        # the dispatch that follows each `key` dispatch, when it is `nxt`
+        v = [rows[i + 1][2] for i in range(len(rows) - 1)
+             if key in rows[i][1] and nxt in rows[i + 1][1]]
+        return sum(v) / len(v) if v else None
+
+    if row is not None:
+        kind, wname, key, nxt, srcs, note = NEXT_COUNTER_ROWS[row]
+        keys = [key] + ([nxt] if nxt else [])
+        f_kib = [mean(fetch, key)] + ([follower_mean(fetch, key, nxt)] if nxt else [])
+        w_kib = [mean(write, key)] + ([follower_mean(write, key, nxt)] if nxt else [])
+        if any(x is None for x in f_kib + w_kib):
+            raise SystemExit(f"no dispatches of {keys} in the counter files")
+        names = [k.split("<")[0] for k in keys]
+        per_kernel = {n: int(round((fk * scale_fetch + wk * scale_write) * 1024))
+                      for n, fk, wk in zip(names, f_kib, w_kib)}
+        d = {"kernel": " + ".join(keys), "workload": wname, "source_digest": source_digest(srcs),
+             "fetch_kib_per_dispatch_raw": dict(zip(names, f_kib)),
+             "write_kib_per_dispatch_raw": dict(zip(names, w_kib)),
+             "copy_probe": {"kernel": copy[1][:100], "bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                            "fetch_kib": copy_fetch, "write_kib": copy[2]},
+             "scale_fetch": scale_fetch, "scale_write": scale_write,
+             "hbm_bytes_per_launch": sum(per_kernel.values()), "bytes_per_kernel": per_kernel,
+             "commands": list(commands), "note": note}
+        path = os.path.join(ROOT, "profiles", f"{kind}_{wname}_hbm_counters.json")
+        with open(path, "w") as fh:
+            json.dump(d, fh, indent=1)
+        print(path)
+        return
 
     kinds = {
         "prefill_bf16": (workload, ["prefill_bf16_kernel"], ATTN_SOURCES,
@@ -904,11 +968,12 @@ def main():
     ap.add_argument("--counters-json", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None)
     ap.add_argument("--out", default=None)
     ap.add_argument("--command", default="")
+    ap.add_argument("--counters-row", default=None, choices=sorted(NEXT_COUNTER_ROWS))
     args = ap.parse_args()
 
     if args.counters_json:
         counters_json(args.counters_json[0], args.counters_json[1], args.workload,
-                      args.command.split(" ;; ") if args.command else [])
+                      args.command.split(" ;; ") if args.command else [], args.counters_row)
         return 0
     if args.summarize:
         summarize(args.summarize, args.out or "summary.txt", args.command)

@@ -155,3 +155,50 @@ def test_counters_json_scales_by_the_copy_and_sums_kernels(tmp_path, monkeypatch
     assert d["bytes_per_kernel"]["decode_mfma_kernel"] == int(round((500 * 2 + 1) * 1024))
     assert d["bytes_per_kernel"]["decode_merge_kernel"] == int(round((10 * 2 + 2) * 1024))
     assert d["hbm_bytes_per_launch"] == sum(d["bytes_per_kernel"].values())
+
+
+def test_counters_json_of_a_next_row_pairs_each_split_with_its_merge(tmp_path, monkeypatch):
+    bench = _bench()
+    for rel in set(bench.ATTN_SOURCES + bench.DECODE_SOURCES):
+        p = tmp_path / rel
+        p.parent.mkdir(parents=True, exist_ok=True)
+        p.write_text("// placeholder\nint x;\n")
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    gib_kib = (1 << 30) / 1024
+    copy = "__amd_rocclr_copyBuffer"
+    main = "void yr::(anonymous namespace)::decode_mfma_kernel<128, 4, 2, false, false, false, true>(x)"
+    win = "void yr::(anonymous namespace)::decode_mfma_kernel<128, 4, 1, false, true, true, false>(x)"
+    mrg = "void yr::(anonymous namespace)::decode_merge_kernel<128, false, false>(x)"
+    # the decode line's split + merge, then two windowed calls: only the merges
+    # that follow a windowed split count for the row
+    fetch = [(1, copy, gib_kib), (2, main, 9000.0), (3, mrg, 700.0), (4, win, 100.0),
+             (5, mrg, 7.0), (6, win, 300.0), (7, mrg, 9.0)]
+    write = [(1, copy, gib_kib), (2, main, 5.0), (3, mrg, 70.0), (4, win, 1.0), (5, mrg, 2.0),
+             (6, win, 3.0), (7, mrg, 4.0)]
+    for d, rows, cname in (("fetch", fetch, "FETCH_SIZE"), ("write", write, "WRITE_SIZE")):
+        _write_csv(str(tmp_path / d / "run_counter_collection.csv"),
+                   [{"Dispatch_Id": i, "Kernel_Name": k, "Counter_Name": cname, "Counter_Value": v}
+                    for i, k, v in rows])
+    bench.counters_json(str(tmp_path / "fetch"), str(tmp_path / "write"), "unused", ["synthetic"],
+                        row="window_decode")
+    p = json.load(open(tmp_path / "profiles" / "decode_decode_b16_gqa_window4k_sinks4_hbm_counters.json"))
+    assert p["scale_fetch"] == pytest.approx(1.0) and p["scale_write"] == pytest.approx(1.0)
+    assert p["bytes_per_kernel"]["decode_mfma_kernel"] == int(round((200 + 2) * 1024))
+    assert p["bytes_per_kernel"]["decode_merge_kernel"] == int(round((8 + 3) * 1024))
+    assert p["hbm_bytes_per_launch"] == sum(p["bytes_per_kernel"].values())
+    assert p["source_digest"] == bench.source_digest(bench.DECODE_SOURCES)
+    # and the row's roofline reads it back for the same sources
+    kind, wname, _, _, srcs, _ = bench.NEXT_COUNTER_ROWS["window_decode"]
+    assert bench.traffic_from_profiles(kind, wname, bench.source_digest(srcs)) == \
+        p["hbm_bytes_per_launch"]
+    assert bench.traffic_from_profiles(kind, wname, "0" * 16) is None
+
+
+def test_next_counter_rows_name_the_bench_rows():
+    bench = _bench()
+    assert set(bench.NEXT_COUNTER_ROWS) == {"chunked_prefill", "window_prefill", "window_decode",
+                                            "fp8_decode", "large_batch_decode"}
+    names = {r[1] for r in bench.NEXT_COUNTER_ROWS.values()}
+    assert {wl.CHUNK_4X4K.name, wl.LLAMA2_7B_16K_SWA.name, wl.DECODE_B16_SWA.name,
+            wl.DECODE_B256.name, wl.DECODE_B16.name + "_fp8_e4m3"} == names
