@@ -1,4 +1,4 @@
-// bf16 causal prefill on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
+// bf16 causal prefill on gfx950 matrix cores (v_mfma_f32_16x16x32_bf16).
 //
 // Method: scaled dot-product attention with the causal rule ("Arch 03 --
 // Long Context", attention slide; ALiBi slide for i - j >= 0), tiled with an
@@ -8,16 +8,23 @@
 // chip).  Queries are rotated on load with fp64 angles; keys arrive rotated.
 //
 // Work decomposition (one workgroup = 8 waves = 256 query rows of one head):
-//   * Every wave owns 32 consecutive query rows.  Scores are formed
-//     transposed, S^T = K * Q^T, so the 32x32 accumulator of a lane holds ONE
-//     query (lane % 32) against 16 keys; the row max and row sum need only
-//     the lane's own registers plus one exchange with lane ^ 32.
-//   * The output is also formed transposed, O^T = V^T * P^T, so the lane that
-//     owns a query owns its output column and its rescale factor.
-//   * P^T goes straight from the score accumulator into the B operand: the
-//     8 accumulator registers 8*(ks%2)..+7 of key block ks/2 are one 16-key
-//     k-step.  The V^T operand comes from transposing LDS reads
-//     (ds_read_b64_tr_b16) whose key order matches that register order.
+//   * Every wave owns 32 consecutive query rows, as two 16-row blocks.
+//     Scores are formed transposed, S^T = K * Q^T, in 16x16 blocks: lane l
+//     holds rows l % 16 of both row blocks against 4 keys of each 16-key
+//     block, so a row's keys lie in the four lanes l % 16 + 16 g, which
+//     exchange values only for the row max of the slow path and the row sum
+//     at the end.  Each K fragment feeds the MFMAs of both row blocks.
+//   * The output is also formed transposed, O^T = V^T * P^T, so the lanes
+//     that own a row own its output columns and its rescale factor.
+//   * P^T goes straight from the score accumulators into the B operand: the
+//     4 + 4 accumulator values of key blocks 2p and 2p+1 are one 32-key
+//     k-step (k-position 8 g + e stands for key 16 (2p + e/4) + 4 g + e%4).
+//     The V^T operand comes from two transposing LDS reads
+//     (ds_read_b64_tr_b16) per k-step whose key order matches.
+//   * The 16x16x32 shape rather than 32x32x16: with random operands the part
+//     runs this kernel at its power limit, and the smaller shape moves fewer
+//     accumulator bits per FLOP (a probe of back-to-back MFMAs with N(0,1)
+//     bf16 operands: 2.09 against 1.85 PFLOP/s).
 //   * K and V tiles (64 keys) are copied from HBM straight into LDS
 //     (buffer_load ... lds): no staging registers, no VALU, no LDS writes.
 //     Each lane fetches the source chunk that belongs in its LDS slot, which
@@ -49,7 +56,7 @@ namespace yr {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -59,19 +66,33 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 512;
 constexpr int kBQ = kThreads / 2;  // query rows per workgroup (32 per wave)
 constexpr int kBC = 64;            // keys per tile
-constexpr int KB = kBC / 32;       // 32-key blocks of a tile (score accumulators)
-constexpr int KS = kBC / 16;       // 16-key k-steps of a tile (P fragments)
+constexpr int NKB = kBC / 16;      // 16-key blocks of a tile (score accumulators)
+constexpr int NPS = kBC / 32;      // 32-key k-steps of the PV product
+constexpr int RB = 2;              // 16-row blocks of a wave's 32 query rows
 constexpr int kXcds = 8;
 constexpr int kMaxRankedSeqs = 64;  // chunked prefill orders up to this many sequences
 constexpr float kLn2 = 0.69314718055994530942f;
 
-// V chunk swizzle by key row mod 4: for 16 lanes of a transposing read (4 key
-// rows x 2 chunks) the 8 slots are distinct mod 8 (32 banks) and, with 16
-// chunks per row, the 32 lanes of both 16-column halves are distinct mod 16
-// (64 banks).
+// V chunk swizzle by key row mod 8.  Half a wave of transposing reads takes
+// 8 consecutive key rows x the 2 chunks of 16 head dims; slot = chunk ^ vswz
+// puts those 16 (row, chunk) pairs on 16 distinct 4-bank groups of the 64
+// banks: with 16 chunks per row (256 bytes) vswz = 2 (row % 8), with 8 chunks
+// (two 128-byte rows per bank line) vswz = row % 8 rounded down to even, for
+// the 4 rows of each parity.
 template <int CH>
-__device__ __forceinline__ int vswz(int e) {
-  return CH >= 16 ? ((2 * e) ^ (8 * (e & 1))) : 2 * e;
+__device__ __forceinline__ int vswz(int r8) {
+  return CH >= 16 ? 2 * r8 : (r8 & 6);
+}
+
+// The four lanes l16 + 16 g4 (one query row) combined: each gets their max /
+// sum.
+__device__ __forceinline__ float quarter_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float quarter_sum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -250,8 +271,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     long long T, int Hq, int Hkv, const double *__restrict__ theta, float scale_log2,
     void *__restrict__ out, float *__restrict__ lse, int ntiles, int *flag, int kv_len,
     const int *__restrict__ ctx, int window, int sinks, int permuted) {
-  constexpr int KSTEPS = D / 16;     // MFMA k-steps over the head dim
-  constexpr int DBLK = D / 32;       // 32-row blocks of O^T
+  constexpr int KQ = D / 32;         // score MFMA k-steps over the head dim
+  constexpr int DB = D / 16;         // 16-row blocks of O^T (head dims)
   constexpr int CH = D / 8;          // 16-byte chunks per row
   constexpr int RPI = 64 / CH;       // rows per 1 KB tile copy instruction
   constexpr int DPW = kBC / RPI / (kThreads / 64);  // copy instructions per wave per tile
@@ -330,10 +351,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
   const int tw0 = q0 + wave * 32;  // first query row of this wave
-  const int tq = tw0 + l32;        // this lane's query row
 
   // Keys: packed like q (kv_len == 0), or a [B, kv_len, Hkv, D] cache whose
   // first P rows precede this chunk: query row i then sits at position P + i
@@ -353,18 +373,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   // Copy instruction p of a tile fills LDS bytes [1024p, 1024p + 1024) in lane
   // order: lane l lands on row p*RPI + l/CH, slot l%CH, so it fetches the
   // source chunk that belongs in that slot.  K: slot = chunk ^ (row % CH);
-  // V: slot = chunk ^ vswz(row % 4).  Rows past the sequence end read 0.
+  // V: slot = chunk ^ vswz(row % 8).  Rows past the sequence end read 0.
   const uint16_t *kseq = k + (krow0 * Hkv + hk) * (long long)D;
   const uint16_t *vseq = v + (krow0 * Hkv + hk) * (long long)D;
   const uint32_t rbytes = (uint32_t)(rstride * 2);
   const int drow = lane / CH, dslot = lane % CH;
-  uint32_t koff[DPW];
+  uint32_t koff[DPW], voff[DPW];
 #pragma unroll
   for (int i = 0; i < DPW; ++i) {
     const int row = (wave * DPW + i) * RPI + drow;
     koff[i] = drow * rbytes + 16 * (dslot ^ (row & (CH - 1)));
+    voff[i] = drow * rbytes + 16 * (dslot ^ vswz<CH>(row & 7));
   }
-  const uint32_t voff = drow * rbytes + 16 * (dslot ^ vswz<CH>(drow & 3));
   auto copy_tile = [&](uint16_t *dst, const uint16_t *seq, int t, bool is_v) YR_INLINE {
     const int key0 = t * kBC;
     const __amdgpu_buffer_rsrc_t rs =
@@ -373,7 +393,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     for (int i = 0; i < DPW; ++i) {
       const int p = wave * DPW + i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (YR_LDS void *)(dst + p * 512), 16,
-                                               (int)(is_v ? voff : koff[i]),
+                                               (int)(is_v ? voff[i] : koff[i]),
                                                (int)(p * RPI * rbytes), 0, 0);
     }
   };
@@ -424,15 +444,20 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   });
 
   // ---- Q fragments (B operand of S^T = K Q^T), rotated on load -----------
-  bf16x8 qf[KSTEPS];
-  {
-    const bool qvalid = tq < n;
-    const uint16_t *qp = q + ((s0 + (qvalid ? tq : 0)) * Hq + h) * (long long)D + hh * 8;
+  // Lane l holds query rows tq[rb] = tw0 + 16 rb + l16 (rb = 0, 1) and, for
+  // k-step ks, head dims 32 ks + 8 g4 .. +7.
+  bf16x8 qf[RB][KQ];
+  int tq[RB];
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
+  for (int rb = 0; rb < RB; ++rb) {
+    tq[rb] = tw0 + 16 * rb + l16;
+    const bool qvalid = tq[rb] < n;
+    const uint16_t *qp = q + ((s0 + (qvalid ? tq[rb] : 0)) * Hq + h) * (long long)D + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < KQ; ++ks) {
       u32x4 w = {0u, 0u, 0u, 0u};
       if (qvalid) {
-        w = *reinterpret_cast<const u32x4 *>(qp + kk * 16);
+        w = *reinterpret_cast<const u32x4 *>(qp + ks * 32);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           // the logit scale (log2 units) folded into the query before its one
@@ -440,41 +465,51 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
           // ready for exp2
           float x0 = bf16_to_f32(w[e] & 0xffffu), x1 = bf16_to_f32(w[e] >> 16);
           if (ROTATE_Q) {
-            float c, s;
-            rope_cos_sin((double)(P + tq), theta[kk * 8 + hh * 4 + e], &c, &s);
-            rotate_pair(x0, x1, c, s);
+            float c, sn;
+            rope_cos_sin((double)(P + tq[rb]), theta[ks * 16 + g4 * 4 + e], &c, &sn);
+            rotate_pair(x0, x1, c, sn);
           }
           w[e] = pack_bf16x2(x0 * scale_log2, x1 * scale_log2);
         }
       }
-      qf[kk] = as_bf16x8(w);
+      qf[rb][ks] = as_bf16x8(w);
     }
   }
 
-  f32x16 o[DBLK];
+  f32x4 o[DB][RB];
 #pragma unroll
-  for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY;
-  float l_part = 0.f;
-  // -m_run (0 while m_run = -inf) in every slot: the accumulator the score
+  for (int i = 0; i < DB; ++i)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) o[i][rb] = f32x4{};
+  float m_run[RB], l_part[RB];
+  // -m_run (0 while m_run = -inf) in every slot: the accumulators the score
   // MFMAs start from, so that they return s * scale - m directly
-  f32x16 negm = f32x16{};
-
-  // LDS operand addresses (elements).  K: row kb*32 + l32, chunk 2kk + hh.
-  // V^T (transposing reads): lane t of a 16-lane group reads 4 elements of key
-  // row 4*hh + (t >> 2) (+32 kb + 16 ks' + 8 r) at columns 32*db + 16*group
-  // parity + 4*(t & 3), and receives column t of 4 consecutive key rows.
-  const int kx = l32 & (CH - 1);
-  int vbase[DBLK];
-  {
-    const int t16 = lane & 15;
-    const int vrow = 4 * hh + (t16 >> 2);
-    const int vx = vswz<CH>(t16 >> 2);
-    const int vcol = 2 * ((lane >> 4) & 1) + ((t16 & 3) >> 1);
+  f32x4 negm[RB];
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db)
-      vbase[db] = vrow * D + 8 * ((4 * db + vcol) ^ vx) + 4 * (t16 & 1);
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_part[rb] = 0.f;
+    negm[rb] = f32x4{};
   }
+
+  // LDS operand addresses (elements).  K: row 16 kb + l16, chunk 4 ks + g4.
+  // V^T (transposing reads): lane t = l16 of group g4 reads 4 elements of key
+  // row 4 g4 + (t >> 2) (+16 kb) at head dims 16 db + 4 (t & 3) and receives
+  // head dim 16 db + t of 4 consecutive key rows.
+  const int kx = l16 & (CH - 1);
+  const int vrow = 4 * g4 + (l16 >> 2);
+  // element offset of the lane's V^T read for head-dim block db:
+  // vrow * D + 8 * ((2 db + (l16 & 3) / 2) ^ vswz(vrow % 8)) + 4 (l16 & 1).
+  // With 16 chunks a row, vswz = 2 (vrow % 8) only flips the bits of 2 db, so
+  // the offset is vbase ^ (16 db): one base register for every block.
+  const int vbase = vrow * D + 8 * ((((l16 & 3) >> 1)) ^ vswz<CH>(vrow & 7)) + 4 * (l16 & 1);
+  auto voffs = [&](int vb, int db) YR_INLINE {
+    if constexpr (CH >= 16) {
+      return vb ^ (16 * db);
+    } else {
+      return vrow * D + 8 * ((2 * db + ((l16 & 3) >> 1)) ^ vswz<CH>(vrow & 7)) + 4 * (l16 & 1);
+    }
+  };
 
   // ---- per-tile work -------------------------------------------------------
   // Tile j has keys j*64 .. j*64+63.  The wave (rows tw0 .. tw0+31, positions
@@ -486,17 +521,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     return window == 0 || j * kBC + kBC - 1 > P + tw0 - window || j * kBC < sinks;
   };
 
-  // S^T = K Q^T for one tile (two 32-key blocks); accumulator slot rr of block
-  // kb (lane half hh) holds key 32 kb + 8 (rr >> 2) + 4 hh + (rr & 3)
-  auto scores = [&](auto par, f32x16 (&s)[KB]) YR_INLINE {
-    const uint16_t *ks = kst(par);
+  // S^T = K Q^T for one tile (four 16-key blocks by two 16-row blocks); slot
+  // r of accumulator [kb][rb] holds key 16 kb + 4 g4 + r of row tq[rb].  Each
+  // K fragment feeds the MFMAs of both row blocks.
+  auto scores = [&](auto par, f32x4 (&s)[NKB][RB]) YR_INLINE {
+    const uint16_t *ks_ = kst(par);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        const bf16x8 a = as_bf16x8(
-            *reinterpret_cast<const u32x4 *>(ks + (kb * 32 + l32) * D + 8 * ((2 * kk + hh) ^ kx)));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], kk == 0 ? negm : s[kb], 0, 0, 0);
+      for (int ks = 0; ks < KQ; ++ks) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+            ks_ + (kb * 16 + l16) * D + 8 * ((4 * ks + g4) ^ kx)));
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          s[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rb][ks],
+                                                              ks == 0 ? negm[rb] : s[kb][rb], 0, 0,
+                                                              0);
       }
     }
   };
@@ -506,57 +546,76 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   // the tile's P are at most 1 afterwards.  The tile's scores and the
   // already issued scores of the next tile (nx, computed against the old
   // reference) shift with it, and O and the row sum are rescaled.  A row that
-  // has seen no visible key keeps -inf (alpha 1).
-  auto move_reference = [&](f32x16 (&s)[KB], f32x16 (&nx)[KB]) YR_INLINE {
-    float mx = -INFINITY;
+  // has seen no visible key keeps -inf (alpha 1).  A row's 64 keys lie in the
+  // four lanes l16 + 16 g4, which exchange their maxima.
+  auto move_reference = [&](f32x4 (&s)[NKB][RB], f32x4 (&nx)[NKB][RB]) YR_INLINE {
+    float mx[RB];
+    bool grow[RB], first[RB];
+    bool any = false;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int rb = 0; rb < RB; ++rb) {
+      float x = -INFINITY;
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x = fmaxf(x, s[kb][rb][r]);
+      // the tile's row max less m_run (the scores carry -m_run already)
+      mx[rb] = quarter_max(x);
+      first[rb] = m_run[rb] == -INFINITY;
+      grow[rb] = first[rb] ? mx[rb] > -INFINITY : mx[rb] > 0.f;
+      any = any || grow[rb];
     }
-    // the tile's row max less m_run (the scores carry -m_run already)
-    mx = half_max(mx);
-    const bool first = m_run == -INFINITY;
-    const bool grow = first ? mx > -INFINITY : mx > 0.f;
-    if (__any(grow)) {
-      const float m_new = grow ? (first ? mx : m_run + mx) : m_run;
-      // 0 when m_run = -inf; 1 for a row that has seen no visible key yet
-      // (with a window a row can meet tiles it does not see at all)
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      // move this tile's scores to the new reference
-      const float shift = (first ? 0.f : m_run) - (m_new == -INFINITY ? 0.f : m_new);
-      m_run = m_new;
-      l_part *= alpha;
+    if (__any(any)) {
 #pragma unroll
-      for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
+      for (int rb = 0; rb < RB; ++rb) {
+        const float m_new = grow[rb] ? (first[rb] ? mx[rb] : m_run[rb] + mx[rb]) : m_run[rb];
+        // 0 when m_run = -inf; 1 for a row that has seen no visible key yet
+        // (with a window a row can meet tiles it does not see at all)
+        const float alpha =
+            m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        // move this tile's scores to the new reference
+        const float shift = (first[rb] ? 0.f : m_run[rb]) - (m_new == -INFINITY ? 0.f : m_new);
+        m_run[rb] = m_new;
+        l_part[rb] *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int i = 0; i < DB; ++i) o[i][rb] *= alpha;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          s[kb][rr] += shift;
-          nx[kb][rr] += shift;
-        }
-      const float nm = m_run == -INFINITY ? 0.f : -m_run;
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) negm[rr] = nm;
+          for (int r = 0; r < 4; ++r) {
+            s[kb][rb][r] += shift;
+            nx[kb][rb][r] += shift;
+          }
+        const float nm = m_run[rb] == -INFINITY ? 0.f : -m_run[rb];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) negm[rb][r] = nm;
+      }
     }
   };
 
-  // O^T += V^T P^T (k-step major: the MFMAs of k-step ks need only pf[ks]).
-  // Element e of the operands is key 16 ks + 4 hh + 8 (e >> 2) + (e & 3), the
-  // order in which the score accumulator holds P.
-  auto pv = [&](auto par, bf16x8 (&pf)[KS]) YR_INLINE {
+  // O^T += V^T P^T over two 32-key k-steps.  In k-step ps, k-position
+  // 8 g4 + e stands for key 16 (2 ps + e / 4) + 4 g4 + e % 4: the B operand is
+  // the lane's own P of key blocks 2 ps and 2 ps + 1, and the A operand is two
+  // transposing reads of those key rows.  Each V^T fragment feeds the MFMAs
+  // of both row blocks.
+  auto pv = [&](auto par, bf16x8 (&pf)[NPS][RB]) YR_INLINE {
     const uint16_t *vs = vst(par);
+    // an opaque copy of the base, so that the eight offsets are formed here
+    // (one XOR each) rather than held in registers across the loop
+    int vb = vbase;
+    asm volatile("" : "+v"(vb));
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ps = 0; ps < NPS; ++ps) {
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const uint16_t *ap = vs + vbase[db] + 16 * ks * D;
+      for (int db = 0; db < DB; ++db) {
+        const uint16_t *ap = vs + 32 * ps * D + voffs(vb, db);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YR_LDS i16x4 *)(ap));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YR_LDS i16x4 *)(ap + 8 * D));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((YR_LDS i16x4 *)(ap + 16 * D));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 w = {l2[0], l2[1], h2[0], h2[1]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), pf[ks], o[db], 0, 0, 0);
+        const bf16x8 a = as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[ps][rb], o[db][rb], 0, 0, 0);
       }
     }
   };
@@ -576,72 +635,98 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     if (i + NS < count) copy_tile(kst(par), kseq, tile_of(i + NS), false);
     if (i + NS - 1 < count) copy_tile(vst(prevp(par)), vseq, tile_of(i + NS - 1), true);
   };
-  // P = exp2(s - m) of a whole tile into bf16 fragments; returns the lane's
-  // sum of the tile's P (its 32 keys of its row)
-  auto exp_tile = [&](f32x16 (&s)[KB], bf16x8 (&pf)[KS]) YR_INLINE -> float {
-    float ts = 0.f;
+  // P = exp2(s - m) of a whole tile into bf16 fragments, in the B-operand
+  // order of pv; ts[rb] gets the lane's sum of row tq[rb]'s 16 P of the tile
+  auto exp_tile = [&](f32x4 (&s)[NKB][RB], bf16x8 (&pf)[NPS][RB], float (&ts)[RB]) YR_INLINE {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 w;
+    for (int rb = 0; rb < RB; ++rb) {
+      float t = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(s[ks >> 1][(ks & 1) * 8 + 2 * e]);
-        const float p1 = __builtin_amdgcn_exp2f(s[ks >> 1][(ks & 1) * 8 + 2 * e + 1]);
-        ts += p0 + p1;
-        w[e] = pack_bf16x2(p0, p1);
+      for (int ps = 0; ps < NPS; ++ps) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x4 &x = s[2 * ps + (e >> 1)][rb];
+          const float p0 = __builtin_amdgcn_exp2f(x[2 * (e & 1)]);
+          const float p1 = __builtin_amdgcn_exp2f(x[2 * (e & 1) + 1]);
+          t += p0 + p1;
+          w[e] = pack_bf16x2(p0, p1);
+        }
+        pf[ps][rb] = as_bf16x8(w);
       }
-      pf[ks] = as_bf16x8(w);
+      ts[rb] = t;
     }
-    return ts;
   };
   // Mask of a diagonal, window-edge, sink or tail tile: the keys of the tile
-  // this lane's row sees, as offsets c from the tile's first key, are
-  // c <= hi (causal, and inside the sequence) and c >= lo (inside the
-  // window), or c < se (a sink).  Slot rr of block kb holds offset
-  // 32 kb + 8 (rr >> 2) + 4 hh + (rr & 3); the lane half's 4 hh goes into
-  // the bounds, so each slot compares a constant.
-  auto apply_mask = [&](int j, f32x16 (&s)[KB]) YR_INLINE {
+  // row tq[rb] sees, as offsets c from the tile's first key, are c <= hi
+  // (causal, and inside the sequence) and c >= lo (inside the window), or
+  // c < se (a sink).  Slot r of block kb holds offset 16 kb + 4 g4 + r; the
+  // lane's 4 g4 goes into the bounds, so each slot compares a constant.
+  auto apply_mask = [&](int j, f32x4 (&s)[NKB][RB]) YR_INLINE {
     const int key0 = j * kBC;
-    const int pos = P + tq;
-    const int hi = min(pos, nk - 1) - key0 - 4 * hh;
-    if (window > 0) {
-      const int lo = pos - window + 1 - key0 - 4 * hh;
-      const int se = sinks - key0 - 4 * hh;
-      const unsigned span = (unsigned)(hi - lo);
-      if (key0 < sinks) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+    for (int rb = 0; rb < RB; ++rb) {
+      const int pos = P + tq[rb];
+      const int hi = min(pos, nk - 1) - key0 - 4 * g4;
+      if (window > 0) {
+        const int lo = pos - window + 1 - key0 - 4 * g4;
+        const int se = sinks - key0 - 4 * g4;
+        const unsigned span = (unsigned)(hi - lo);
+        if (key0 < sinks) {
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int c = kb * 32 + (rr >> 2) * 8 + (rr & 3);
-            const bool vis = c <= hi && (c >= lo || c < se);
-            s[kb][rr] = vis ? s[kb][rr] : -INFINITY;
-          }
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int c = kb * 16 + r;
+              const bool vis = c <= hi && (c >= lo || c < se);
+              s[kb][rb][r] = vis ? s[kb][rb][r] : -INFINITY;
+            }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int c = kb * 16 + r;
+              // lo <= c <= hi as one unsigned compare (empty when hi < lo)
+              const bool vis = hi >= lo && (unsigned)(c - lo) <= span;
+              s[kb][rb][r] = vis ? s[kb][rb][r] : -INFINITY;
+            }
+        }
       } else {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int c = kb * 32 + (rr >> 2) * 8 + (rr & 3);
-            // lo <= c <= hi as one unsigned compare (empty when hi < lo)
-            const bool vis = hi >= lo && (unsigned)(c - lo) <= span;
-            s[kb][rr] = vis ? s[kb][rr] : -INFINITY;
+          for (int r = 0; r < 4; ++r) {
+            const int c = kb * 16 + r;
+            s[kb][rb][r] = c <= hi ? s[kb][rb][r] : -INFINITY;
           }
       }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int c = kb * 32 + (rr >> 2) * 8 + (rr & 3);
-          s[kb][rr] = c <= hi ? s[kb][rr] : -INFINITY;
-        }
     }
+  };
+  // Optimistic softmax: exponentiate against the current reference first.
+  // Every P of the tile is at most 2^8 when the lane's tile sum is (P >= 0),
+  // which is the lazy-max bound; only when a sum exceeds it (or is not a
+  // number, or a row has no reference yet) does the wave take the row max,
+  // move the reference to it and exponentiate again.
+  auto softmax_pv = [&](auto par, f32x4 (&cur)[NKB][RB], f32x4 (&nxt)[NKB][RB]) YR_INLINE {
+    bf16x8 pf[NPS][RB];
+    float ts[RB];
+    exp_tile(cur, pf, ts);
+    bool slow = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) slow = slow || !(ts[rb] <= 256.f) || m_run[rb] == -INFINITY;
+    if (__any(slow)) {
+      move_reference(cur, nxt);
+      exp_tile(cur, pf, ts);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) l_part[rb] += ts[rb];
+    pv(par, pf);
   };
   // General step (diagonal, window-edge and tail tiles, the last step): every
   // check.  The mask goes first; then the same optimistic softmax as the
   // clear steps (a row that has seen no key yet takes the row max path).
-  auto step = [&](auto par, int i, f32x16 (&cur)[KB], f32x16 (&nxt)[KB]) YR_INLINE {
+  auto step = [&](auto par, int i, f32x4 (&cur)[NKB][RB], f32x4 (&nxt)[NKB][RB]) YR_INLINE {
     stage(par, i);
     if (i + 1 < count && active(tile_of(i + 1))) scores(nextp(par), nxt);
     if (active(tile_of(i))) {
@@ -649,52 +734,32 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       const int key0 = j * kBC;
       const bool wmask = window > 0 && key0 <= P + tw0 + 31 - window && key0 + kBC > sinks;
       if ((key0 + kBC - 1 > P + tw0) || (key0 + kBC > nk) || wmask) apply_mask(j, cur);
-      bf16x8 pf[KS];
-      float ts = exp_tile(cur, pf);
-      if (__any(!(ts <= 256.f) || m_run == -INFINITY)) {
-        move_reference(cur, nxt);
-        ts = exp_tile(cur, pf);
-      }
-      l_part += ts;
-      pv(par, pf);
+      softmax_pv(par, cur, nxt);
     }
   };
   // Clear step: tiles i and i+1 of the list need no mask for any row (below
   // the diagonal of the workgroup's first row, inside the window of its last
   // row) and every wave works on both, so the score MFMAs of tile i+1 go out
-  // first, right after the barrier, and the row max, exp / convert work of
-  // tile i and its PV MFMAs follow (measured 1-1.5% faster than issuing the
-  // scores after the row max).
-  auto step_clear = [&](auto par, int i, f32x16 (&cur)[KB], f32x16 (&nxt)[KB]) YR_INLINE {
+  // first, right after the barrier, and the exp / convert work of tile i and
+  // its PV MFMAs follow.
+  auto step_clear = [&](auto par, int i, f32x4 (&cur)[NKB][RB], f32x4 (&nxt)[NKB][RB]) YR_INLINE {
     stage(par, i);
     scores(nextp(par), nxt);
-    // Optimistic softmax: exponentiate against the current reference first.
-    // Every P of the tile is at most 2^8 when the lane's tile sum is (P >= 0),
-    // which is the lazy-max bound; only when a sum exceeds it (or is not a
-    // number, or the row has no reference yet) does the wave take the row
-    // max, move the reference to it and exponentiate again.
-    bf16x8 pf[KS];
-    float ts = exp_tile(cur, pf);
-    if (__any(!(ts <= 256.f) || m_run == -INFINITY)) {
-      move_reference(cur, nxt);
-      ts = exp_tile(cur, pf);
-    }
-    l_part += ts;
-    pv(par, pf);
+    softmax_pv(par, cur, nxt);
   };
 
   // prologue: every prologue copy landed; S(tile(0))
   wait_dma<0>();
   __syncthreads();
-  f32x16 sa[KB], sb[KB];
+  f32x4 sa[NKB][RB], sb[NKB][RB];
   if (active(tile_of(0))) scores(std::integral_constant<int, 0>{}, sa);
   // Steps are unrolled over the stage index (i % NS) and the score buffer
   // (i % 2), so every LDS array and register array is picked at compile time.
   constexpr int BL = 2;
-  auto sbuf = [&](auto ic) YR_INLINE -> f32x16(&)[KB] {
+  auto sbuf = [&](auto ic) YR_INLINE -> f32x4(&)[NKB][RB] {
     if constexpr (decltype(ic)::value % 2 == 0) return sa; else return sb;
   };
-  auto obuf = [&](auto ic) YR_INLINE -> f32x16(&)[KB] {
+  auto obuf = [&](auto ic) YR_INLINE -> f32x4(&)[NKB][RB] {
     if constexpr (decltype(ic)::value % 2 == 0) return sb; else return sa;
   };
   // The tiles that need no mask for any row form one run of the list: from
@@ -770,28 +835,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   for (; i < count; i += BL) general_block(i);
 
   // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ---------------------
-  const float l_tot = half_sum(l_part);
-  if (tq >= n) return;
-  const float inv = 1.f / l_tot;
-  const long long orow = ((s0 + tq) * Hq + h) * (long long)D;
+  // lane l holds head dims 16 db + 4 g4 .. +3 of row tq[rb]
 #pragma unroll
-  for (int db = 0; db < DBLK; ++db) {
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l_tot = quarter_sum(l_part[rb]);
+    if (tq[rb] >= n) continue;
+    const float inv = 1.f / l_tot;
+    const long long orow = ((s0 + tq[rb]) * Hq + h) * (long long)D;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int d0 = db * 32 + jj * 8 + hh * 4;
-      const float y0 = o[db][jj * 4 + 0] * inv, y1 = o[db][jj * 4 + 1] * inv;
-      const float y2 = o[db][jj * 4 + 2] * inv, y3 = o[db][jj * 4 + 3] * inv;
+    for (int db = 0; db < DB; ++db) {
+      const int d0 = db * 16 + 4 * g4;
+      const f32x4 y = o[db][rb] * inv;
       if (OUT_F32) {
-        *reinterpret_cast<float4 *>((float *)out + orow + d0) = make_float4(y0, y1, y2, y3);
+        *reinterpret_cast<float4 *>((float *)out + orow + d0) = make_float4(y[0], y[1], y[2], y[3]);
       } else {
         u32x2 pk;
-        pk[0] = pack_bf16x2(y0, y1);
-        pk[1] = pack_bf16x2(y2, y3);
+        pk[0] = pack_bf16x2(y[0], y[1]);
+        pk[1] = pack_bf16x2(y[2], y[3]);
         *reinterpret_cast<u32x2 *>((uint16_t *)out + orow + d0) = pk;
       }
     }
+    if (lse != nullptr && g4 == 0)
+      lse[(long long)h * T + s0 + tq[rb]] = (m_run[rb] + __log2f(l_tot)) * kLn2;
   }
-  if (lse != nullptr && hh == 0) lse[(long long)h * T + s0 + tq] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
 template <int D, bool OUT_F32, bool ROT, bool EXT>
