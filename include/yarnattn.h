@@ -209,7 +209,10 @@ size_t attn_prefill_workspace_bytes(long long T, int Hkv, int head_dim, int in_d
  *   lse            device float[Hq, T] or NULL
  *   workspace      device, 256-byte aligned, >= attn_prefill_workspace_bytes(T,
  *                  Hkv, head_dim, in_dtype) bytes when the library rotates the
- *                  keys (it holds them), else >= YR_WORKSPACE_HEADER_BYTES
+ *                  keys (it holds them), else >= YR_WORKSPACE_HEADER_BYTES;
+ *                  its header holds the device error word and the counters of
+ *                  the work queues the workgroups take their items from (the
+ *                  library clears them on the stream before each launch)
  *   head_dim       64 or 128;  Hq % Hkv == 0
  * With T = 0 (every sequence empty) q, k, v and out may be NULL; cu_seqlens
  * is still checked on the device.
@@ -246,7 +249,8 @@ int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
  *   inv_freq_f64     device double[head_dim/2], or NULL when q is rotated
  *   out, lse         as attn_prefill_fwd ([Tq, Hq, head_dim], float[Hq, Tq])
  *   workspace        device, 256-byte aligned, >= YR_WORKSPACE_HEADER_BYTES
- *                    (holds the device error word)
+ *                    (holds the device error word and work-queue counters, as
+ *                    for attn_prefill_fwd)
  * With Tq = 0 q, the caches and out may be NULL; cu_seqlens_q and ctx_lens
  * are still checked on the device.
  */

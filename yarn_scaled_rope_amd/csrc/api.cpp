@@ -22,6 +22,9 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool dims_ok(int head_dim) { return head_dim == 64 || head_dim == 128; }
 
 int *flag_of(void *ws) { return static_cast<int *>(ws); }
+// work-queue counters of the queued tail of a large prefill launch: 8 ints at
+// byte 128 of the header (a cache line of their own, apart from the error word)
+int *queues_of(void *ws) { return reinterpret_cast<int *>(static_cast<char *>(ws) + 128); }
 }  // namespace
 
 int fail(int status, const char *msg) {
@@ -337,6 +340,7 @@ int attn_prefill_fwd(const void *q, const void *k, const void *v, int in_dtype,
   p.window = window;
   p.sinks = sinks;
   p.permuted_order = (flags & YR_PREFILL_PERMUTED_ORDER) ? 1 : 0;
+  p.work_queues = queues_of(workspace);
 
   if (key_pass && T > 0) {
     // rotate every key once into the workspace; the attention kernel rotates
@@ -423,6 +427,7 @@ int attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cache, 
   p.ctx_lens = ctx_lens;
   p.window = window;
   p.sinks = sinks;
+  p.work_queues = queues_of(workspace);
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = in_dtype == YR_F32 ? launch_prefill_f32(p, s) : launch_prefill_bf16(p, s);
   if (e != hipSuccess) return fail_hip(e, "attn_prefill_chunk");

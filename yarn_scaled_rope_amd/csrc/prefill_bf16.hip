@@ -262,6 +262,38 @@ __device__ __forceinline__ bool packed_item(const int *__restrict__ cu, int B, l
   return false;  // not reached: cnt > k
 }
 
+// Number of q-tiles of a packed batch, sum_b ceil(n_b / kBQ) (uniform over
+// the wave; the sequences spread over the lanes).
+__device__ __forceinline__ int packed_tiles(const int *__restrict__ cu, int B, long long T,
+                                            int max_seqlen) {
+  int acc = 0;
+  for (int bb = (int)(threadIdx.x & 63); bb < B; bb += 64) {
+    long long s0;
+    int nb;
+    seq_bounds(cu, bb, T, max_seqlen, &s0, &nb);
+    acc += (nb + kBQ - 1) / kBQ;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  return __builtin_amdgcn_readfirstlane(acc);
+}
+
+// Work queues for the tail of a large packed launch.  The XCDs run at
+// different clocks (a spread of ~6% on one part), and each runs the
+// workgroups of its share of block indices at its own pace, so with a static
+// map the fastest idles at the end while the slowest finishes.  Items below
+// `static_items` (a multiple of 8) go by block index; counter x hands out the
+// items above it that are congruent to x modulo 8, in increasing order (its
+// k-th take returns static_items + x + 8k), the items the block-index map
+// would give XCD x.  A workgroup past the static part takes from the queue of
+// its XCD and, once that is empty, from the others in turn; with a few more
+// workgroups than items an XCD that runs ahead takes tail items a slower one
+// has not reached.  Counters only grow; a take past the end is harmless.
+// Only thread 0 calls this.
+__device__ __forceinline__ int queue_take(int *queues, int x) {
+  return x + kXcds * atomicAdd(queues + x, 1);
+}
+
 // EXT: keys from a cache with a prefix (chunked prefill) and / or a sliding
 // window with sinks; without it those are compiled out (plain causal).
 template <int D, bool OUT_F32, bool ROTATE_Q, bool EXT>
@@ -270,7 +302,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const uint16_t *__restrict__ v, const int *__restrict__ cu, int B, int max_seqlen,
     long long T, int Hq, int Hkv, const double *__restrict__ theta, float scale_log2,
     void *__restrict__ out, float *__restrict__ lse, int ntiles, int *flag, int kv_len,
-    const int *__restrict__ ctx, int window, int sinks, int permuted) {
+    const int *__restrict__ ctx, int window, int sinks, int permuted, int *__restrict__ queues,
+    int static_items) {
   constexpr int KQ = D / 32;         // score MFMA k-steps over the head dim
   constexpr int DB = D / 16;         // 16-row blocks of O^T (head dims)
   constexpr int CH = D / 8;          // 16-byte chunks per row
@@ -333,9 +366,30 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     if (b >= B) return;
     seq_bounds(cu, b, T, max_seqlen, &s0, &n);
   } else {
-    const int nwg = (int)gridDim.x;
     int item = (int)blockIdx.x;
-    if (permuted) item = (int)(((long long)(nwg - 1 - item) + nwg / 3) % nwg);
+    int total = -1;  // items of the packed map, formed when needed
+    if (queues != nullptr && item >= static_items) {
+      // the first take goes out before the item count is formed, so that the
+      // atomic's round trip overlaps the count's loads
+      __shared__ int item_slot;
+      const int x0 = (int)(blockIdx.x % kXcds);
+      int it = 0;
+      if (threadIdx.x == 0) it = static_items + queue_take(queues, x0);
+      total = Hq * packed_tiles(cu, B, T, max_seqlen);
+      if (threadIdx.x == 0) {
+        for (int d = 1; it >= total && d < kXcds; ++d)
+          it = static_items + queue_take(queues, (x0 + d) % kXcds);
+        item_slot = it < total ? it : -1;
+      }
+      __syncthreads();
+      item = item_slot;
+      if (item < 0) return;
+    }
+    if (permuted) {  // any bijection of the items (order-independence test)
+      if (total < 0) total = Hq * packed_tiles(cu, B, T, max_seqlen);
+      if (item >= total) return;
+      item = (int)(((long long)(total - 1 - item) + total / 3) % total);
+    }
     if (!packed_item(cu, B, T, max_seqlen, Hq, ntiles, item, &tile, &b, &h, &s0, &n)) return;
   }
   const int hk = h / (Hq / Hkv);
@@ -860,16 +914,47 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   }
 }
 
+// Zeroes the work-queue counters (a kernel rather than a memset, so that a
+// captured graph replays it correctly).
+__global__ void prefill_queue_reset(int *queues) {
+  if (threadIdx.x < kXcds) queues[threadIdx.x] = 0;
+}
+
+// Packed launches of at least this many work items (32 per CU on 256 CUs)
+// hand out the last third of their items through the work queues; shorter
+// ones gain less from it than the atomics cost (16K MHA: -2% with every item
+// queued, the 128K GQA and ragged 70B launches +1.2 to +1.6%).
+constexpr long long kQueueMinItems = 8192;
+
 template <int D, bool OUT_F32, bool ROT, bool EXT>
 hipError_t launch_one(const PrefillArgs &a, hipStream_t s) {
   const int ntiles = (a.max_seqlen + kBQ - 1) / kBQ;
-  const long long blocks = (long long)ntiles * a.B * a.Hq;
   const float scale_log2 = (float)((double)a.softmax_scale * 1.4426950408889634074);
+  // The ranked map of chunked prefill takes one block per (rank, q-tile,
+  // head).  The packed map has at most Hq * min(ntiles * B, ceil(T / kBQ) +
+  // B) items (sum_b ceil(n_b / kBQ) is at most both); large launches add 1/16
+  // spare workgroups for the queued tail.
+  const bool ranked = a.kv_cache_len > 0 && a.B <= kMaxRankedSeqs;
+  long long blocks = (long long)ntiles * a.B * a.Hq;
+  int *queues = nullptr;
+  int static_items = 0;
+  if (!ranked) {
+    const long long tiles = std::min<long long>((long long)ntiles * a.B, (a.T + kBQ - 1) / kBQ + a.B);
+    const long long items = tiles * a.Hq;
+    blocks = items;
+    if (a.work_queues != nullptr && items >= kQueueMinItems) {
+      static_items = (int)(items * 2 / 3) & ~(kXcds - 1);
+      blocks = items + items / 16 + kXcds;
+      queues = a.work_queues;
+      hipLaunchKernelGGL(prefill_queue_reset, dim3(1), dim3(64), 0, s, queues);
+    }
+  }
+  if (blocks < 1) blocks = 1;  // validates cu_seqlens even when nothing is computed
   hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_F32, ROT, EXT>), dim3((unsigned)blocks), dim3(kThreads),
                      0, s, (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                      a.cu_seqlens, a.B, a.max_seqlen, a.T, a.Hq, a.Hkv, a.theta, scale_log2, a.out,
                      a.lse, ntiles, a.dev_flag, a.kv_cache_len, a.ctx_lens, a.window, a.sinks,
-                     a.permuted_order);
+                     a.permuted_order, queues, static_items);
   return hipGetLastError();
 }
 

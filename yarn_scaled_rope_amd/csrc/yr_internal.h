@@ -57,6 +57,9 @@ struct PrefillArgs {
   int window;            // 0 = plain causal
   int sinks;
   int permuted_order;    // 1: workgroups take the work items in a permuted order
+  // 8 ints of device memory (in the workspace header) for the work-queue
+  // counters of a large launch's queued tail, or NULL: items by block index
+  int *work_queues;
 };
 
 struct DecodeArgs {
