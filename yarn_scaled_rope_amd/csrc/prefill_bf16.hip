@@ -499,32 +499,47 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 
   // ---- Q fragments (B operand of S^T = K Q^T), rotated on load -----------
   // Lane l holds query rows tq[rb] = tw0 + 16 rb + l16 (rb = 0, 1) and, for
-  // k-step ks, head dims 32 ks + 8 g4 .. +7.
+  // k-step ks, head dims 32 ks + 8 g4 .. +7.  Every load goes out before any
+  // arithmetic: written per fragment, the compiler waited for each
+  // fragment's loads in turn (and the first wait also for the tile copies
+  // issued above), 8 round trips in a row before the first tile.  A row past
+  // the sequence end reads row 0 and is zeroed.
   bf16x8 qf[RB][KQ];
   int tq[RB];
+  u32x4 qw[RB][KQ];
+  double thq[KQ][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     tq[rb] = tw0 + 16 * rb + l16;
+    const uint16_t *qp = q + ((s0 + (tq[rb] < n ? tq[rb] : 0)) * Hq + h) * (long long)D + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < KQ; ++ks) qw[rb][ks] = *reinterpret_cast<const u32x4 *>(qp + ks * 32);
+  }
+  if (ROTATE_Q) {
+#pragma unroll
+    for (int ks = 0; ks < KQ; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) thq[ks][e] = theta[ks * 16 + g4 * 4 + e];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
     const bool qvalid = tq[rb] < n;
-    const uint16_t *qp = q + ((s0 + (qvalid ? tq[rb] : 0)) * Hq + h) * (long long)D + 8 * g4;
 #pragma unroll
     for (int ks = 0; ks < KQ; ++ks) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (qvalid) {
-        w = *reinterpret_cast<const u32x4 *>(qp + ks * 32);
+      u32x4 w = qw[rb][ks];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // the logit scale (log2 units) folded into the query before its one
-          // rounding to bf16, so that the scores come out of the matrix cores
-          // ready for exp2
-          float x0 = bf16_to_f32(w[e] & 0xffffu), x1 = bf16_to_f32(w[e] >> 16);
-          if (ROTATE_Q) {
-            float c, sn;
-            rope_cos_sin((double)(P + tq[rb]), theta[ks * 16 + g4 * 4 + e], &c, &sn);
-            rotate_pair(x0, x1, c, sn);
-          }
-          w[e] = pack_bf16x2(x0 * scale_log2, x1 * scale_log2);
+      for (int e = 0; e < 4; ++e) {
+        // the logit scale (log2 units) folded into the query before its one
+        // rounding to bf16, so that the scores come out of the matrix cores
+        // ready for exp2
+        float x0 = bf16_to_f32(w[e] & 0xffffu), x1 = bf16_to_f32(w[e] >> 16);
+        if (ROTATE_Q) {
+          float c, sn;
+          rope_cos_sin((double)(P + tq[rb]), thq[ks][e], &c, &sn);
+          rotate_pair(x0, x1, c, sn);
         }
+        w[e] = qvalid ? pack_bf16x2(x0 * scale_log2, x1 * scale_log2) : 0u;
       }
       qf[rb][ks] = as_bf16x8(w);
     }
