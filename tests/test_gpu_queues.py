@@ -4,7 +4,8 @@ sequence, head) items): windowed and plain prefill with 128 query heads over
 16K tokens, and chunked prefill of more sequences than the ranked map takes
 (so the packed map and its queues serve it), each on sampled rows against the
 oracle; the same bits with the items permuted, from a workspace header full
-of stale values, and on a second call with the same workspace."""
+of stale values, on a second call with the same workspace, and on every
+replay of a captured graph."""
 
 import numpy as np
 import pytest
@@ -122,3 +123,45 @@ def test_queued_chunk_packed_map():
     e_lse = max_abs(np.array([l[h, t] for t, h in rows]), rl)
     print(f"{len(rows)} rows: max-abs out {e_out:.3e} lse {e_lse:.3e}")
     assert e_out <= BF16_TOL and e_lse <= BF16_TOL
+
+
+def test_queued_prefill_graph_replays_match_eager(big):
+    """A queued launch captured in a HIP graph: the counter reset is a kernel
+    node, so every replay starts from zeroed queues.  Three replays with new
+    queries written eagerly between them, each against an eager call."""
+    _, dev = big
+    say("prefill 16K x 128 heads (queued tail) in a graph, 3 replays")
+    q0 = dev["q"].clone()
+    q = dev["q"].clone()
+    T = CFG.seq_lens[0]
+    out = torch.empty((T, CFG.hq, CFG.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((CFG.hq, T), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ops.attn_prefill_workspace_bytes(T, CFG.hkv, CFG.head_dim, ops.YR_BF16),
+                     dtype=torch.uint8, device="cuda")
+
+    def call():
+        ops.attn_prefill_fwd(q, dev["k"], dev["v"], dev["cu"], CFG.max_seqlen, dev["theta"],
+                             dev["scale"], out=out, out_dtype=ops.YR_F32, lse=lse, workspace=ws,
+                             window=4096, sinks=4)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for r in range(1, 4):
+        q.copy_(q0.roll(shifts=97 * r, dims=0))  # other rows at every position
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_o, got_l = out.clone(), lse.clone()
+        ref_o, ref_l = ops.attn_prefill_fwd(q, dev["k"], dev["v"], dev["cu"], CFG.max_seqlen,
+                                            dev["theta"], dev["scale"], out_dtype=ops.YR_F32,
+                                            window=4096, sinks=4)
+        torch.cuda.synchronize()
+        assert torch.equal(got_o, ref_o) and torch.equal(got_l, ref_l), f"replay {r}"
