@@ -47,6 +47,9 @@
 //     are spread over the 8 XCDs so that the query heads of one KV head land
 //     on one XCD and share its L2; with a window, each sweeps its window
 //     rotated so that neighbouring q-tiles read the same tile together.
+//     Large launches hand out the last third of their items through per-XCD
+//     work queues, so that XCDs at a higher clock take up the tail of the
+//     slower ones.
 #include "device_common.h"
 #include "yr_internal.h"
 
